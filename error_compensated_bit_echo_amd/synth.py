@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for the Echo all-reduce (no method arithmetic here).
+
+This module only draws random numbers and shapes them into rank partials: it
+holds none of the all-reduce's own arithmetic, so both the HIP path's tests and
+the CPU oracle can be fed from it without sharing any code of the method.
+
+Recipe (host side, numpy):
+  seed(cfg, dir, call, rank) = cfg*10**9 + dir*10**8 + call*10**3 + rank;
+  x = Generator(PCG64(seed)).standard_normal(n, float32) * std;
+  outliers: mask = rng.random(n) < p from the same generator, x[mask] *= k;
+  bf16 partials are x rounded to bfloat16 (round to nearest even).
+
+Large messages are drawn on the device instead (torch's Philox generator
+seeded with the same seed formula), because drawing gigabytes on one host core
+takes minutes; the checked windows are copied back for the oracle.
+
+The workloads stand in for the pages' tensor-parallel layers (hidden size 4096,
+Qwen3-8B-like prefill and decode, a training step, and a 1 GB message); no
+model weights or datasets are used.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+# name, P, shape, dtype, value distribution, calls per run
+CONFIGS = {
+    1: dict(name="tiny", P=2, shape=(8, 256), dtype="f32", std=1.0,
+            outlier_p=0.0, outlier_mult=1.0, calls=16),
+    2: dict(name="prefill", P=4, shape=(2048, 4096), dtype="bf16", std=0.02,
+            outlier_p=1e-3, outlier_mult=50.0, calls=72),
+    3: dict(name="decode", P=8, shape=(64, 4096), dtype="bf16", std=0.02,
+            outlier_p=0.0, outlier_mult=1.0, calls=128),
+    4: dict(name="training", P=4, shape=(4096, 4096), dtype="bf16", std=0.02,
+            std_bwd=1e-3, outlier_p=0.0, outlier_mult=1.0, calls=56),
+    5: dict(name="headline_1GiB", P=8, shape=(131072, 4096), dtype="bf16",
+            std=1.0, outlier_p=1e-4, outlier_mult=100.0, calls=10),
+}
+
+
+def numel(cfg_id: int) -> int:
+    r, c = CONFIGS[cfg_id]["shape"]
+    return r * c
+
+
+def seed_of(cfg_id: int, direction: int, call: int, rank: int) -> int:
+    return cfg_id * 10**9 + direction * 10**8 + call * 10**3 + rank
+
+
+def normal_f32(seed: int, n: int, std: float = 1.0, outlier_p: float = 0.0,
+               outlier_mult: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws with an optional sprinkle of scaled outliers."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal(n, dtype=F32)
+    if std != 1.0:
+        x *= F32(std)
+    if outlier_p > 0.0:
+        mask = rng.random(n) < outlier_p
+        x[mask] *= F32(outlier_mult)
+    return x
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bfloat16 (nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=F32).view(np.uint32).astype(np.uint64)
+    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
+    """The float32 value of bfloat16 bit patterns (a 16-bit shift)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
+
+
+def host_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | None = None,
+                  n: int | None = None, dtype: str | None = None, std: float | None = None):
+    """Rank partials for one call, drawn on the host.
+
+    Returns ``(raw, values)``: ``raw`` is what is uploaded ([P, n] float32, or
+    uint16 bfloat16 bit patterns), ``values`` the same numbers as float32.
+    """
+    c = CONFIGS[cfg_id]
+    P = c["P"] if P is None else P
+    n = numel(cfg_id) if n is None else n
+    dtype = c["dtype"] if dtype is None else dtype
+    if std is None:
+        std = c.get("std_bwd", c["std"]) if direction == 1 else c["std"]
+    rows = [normal_f32(seed_of(cfg_id, direction, call, r), n, std,
+                       c["outlier_p"], c["outlier_mult"]) for r in range(P)]
+    x = np.stack(rows) if P else np.zeros((0, n), F32)
+    if dtype == "f32":
+        return x, x
+    bits = f32_to_bf16_bits(x)
+    return bits, bf16_bits_as_f32(bits)
+
+
+def device_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | None = None,
+                    n: int | None = None, device: str = "cuda"):
+    """Rank partials drawn on the device with torch (for messages of gigabytes).
+
+    Returns a list of P contiguous bfloat16 (or float32) tensors of n elements.
+    """
+    import torch
+
+    c = CONFIGS[cfg_id]
+    P = c["P"] if P is None else P
+    n = numel(cfg_id) if n is None else n
+    std = c.get("std_bwd", c["std"]) if direction == 1 else c["std"]
+    out = []
+    for r in range(P):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed_of(cfg_id, direction, call, r))
+        x = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            x.mul_(std)
+        if c["outlier_p"] > 0.0:
+            mask = torch.rand(n, generator=g, device=device) < c["outlier_p"]
+            x[mask] *= c["outlier_mult"]
+            del mask
+        out.append(x if c["dtype"] == "f32" else x.to(torch.bfloat16))
+        del x
+    return out

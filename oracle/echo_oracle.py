@@ -1,0 +1,296 @@
+"""Plain numpy oracle of one Echo all-reduce call (TEST INFRASTRUCTURE ONLY).
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may use this module; the product path never does.  It imports nothing from the
+HIP library's package.
+
+What is computed, step by step, for P rank partials x_0..x_{P-1} of N elements
+each, on a direction d ("fwd" = 0, "bwd" = 1) whose compensator state is the
+pair (m_fast, m_slow) of fp32 vectors of length N:
+
+  1. Stage 1, on every rank: each group of 32 consecutive elements is mapped to
+     4-bit integer codes and one fp32 scale by Q below.  The pages say the ranks
+     ship their segments as 4-bit integers
+     [rit.work "echo-4-bit-gpu-communication", «Как Echo возвращает ошибку в
+     следующие вызовы»].
+  2. Exchange: the owner of segment j receives segment j of every rank's
+     payload (emulated: the owner reads it in place).
+  3. Owner sum: d_r = fl(q_r * s_r), S = (((d_0 + d_1) + d_2) + ...) in fp32,
+     in rank order.  The owner restores the codes and adds them in high
+     precision [same section; heraldofai.com «Come Echo permette…»,
+     «Come Echo evita che gli errori si accumulino»].
+  4. Correction: c = fl(fl(0.5*m_fast) + fl(0.5*m_slow)) and V = fl(S + c).
+     The correction from earlier calls enters the value that is about to be
+     rounded, so it reaches every rank's residual stream through the broadcast
+     [rit.work, «Как Echo возвращает ошибку…»].
+  5. Stage 2: (q2, s2) = Q(V); B = fl(q2 * s2) is what every rank decodes.
+     Each element has therefore passed through Q exactly twice, whatever P is
+     [rit.work, «Как Echo возвращает ошибку…»; heraldofai.com,
+     «Come Echo evita che gli errori si accumulino»].
+  6. Error and compensator: r = fl(V - B) is the error the owner's own rounding
+     just introduced; the fast and the slow smoothed estimates are updated as
+     m <- fl(fl(beta*m) + fl(omega*r)), omega = fl(1 - beta), with
+     beta_fast = 0.5 and beta_slow = fl(0.95); forward and backward keep
+     separate pairs [rit.work, «Как Echo возвращает ошибку…»].
+  7. Output: out = B in fp32.
+
+Q(v) for one group v[0..31] of fp32 values:
+  a = max |v_i|;  s = fl(a / 7)  (IEEE binary32 division);
+  if s == 0: every code is 0;
+  else: q_i = the code k in [-7, 7] nearest to the exact real quotient v_i / s,
+        ties to the even k.  (Away from the denormal range this is just the
+        round-half-even of v_i / s, which never leaves [-7, 7].)
+
+Readings where the pages are silent (group 32, absmax/7 scale, half-even
+ties, nearest-code saturation, correction weights 1/2 + 1/2, beta values,
+r = V - B, fp32 output) are fixed in the design notes of this repository.
+
+Every operation below is a single IEEE binary32 operation with round-to-nearest-
+even (numpy float32 arithmetic; denormals are kept), except the code choice in
+Q, which evaluates v/s in binary64: for binary32 v and s, a quotient that is
+not a tie lies at least 2**-26 (relative) away from every half-integer, far
+beyond binary64's rounding error, and an exact tie is representable, so the
+binary64 quotient always selects the same code as the exact one.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+QMAX = 7
+F32 = np.float32
+F64 = np.float64
+
+FWD = 0
+BWD = 1
+
+
+# ----------------------------------------------------------------------------
+# data conversion
+# ----------------------------------------------------------------------------
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly (16-bit shift)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(F32)
+
+
+# ----------------------------------------------------------------------------
+# the quantizer Q
+# ----------------------------------------------------------------------------
+def quantize_groups(v: np.ndarray):
+    """Q applied to every group of 32 consecutive elements of ``v``.
+
+    Returns ``(codes, scales)``: int8 codes in [-7, 7] with the shape of ``v``
+    flattened to ``(-1, 32)`` and one float32 scale per group.
+    """
+    v = np.ascontiguousarray(v, dtype=F32).reshape(-1, GROUP)
+    a = np.max(np.abs(v), axis=1)
+    s = a / F32(QMAX)  # binary32 division, round to nearest even
+    codes = np.zeros(v.shape, dtype=np.int8)
+    nz = s != F32(0)
+    if np.any(nz):
+        quot = v[nz].astype(F64) / s[nz].astype(F64)[:, None]
+        k = np.rint(quot)  # round half to even
+        k = np.clip(k, -QMAX, QMAX)  # nearest admissible code
+        codes[nz] = k.astype(np.int8)
+    return codes, s.astype(F32)
+
+
+def dequantize_groups(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fl(q * s) per element, as float32 of shape ``(-1, 32)``."""
+    codes = np.asarray(codes, dtype=np.int8).reshape(-1, GROUP)
+    scales = np.asarray(scales, dtype=F32).reshape(-1)
+    return codes.astype(F32) * scales[:, None]
+
+
+# ----------------------------------------------------------------------------
+# wire format: two's-complement nibbles, element 2k in the low nibble of byte k
+# ----------------------------------------------------------------------------
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int8).reshape(-1)
+    u = c.view(np.uint8) & np.uint8(0x0F)
+    return (u[0::2] | (u[1::2] << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    b = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    out = np.empty(b.size * 2, dtype=np.int8)
+    lo = (b & np.uint8(0x0F)).astype(np.int16)
+    hi = (b >> np.uint8(4)).astype(np.int16)
+    out[0::2] = ((lo ^ 8) - 8).astype(np.int8)
+    out[1::2] = ((hi ^ 8) - 8).astype(np.int8)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# owner segments and wire bytes
+# ----------------------------------------------------------------------------
+def owner_segments(n_groups: int, P: int):
+    """Group ranges [start, end) owned by ranks 0..P-1 (ceil split, last short)."""
+    per = -(-n_groups // P) if P > 0 else 0
+    segs = []
+    for j in range(P):
+        lo = min(n_groups, j * per)
+        hi = min(n_groups, (j + 1) * per)
+        segs.append((lo, hi))
+    return segs
+
+
+def payload_bytes(n_elems: int) -> int:
+    """Bytes one int4 payload of ``n_elems`` occupies: codes plus fp32 scales."""
+    return n_elems // 2 + 4 * (n_elems // GROUP)
+
+
+def wire_bytes(P: int, N: int):
+    """Bytes each rank would put on the wire for one call.
+
+    rs: largest over ranks of what a rank sends to the other owners;
+    ag: largest over owners of what an owner broadcasts to the other ranks;
+    bf16: a ring all-reduce of the same message in bfloat16, 2(P-1)/P * 2N.
+    """
+    segs = owner_segments(N // GROUP, P)
+    seg_b = [payload_bytes((hi - lo) * GROUP) for lo, hi in segs]
+    rs = max((sum(seg_b) - seg_b[r] for r in range(P)), default=0)
+    ag = max(((P - 1) * b for b in seg_b), default=0)
+    bf16 = (2 * (P - 1) * 2 * N) // P if P > 0 else 0
+    return {"rs_per_rank": rs, "ag_per_rank": ag, "bf16_allreduce_per_rank": bf16}
+
+
+# ----------------------------------------------------------------------------
+# compensator state
+# ----------------------------------------------------------------------------
+class OracleState:
+    """(m_fast, m_slow) per direction, fp32, all zero after a reset."""
+
+    def __init__(self, N: int):
+        self.N = N
+        self.m_fast = {FWD: np.zeros(N, F32), BWD: np.zeros(N, F32)}
+        self.m_slow = {FWD: np.zeros(N, F32), BWD: np.zeros(N, F32)}
+
+    def reset(self, mask: int = 3):
+        for d in (FWD, BWD):
+            if mask & (1 << d):
+                self.m_fast[d][:] = 0
+                self.m_slow[d][:] = 0
+
+    def copy(self) -> "OracleState":
+        o = OracleState(self.N)
+        for d in (FWD, BWD):
+            o.m_fast[d] = self.m_fast[d].copy()
+            o.m_slow[d] = self.m_slow[d].copy()
+        return o
+
+
+# ----------------------------------------------------------------------------
+# one call
+# ----------------------------------------------------------------------------
+def echo_call(partials, state: OracleState | None, direction: int = FWD,
+              compensate: bool = True, beta_fast: float = 0.5,
+              beta_slow: float = 0.95):
+    """One Echo all-reduce of ``partials`` ([P, N] float32).
+
+    Advances ``state`` (direction ``direction``) in place when compensating and
+    returns a dict with every intermediate the GPU path exposes.
+    """
+    x = np.ascontiguousarray(partials, dtype=F32)
+    if x.ndim != 2:
+        raise ValueError("partials must be [P, N]")
+    P, N = x.shape
+    if N % GROUP:
+        raise ValueError("N must be a multiple of 32")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("partials must be finite")
+    n_g = N // GROUP
+
+    # 1. stage 1 on every rank
+    q1 = np.empty((P, N), np.int8)
+    s1 = np.empty((P, n_g), F32)
+    for r in range(P):
+        q, s = quantize_groups(x[r])
+        q1[r] = q.reshape(-1)
+        s1[r] = s
+
+    # 2.-6. each owner works on its own segment of every rank's payload
+    S = np.empty(N, F32)
+    c = np.zeros(N, F32)
+    V = np.empty(N, F32)
+    q2 = np.empty(N, np.int8)
+    s2 = np.empty(n_g, F32)
+    B = np.empty(N, F32)
+    err = np.zeros(N, F32)
+    if compensate:
+        bf, bs = F32(beta_fast), F32(beta_slow)
+        wf, ws = F32(1) - bf, F32(1) - bs
+        mf = state.m_fast[direction]
+        ms = state.m_slow[direction]
+    for g0, g1 in owner_segments(n_g, P):
+        if g1 <= g0:
+            continue
+        e0, e1 = g0 * GROUP, g1 * GROUP
+        # 3. dequantize every rank's contribution and add in rank order
+        acc = None
+        for r in range(P):
+            d = dequantize_groups(q1[r, e0:e1], s1[r, g0:g1]).reshape(-1)
+            acc = d if acc is None else acc + d
+        S[e0:e1] = acc
+        # 4. correction from the two smoothed error estimates
+        if compensate:
+            cc = F32(0.5) * mf[e0:e1] + F32(0.5) * ms[e0:e1]
+            c[e0:e1] = cc
+            vv = acc + cc
+        else:
+            vv = acc
+        V[e0:e1] = vv
+        # 5. stage 2
+        qq, ss = quantize_groups(vv)
+        q2[e0:e1] = qq.reshape(-1)
+        s2[g0:g1] = ss
+        bb = dequantize_groups(qq, ss).reshape(-1)
+        B[e0:e1] = bb
+        # 6. error of this rounding, then the two estimates
+        if compensate:
+            rr = vv - bb
+            err[e0:e1] = rr
+            mf[e0:e1] = bf * mf[e0:e1] + wf * rr
+            ms[e0:e1] = bs * ms[e0:e1] + ws * rr
+
+    # 7. every rank decodes the broadcast payload
+    codes2 = pack_nibbles(q2)
+    out = dequantize_groups(unpack_nibbles(codes2), s2).reshape(-1)
+    return {
+        "codes1": np.stack([pack_nibbles(q1[r]) for r in range(P)]) if P else np.zeros((0, N // 2), np.uint8),
+        "scales1": s1,
+        "q1": q1,
+        "S": S,
+        "c": c,
+        "V": V,
+        "q2": q2,
+        "codes2": codes2,
+        "scales2": s2,
+        "B": B,
+        "r": err,
+        "out": out,
+    }
+
+
+def plain_sum(partials) -> np.ndarray:
+    """Exact-as-possible reference sum, in binary64, of [P, N] partials."""
+    return np.sum(np.asarray(partials, dtype=F64), axis=0)
+
+
+def naive_ring_int4(partials) -> np.ndarray:
+    """Comparator: ring reduce that re-quantizes the running sum at every hop.
+
+    Rank 0 quantizes its partial and sends it on; every later rank decodes what
+    it received, adds its own partial in fp32 and quantizes again before
+    forwarding.  The last rank's payload is what everybody decodes.  An element
+    is therefore rounded P times, which is the failure mode the pages contrast
+    Echo with [rit.work, «Почему обычное 4-битное суммирование портит модель»].
+    """
+    x = np.asarray(partials, dtype=F32)
+    q, s = quantize_groups(x[0])
+    acc = dequantize_groups(q, s).reshape(-1)
+    for r in range(1, x.shape[0]):
+        q, s = quantize_groups(acc + x[r])
+        acc = dequantize_groups(q, s).reshape(-1)
+    return acc

@@ -1,0 +1,159 @@
+"""Exact-rational brute-force checker (TEST INFRASTRUCTURE ONLY).
+
+A second, independent statement of the same call as :mod:`oracle.echo_oracle`,
+written with Python ``fractions``: every arithmetic result is computed exactly
+and then rounded to the IEEE binary32 grid by :func:`round_to_binary32`, which
+is written out here from the definition of the format (24-bit significand,
+exponent range -126..127, gradual underflow down to 2**-149, ties to even).
+Quantization codes are chosen by brute force over all fifteen codes.  It is
+slow and meant for tiny tensors; its job is to pin the numpy oracle.
+
+The method is the one described in prose in the rit.work blog post
+"echo-4-bit-gpu-communication", section «Как Echo возвращает ошибку в следующие
+вызовы», and in the heraldofai.com article «Come Echo permette ai modelli AI di
+grandi dimensioni…», section «Come Echo evita che gli errori si accumulino».
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+GROUP = 32
+QMAX = 7
+
+_EMIN = -126          # smallest normal exponent of binary32
+_PREC = 24            # significand bits (with the hidden one)
+_TINY = Fraction(1, 2 ** 149)   # smallest subnormal step
+_OVER = Fraction(2 ** 128)      # first value beyond the largest finite
+HALF = Fraction(1, 2)
+
+
+def _round_half_even_int(y: Fraction) -> int:
+    """Nearest integer to ``y`` (y >= 0), ties to the even integer."""
+    fl = y.numerator // y.denominator
+    rem = y - fl
+    if rem > HALF:
+        return fl + 1
+    if rem < HALF:
+        return fl
+    return fl if fl % 2 == 0 else fl + 1
+
+
+def _floor_log2(m: Fraction) -> int:
+    e = m.numerator.bit_length() - m.denominator.bit_length()
+    # now 2**(e-1) < m < 2**(e+1); settle it
+    while Fraction(2) ** e > m:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= m:
+        e += 1
+    return e
+
+
+def round_to_binary32(x) -> Fraction:
+    """Round an exact rational to the nearest binary32 value (ties to even)."""
+    x = Fraction(x)
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    m = abs(x)
+    e = _floor_log2(m)
+    quantum = Fraction(2) ** (e - (_PREC - 1)) if e >= _EMIN else _TINY
+    k = _round_half_even_int(m / quantum)
+    r = k * quantum
+    if r >= _OVER:
+        raise OverflowError("result exceeds the binary32 range")
+    return sign * r
+
+
+def f32(x) -> Fraction:
+    """The binary32 value of a Python float / int / Fraction (rounded)."""
+    return round_to_binary32(Fraction(x))
+
+
+def add(a: Fraction, b: Fraction) -> Fraction:
+    return round_to_binary32(a + b)
+
+
+def sub(a: Fraction, b: Fraction) -> Fraction:
+    return round_to_binary32(a - b)
+
+
+def mul(a: Fraction, b: Fraction) -> Fraction:
+    return round_to_binary32(a * b)
+
+
+def div(a: Fraction, b: Fraction) -> Fraction:
+    return round_to_binary32(a / b)
+
+
+def nearest_code(v: Fraction, s: Fraction) -> int:
+    """argmin over k in [-7, 7] of |v - k*s|, exact; ties go to the even k."""
+    best_k, best_d = None, None
+    for k in range(-QMAX, QMAX + 1):
+        d = abs(v - k * s)
+        if best_d is None or d < best_d or (d == best_d and k % 2 == 0):
+            best_k, best_d = k, d
+    return best_k
+
+
+def quantize_group(v):
+    """Q of one group (list of 32 exact binary32 values) -> (codes, scale)."""
+    a = max(abs(t) for t in v)
+    s = div(a, Fraction(QMAX))
+    if s == 0:
+        return [0] * len(v), s
+    return [nearest_code(t, s) for t in v], s
+
+
+def quantize(v):
+    codes, scales = [], []
+    for g in range(0, len(v), GROUP):
+        q, s = quantize_group(v[g:g + GROUP])
+        codes.extend(q)
+        scales.append(s)
+    return codes, scales
+
+
+def dequantize(codes, scales):
+    return [mul(Fraction(q), scales[i // GROUP]) for i, q in enumerate(codes)]
+
+
+def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
+              beta_slow=0.95):
+    """One call on exact binary32 values.
+
+    ``partials`` is a list of P lists of Fractions (each a binary32 value);
+    ``m_fast``/``m_slow`` are lists of Fractions, updated in place when
+    compensating.  Returns a dict of lists of Fractions / ints.
+    """
+    P = len(partials)
+    N = len(partials[0])
+    q1, s1 = [], []
+    for r in range(P):
+        q, s = quantize(partials[r])
+        q1.append(q)
+        s1.append(s)
+    S = []
+    for i in range(N):
+        acc = None
+        for r in range(P):
+            d = mul(Fraction(q1[r][i]), s1[r][i // GROUP])
+            acc = d if acc is None else add(acc, d)
+        S.append(acc)
+    if compensate:
+        c = [add(mul(HALF, m_fast[i]), mul(HALF, m_slow[i])) for i in range(N)]
+        V = [add(S[i], c[i]) for i in range(N)]
+    else:
+        c = [Fraction(0)] * N
+        V = list(S)
+    q2, s2 = quantize(V)
+    B = dequantize(q2, s2)
+    err = [Fraction(0)] * N
+    if compensate:
+        bf, bs = f32(beta_fast), f32(beta_slow)
+        wf, ws = sub(Fraction(1), bf), sub(Fraction(1), bs)
+        for i in range(N):
+            err[i] = sub(V[i], B[i])
+            m_fast[i] = add(mul(bf, m_fast[i]), mul(wf, err[i]))
+            m_slow[i] = add(mul(bs, m_slow[i]), mul(ws, err[i]))
+    return {"q1": q1, "scales1": s1, "S": S, "c": c, "V": V, "q2": q2,
+            "scales2": s2, "B": B, "r": err, "out": B}

@@ -1,0 +1,456 @@
+"""CPU pins of the oracle: each checks it against something other than itself.
+
+Brute force in exact rationals, hand-worked golden values, closed forms of the
+compensator, special cases that reduce to textbook routines, and invariants
+that the pages state (at most two roundings per element; a payload of about a
+quarter of the 16-bit bytes; an accumulated error that stays bounded with
+compensation and grows without it).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import echo_oracle as eo
+from oracle import exact as ex
+from error_compensated_bit_echo_amd import synth
+
+F32 = np.float32
+F64 = np.float64
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _fr(a):
+    return [Fraction(float(t)) for t in np.asarray(a, F32).reshape(-1)]
+
+
+def _as_f32(frs):
+    return np.array([float(t) for t in frs], dtype=F32)
+
+
+# ---------------------------------------------------------------------------
+# binary32 rounding of the exact checker vs the library cast
+# ---------------------------------------------------------------------------
+def test_exact_rounding_matches_float64_to_float32_cast():
+    rng = np.random.default_rng(1)
+    vals = list(rng.standard_normal(3000) * 10.0 ** rng.integers(-45, 38, 3000))
+    # exact midpoints between neighbouring binary32 values, including subnormals
+    for f in [F32(1.0), F32(3.1), F32(1e-39), F32(2.0 ** -149), F32(1e-45) * 5, F32(3e38)]:
+        nxt = np.nextafter(f, F32(np.inf))
+        vals.append((F64(f) + F64(nxt)) / 2)
+        vals.append(-(F64(f) + F64(nxt)) / 2)
+    for v in vals:
+        v = F64(v)
+        want = F32(v)
+        if not np.isfinite(want):
+            continue
+        got = ex.round_to_binary32(Fraction(float(v)))
+        assert float(got) == float(want), (v, got, want)
+
+
+# ---------------------------------------------------------------------------
+# P1: the quantizer against brute force in exact rationals
+# ---------------------------------------------------------------------------
+def _tie_groups(rng, n_groups):
+    """Groups whose scale is exact and whose members are exact half-integer ties."""
+    groups = []
+    for _ in range(n_groups):
+        m = int(rng.integers(1, 2 ** 12)) | 1
+        e = int(rng.integers(-20, 20))
+        s = F64(m) * 2.0 ** e
+        g = np.empty(32, F64)
+        g[0] = 7 * s * (1 if rng.random() < 0.5 else -1)
+        k = rng.integers(-7, 7, 31)
+        half = rng.random(31) < 0.7
+        g[1:] = (k + np.where(half, 0.5, 0.0)) * s
+        g = g.astype(F32)
+        assert np.all(g.astype(F64) == np.concatenate([[g[0]], (k + np.where(half, 0.5, 0.0)) * s]))
+        groups.append(g)
+    return np.concatenate(groups)
+
+
+@pytest.mark.parametrize("kind", ["normal", "tiny", "huge", "ties", "subnormal", "sparse"])
+def test_quantizer_matches_brute_force(kind):
+    rng = np.random.default_rng({"normal": 1, "tiny": 2, "huge": 3, "ties": 4,
+                                 "subnormal": 5, "sparse": 6}[kind])
+    n = 32 * 24
+    if kind == "normal":
+        v = rng.standard_normal(n).astype(F32)
+    elif kind == "tiny":
+        v = (rng.standard_normal(n) * 1e-30).astype(F32)
+    elif kind == "huge":
+        v = (rng.standard_normal(n) * 1e30).astype(F32)
+    elif kind == "ties":
+        v = _tie_groups(rng, 24)
+    elif kind == "subnormal":
+        v = (rng.integers(-80, 80, n) * 2.0 ** -149).astype(F32)
+        v[:32] = (rng.integers(-3, 4, 32) * 2.0 ** -149).astype(F32)  # s underflows to 0
+    else:
+        v = rng.standard_normal(n).astype(F32)
+        v[rng.random(n) < 0.8] = 0
+        v[:32] = 0
+        v[32:64] = -0.0
+    q, s = eo.quantize_groups(v)
+    qx, sx = ex.quantize(_fr(v))
+    assert np.array_equal(q.reshape(-1), np.array(qx, np.int8))
+    assert np.array_equal(s, _as_f32(sx))
+    # the scale is the binary32 quotient of the group absmax by 7
+    a = np.max(np.abs(v.reshape(-1, 32)), axis=1)
+    assert np.array_equal(s, _as_f32([ex.div(Fraction(float(t)), Fraction(7)) for t in a]))
+
+
+def test_quantizer_subnormal_saturation_is_nearest_code():
+    # a = 10 * 2**-149 gives s = fl(10/7 * 2**-149) = 2**-149, so a/s = 10 > 7.5:
+    # the nearest admissible code is 7.
+    v = np.zeros(32, F32)
+    v[0] = F32(10 * 2.0 ** -149)
+    v[1] = -F32(9 * 2.0 ** -149)
+    q, s = eo.quantize_groups(v)
+    assert s[0] == F32(2.0 ** -149)
+    assert q[0, 0] == 7 and q[0, 1] == -7
+    qx, _ = ex.quantize(_fr(v))
+    assert qx[0] == 7 and qx[1] == -7
+
+
+# ---------------------------------------------------------------------------
+# P2: hand-worked tie table and special cases
+# ---------------------------------------------------------------------------
+def _load_ties():
+    rows = []
+    with open(os.path.join(GOLDEN, "quantizer_ties.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split()
+            rows.append((F32(float(a)), int(b)))
+    return rows
+
+
+def test_quantizer_tie_table_golden():
+    rows = _load_ties()
+    for val, want in rows:
+        g = np.zeros(32, F32)
+        g[0] = F32(7.0)
+        g[1] = val
+        q, s = eo.quantize_groups(g)
+        assert s[0] == F32(1.0)
+        assert q[0, 1] == want, (val, q[0, 1], want)
+
+
+def test_quantizer_special_cases():
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal(32 * 64).astype(F32)
+    q, s = eo.quantize_groups(v)
+    g = v.reshape(-1, 32)
+    # the absmax element always maps to +-7
+    idx = np.argmax(np.abs(g), axis=1)
+    assert np.all(np.abs(q[np.arange(len(idx)), idx]) == 7)
+    # every value is within half a step of its code
+    err = np.abs(g.astype(F64) - q.astype(F64) * s.astype(F64)[:, None])
+    assert np.all(err <= s.astype(F64)[:, None] / 2)
+    # a zero group has a zero scale and zero codes
+    z, zs = eo.quantize_groups(np.zeros(32, F32))
+    assert zs[0] == 0 and not np.any(z)
+
+
+# ---------------------------------------------------------------------------
+# P3: the measured error is exact and bounded
+# ---------------------------------------------------------------------------
+def test_error_is_exact_and_bounded():
+    st = eo.OracleState(2048)
+    for t in range(8):
+        _, x = synth.host_partials(1, 0, t)
+        o = eo.echo_call(x, st)
+        V, B, r = o["V"].astype(F64), o["B"].astype(F64), o["r"].astype(F64)
+        assert np.array_equal(r + B, V)
+        s2 = np.repeat(o["scales2"].astype(F64), 32)
+        ulpB = np.spacing(np.abs(o["B"])).astype(F64)
+        assert np.all(np.abs(r) <= s2 / 2 + ulpB / 2)
+
+
+# ---------------------------------------------------------------------------
+# P4: payload layout and byte counts
+# ---------------------------------------------------------------------------
+def test_nibble_layout_golden():
+    with open(os.path.join(GOLDEN, "nibble_layout.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split("|")
+            codes = np.array([int(t) for t in a.split()], np.int8)
+            want = bytes.fromhex(b.replace(" ", ""))
+            got = eo.pack_nibbles(codes).tobytes()
+            assert got == want
+            assert np.array_equal(eo.unpack_nibbles(np.frombuffer(want, np.uint8)), codes)
+
+
+def test_payload_is_about_a_quarter_of_bf16():
+    for N in (2048, 4096 * 2048, 536870912):
+        assert eo.payload_bytes(N) == N // 2 + N // 8
+        assert eo.payload_bytes(N) / (2 * N) == 0.3125
+    for P, N in ((2, 2048), (4, 4096 * 2048), (8, 536870912), (8, 262144)):
+        w = eo.wire_bytes(P, N)
+        assert w["rs_per_rank"] == (P - 1) * eo.payload_bytes(N) // P
+        assert w["ag_per_rank"] == (P - 1) * eo.payload_bytes(N) // P
+        assert (w["rs_per_rank"] + w["ag_per_rank"]) / w["bf16_allreduce_per_rank"] == 0.3125
+    # ragged segments: every group owned exactly once
+    for n_g, P in ((1, 8), (7, 3), (100, 16), (64, 2)):
+        segs = eo.owner_segments(n_g, P)
+        owned = np.zeros(n_g, int)
+        for lo, hi in segs:
+            owned[lo:hi] += 1
+        assert np.all(owned == 1)
+    o = eo.echo_call(np.zeros((3, 64), F32), eo.OracleState(64))
+    assert o["codes2"].nbytes + o["scales2"].nbytes == eo.payload_bytes(64)
+
+
+# ---------------------------------------------------------------------------
+# P5: closed form of the compensator
+# ---------------------------------------------------------------------------
+def _run(T, compensate, P=2, N=2048, cfg=1, same=False, beta_fast=0.5, beta_slow=0.95):
+    st = eo.OracleState(N)
+    outs = []
+    for t in range(T):
+        _, x = synth.host_partials(cfg, 0, 0 if same else t, P=P, n=N)
+        outs.append(eo.echo_call(x, st, compensate=compensate,
+                                 beta_fast=beta_fast, beta_slow=beta_slow))
+    return outs
+
+
+def test_compensator_closed_form():
+    T = 200
+    outs = _run(T, True)
+    r = np.stack([o["r"].astype(F64) for o in outs])          # [T, N]
+    D = np.cumsum(np.stack([o["B"].astype(F64) - o["S"].astype(F64) for o in outs]), 0)
+    bf, bs = F64(F32(0.5)), F64(F32(0.95))
+    k = 0.5 * (bf ** np.arange(T) + bs ** np.arange(T))
+    for Tq in (1, 2, 10, 50, 200):
+        pred = -np.sum(k[:Tq, None] * r[Tq - 1::-1], axis=0)
+        assert np.max(np.abs(D[Tq - 1] - pred)) < 1e-4 * np.max(np.abs(r))
+        assert np.max(np.abs(D[Tq - 1])) <= 11 * np.max(np.abs(r))
+
+
+def test_error_feedback_special_case_beta_zero():
+    # beta = 0 is classic error feedback: the sum of injected errors telescopes
+    outs = _run(30, True, beta_fast=0.0, beta_slow=0.0)
+    D = sum(o["B"].astype(F64) - o["S"].astype(F64) for o in outs)
+    r_last = outs[-1]["r"].astype(F64)
+    scale = np.max(np.abs(np.stack([o["S"] for o in outs])))
+    assert np.max(np.abs(D + r_last)) < 30 * 2.0 ** -23 * scale
+
+
+def test_no_compensation_grows_linearly_on_repeated_input():
+    off = _run(40, False, same=True)
+    e1 = off[0]["B"].astype(F64) - off[0]["S"].astype(F64)
+    D = np.zeros_like(e1)
+    for t, o in enumerate(off, 1):
+        D += o["B"].astype(F64) - o["S"].astype(F64)
+        assert np.array_equal(D, t * e1) or np.allclose(D, t * e1, rtol=0, atol=1e-12)
+    on = _run(40, True, same=True)
+    Don = sum(o["B"].astype(F64) - o["S"].astype(F64) for o in on)
+    rmax = max(np.max(np.abs(o["r"])) for o in on)
+    assert np.max(np.abs(Don)) <= 11 * rmax
+    assert np.sqrt(np.mean(D ** 2)) > 5 * np.sqrt(np.mean(Don ** 2))
+
+
+def test_single_rank_without_compensation_is_idempotent():
+    _, x = synth.host_partials(1, 0, 0, P=1, n=4096)
+    o = eo.echo_call(x, None, compensate=False)
+    assert np.array_equal(o["q1"][0], o["q2"])
+    s1, s2 = o["scales1"][0], o["scales2"]
+    assert np.all(np.abs(s2.astype(F64) - s1.astype(F64)) <= np.spacing(s1).astype(F64))
+
+
+# ---------------------------------------------------------------------------
+# P7: at most two roundings per element, for every P
+# ---------------------------------------------------------------------------
+def _lossless_partials(P, n_groups, rng):
+    """Integer partials whose stage-1 and stage-2 grids are both exact."""
+    b = rng.integers(-4, 5, (n_groups, 32))
+    b[:, 0] = 7 * np.where(rng.random(n_groups) < 0.5, 1, -1)
+    t = rng.integers(-3, 4, (n_groups, 32))
+    t[:, 0] = 0
+    # zero-sum signs; for odd P the unsigned rank goes first so that the ring
+    # comparator's running sums leave the exact grid
+    eps = ([0] if P % 2 else []) + [(1 if r % 2 == 0 else -1) for r in range(P - P % 2)]
+    x = np.stack([(b + e * t).reshape(-1) for e in eps]).astype(F32)
+    return x, (P * b).reshape(-1).astype(F64)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8, 16])
+def test_two_roundings_for_every_P(P):
+    rng = np.random.default_rng(P)
+    x, exact_sum = _lossless_partials(P, 16, rng)
+    o = eo.echo_call(x, None, compensate=False)
+    # both quantizations land on exact grid points: nothing else may round
+    assert np.array_equal(o["out"].astype(F64), exact_sum)
+    # random data: error within one half-step per stage-1 rank plus one stage-2 half-step
+    _, xr = synth.host_partials(1, 0, 3, P=P, n=4096)
+    o = eo.echo_call(xr, None, compensate=False)
+    bound = (np.sum(o["scales1"].astype(F64), axis=0) / 2 + o["scales2"].astype(F64) / 2)
+    err = np.abs(o["out"].astype(F64) - eo.plain_sum(xr)).reshape(-1, 32).max(axis=1)
+    slop = np.repeat(np.abs(xr).sum(0).reshape(-1, 32).max(1), 1) * P * 2.0 ** -22
+    assert np.all(err <= bound + slop)
+    # contrast: re-quantizing the running sum at every hop of a ring rounds each
+    # element P times; its error grows about linearly in P, Echo's about as sqrt(P)
+    if P >= 8:
+        exact = eo.plain_sum(xr)
+        ring = eo.naive_ring_int4(xr).astype(F64)
+        rms = lambda e: np.sqrt(np.mean(e ** 2))
+        assert rms(ring - exact) > 1.3 * rms(o["out"].astype(F64) - exact)
+
+
+# ---------------------------------------------------------------------------
+# P8: the whole call against the exact-rational implementation
+# ---------------------------------------------------------------------------
+def _compare_exact(x, T, compensate, beta=(0.5, 0.95)):
+    P, N = x[0].shape
+    st = eo.OracleState(N)
+    mf = [Fraction(0)] * N
+    ms = [Fraction(0)] * N
+    for t in range(T):
+        o = eo.echo_call(x[t], st, compensate=compensate, beta_fast=beta[0], beta_slow=beta[1])
+        e = ex.echo_call([_fr(x[t][r]) for r in range(P)], mf, ms, compensate=compensate,
+                         beta_fast=beta[0], beta_slow=beta[1])
+        for r in range(P):
+            assert np.array_equal(o["q1"][r], np.array(e["q1"][r], np.int8))
+            assert np.array_equal(o["scales1"][r], _as_f32(e["scales1"][r]))
+        for key in ("S", "c", "V", "B", "r", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+        assert np.array_equal(o["q2"], np.array(e["q2"], np.int8))
+        assert np.array_equal(o["scales2"], _as_f32(e["scales2"]))
+        if compensate:
+            assert np.array_equal(st.m_fast[0], _as_f32(mf))
+            assert np.array_equal(st.m_slow[0], _as_f32(ms))
+
+
+@pytest.mark.parametrize("compensate", [True, False])
+def test_whole_call_matches_exact_rationals(compensate):
+    xs = [synth.host_partials(1, 0, t, P=2, n=64)[1] for t in range(16)]
+    _compare_exact(xs, 16, compensate)
+
+
+def test_whole_call_matches_exact_rationals_tie_rich():
+    # dyadic inputs on a coarse grid make stage-2 ties and exact cancellations common
+    rng = np.random.default_rng(11)
+    xs = [(rng.integers(-12, 13, (3, 64)) * 0.25).astype(F32) for _ in range(10)]
+    _compare_exact(xs, 10, True)
+
+
+def test_whole_call_matches_exact_rationals_bf16_and_small_scales():
+    xs = []
+    for t in range(6):
+        bits, vals = synth.host_partials(2, 0, t, P=3, n=64)
+        vals = vals.copy()
+        vals[:, :32] *= F32(2.0 ** -120)  # scales near the bottom of the normal range
+        xs.append(vals)
+    _compare_exact(xs, 6, True, beta=(0.5, 0.9))
+
+
+# ---------------------------------------------------------------------------
+# P9: bounded with compensation, growing without it
+# ---------------------------------------------------------------------------
+def _d_rms(outs):
+    D = np.cumsum(np.stack([o["B"].astype(F64) - o["S"].astype(F64) for o in outs]), 0)
+    return np.sqrt(np.mean(D ** 2, axis=1))
+
+
+def test_bounded_accumulated_error_tiny_config():
+    T = synth.CONFIGS[1]["calls"]
+    on, off = _run(T, True), _run(T, False)
+    d_on, d_off = _d_rms(on), _d_rms(off)
+    sig_r = np.sqrt(np.mean(np.stack([o["r"].astype(F64) for o in on]) ** 2))
+    assert np.max(d_on) <= 2.5 * sig_r
+    assert d_off[-1] / d_on[-1] >= 1.8
+
+
+def test_bounded_accumulated_error_deep_chain():
+    # pre-norm residual chain: h <- h + allreduce(partials of a random linear map)
+    P, rows, hid, L = 4, 8, 256, 128
+    rng = np.random.default_rng(3)
+    h0 = (rng.standard_normal((rows, hid)) * 0.02).astype(F32)
+    Ws = [(rng.standard_normal((hid, hid)) / np.sqrt(hid)).astype(F32) for _ in range(L)]
+    sl = hid // P
+    gamma = F32(0.02 * np.sqrt(P))
+    res = {}
+    for comp in (True, False):
+        h = h0.copy()
+        st = eo.OracleState(rows * hid)
+        outs = []
+        for W in Ws:
+            a = (h / np.sqrt(np.mean(h.astype(F64) ** 2))).astype(F32)
+            parts = np.stack([(gamma * (a[:, r * sl:(r + 1) * sl] @ W[r * sl:(r + 1) * sl])).reshape(-1)
+                              for r in range(P)]).astype(F32)
+            o = eo.echo_call(parts, st, compensate=comp)
+            outs.append(o)
+            h = h + o["out"].reshape(rows, hid)
+        res[comp] = outs
+    d_on, d_off = _d_rms(res[True]), _d_rms(res[False])
+    sig_r = np.sqrt(np.mean(np.stack([o["r"].astype(F64) for o in res[True]]) ** 2))
+    assert np.max(d_on) <= 2.5 * sig_r
+    assert d_off[-1] / d_on[-1] >= 4.5
+
+
+# ---------------------------------------------------------------------------
+# P10: determinism, windows, directions, reset
+# ---------------------------------------------------------------------------
+def test_group_aligned_windows_equal_whole_tensor():
+    P, N = 3, 32 * 40
+    xs = [synth.host_partials(2, 0, t, P=P, n=N)[1] for t in range(5)]
+    st = eo.OracleState(N)
+    whole = [eo.echo_call(x, st) for x in xs]
+    for lo, hi in ((0, 32 * 7), (32 * 7, 32 * 8), (32 * 8, N)):
+        sw = eo.OracleState(hi - lo)
+        for t, x in enumerate(xs):
+            o = eo.echo_call(x[:, lo:hi], sw)
+            assert np.array_equal(o["out"], whole[t]["out"][lo:hi])
+            assert np.array_equal(o["codes2"], whole[t]["codes2"][lo // 2:hi // 2])
+        assert np.array_equal(sw.m_fast[0], st.m_fast[0][lo:hi])
+        assert np.array_equal(sw.m_slow[0], st.m_slow[0][lo:hi])
+
+
+def test_directions_are_isolated_and_reset_is_fresh():
+    N = 2048
+    fw = [synth.host_partials(4, 0, t, P=2, n=N)[1] for t in range(4)]
+    bw = [synth.host_partials(4, 1, t, P=2, n=N)[1] for t in range(4)]
+    inter = eo.OracleState(N)
+    outs_i = []
+    for t in range(4):
+        outs_i.append(eo.echo_call(fw[t], inter, eo.FWD))
+        outs_i.append(eo.echo_call(bw[t], inter, eo.BWD))
+    sf, sb = eo.OracleState(N), eo.OracleState(N)
+    for t in range(4):
+        assert np.array_equal(eo.echo_call(fw[t], sf, eo.FWD)["out"], outs_i[2 * t]["out"])
+        assert np.array_equal(eo.echo_call(bw[t], sb, eo.BWD)["out"], outs_i[2 * t + 1]["out"])
+    inter.reset(1)
+    assert not np.any(inter.m_fast[0]) and np.array_equal(inter.m_fast[1], sb.m_fast[1])
+    a = eo.echo_call(fw[0], inter, eo.FWD)["out"]
+    assert np.array_equal(a, outs_i[0]["out"])
+    again = eo.echo_call(fw[0], eo.OracleState(N), eo.FWD)["out"]
+    assert np.array_equal(a, again)
+
+
+def test_rejects_bad_input():
+    with pytest.raises(ValueError):
+        eo.echo_call(np.zeros((2, 33), F32), None, compensate=False)
+    x = np.zeros((2, 64), F32)
+    x[0, 3] = np.inf
+    with pytest.raises(ValueError):
+        eo.echo_call(x, None, compensate=False)
+
+
+def test_synth_recipe_is_deterministic_and_rounds_to_bf16():
+    a = synth.host_partials(2, 0, 5, P=2, n=4096)
+    b = synth.host_partials(2, 0, 5, P=2, n=4096)
+    assert np.array_equal(a[0], b[0])
+    bits, vals = a
+    assert bits.dtype == np.uint16
+    raw = np.stack([synth.normal_f32(synth.seed_of(2, 0, 5, r), 4096, 0.02, 1e-3, 50.0)
+                    for r in range(2)])
+    # nearest bfloat16: no representable bf16 value is closer than the chosen one
+    err = np.abs(vals.astype(F64) - raw.astype(F64))
+    ulp = np.abs(np.spacing(vals.astype(F32))).astype(F64) * 2 ** 16
+    assert np.all(err <= ulp / 2)
