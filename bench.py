@@ -1,0 +1,231 @@
+"""Benchmark of the Echo int4 all-reduce on one MI355X.
+
+Workload: a 1 GiB bfloat16 message per rank (536,870,912 elements, viewed as
+[131072, 4096]), P = 8 emulated ranks whose partials are N(0,1) with 0.01 %
+outliers x100, the same 8 partials for every call, group 32, compensation on.
+A step is one whole all-reduce (stage-1 quantize of all ranks, owner
+sum/correct/requantize, decode), inputs resident in HBM.  Sequence: reset,
+W warm-up calls, reset, K timed back-to-back calls.
+
+Prints one JSON line.  value = bf16-equivalent GB/s = P * 2 * N / t_step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Echo reduce GB/s (bf16-equiv payload) + % HBM peak, 1 GB msg, P=8 emulated"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
+KERNEL_SOURCES = ["error_compensated_bit_echo_amd/csrc/echo_kernels.hip",
+                  "error_compensated_bit_echo_amd/csrc/echo_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool) -> dict:
+    """Bytes each stage must move per call (reads + writes of HBM)."""
+    k1 = P * N * (b_in + 0.625)                # read partials; write codes + scales
+    k2 = N * (0.625 * P + 0.625)               # read P payload segments; write broadcast payload
+    if compensate:
+        k2 += 16.0 * N                         # read and write m_fast, m_slow
+    k3 = N * (0.625 + 4.0)                     # read broadcast payload; write fp32 out
+    return {"stage1": k1, "owner": k2, "decode": k3}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when the kernels changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(P: int, n_sample: int, seed_cfg: int = 5) -> dict:
+    """The CPU oracle, as it stands, timed on one call over a bounded sample."""
+    import numpy as np
+    from error_compensated_bit_echo_amd import synth
+    from oracle import echo_oracle as eo
+
+    _, vals = synth.host_partials(seed_cfg, 0, 0, P=P, n=n_sample)
+    st = eo.OracleState(n_sample)
+    t0 = time.perf_counter()
+    eo.echo_call(vals, st, eo.FWD)
+    dt = time.perf_counter() - t0
+    del vals
+    return {
+        "value": round(P * 2 * n_sample / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"one call, P={P} x {n_sample} elements per rank ({n_sample / 536870912:.4g} of the "
+                  f"1 GiB message), same value distribution, compensation on; {dt:.2f} s; numpy "
+                  f"elementwise ops on one core ({platform.processor() or platform.machine()}, "
+                  f"os.cpu_count()={os.cpu_count()})",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-comp", action="store_true", help="plain two-rounding int4 all-reduce")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 25,
+                    help="elements per rank in the CPU oracle's timed sample")
+    ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle leg")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P ranks "
+              "are emulated as P partial buffers in one GPU's HBM.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import error_compensated_bit_echo_amd as E
+    from error_compensated_bit_echo_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg_id = 5
+    c = synth.CONFIGS[cfg_id]
+    P, N = c["P"], synth.numel(cfg_id)
+    comp = not args.no_comp
+    print(f"# generating {P} x {N} bf16 partials on the device", file=sys.stderr, flush=True)
+    parts = synth.device_partials(cfg_id, 0, 0, device=dev)
+    cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp)
+    st = E.echo_init_state(cfg, device=dev)
+    out = torch.empty(N, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    # warm-up, then a fresh state for the timed calls
+    for _ in range(args.warmup):
+        E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    E.echo_reset(st, 3)
+    torch.cuda.synchronize()
+    print(f"# warm-up done ({args.warmup} calls)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        e = ev[k]
+        e[0].record()
+        E.echo_stage1(parts, st)
+        e[1].record()
+        E.echo_owner(st, E.ECHO_FWD)
+        e[2].record()
+        E.echo_decode(out, st)
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / K
+    kern_ms = {
+        "stage1": sum(e[0].elapsed_time(e[1]) for e in ev) / K,
+        "owner": sum(e[1].elapsed_time(e[2]) for e in ev) / K,
+        "decode": sum(e[2].elapsed_time(e[3]) for e in ev) / K,
+    }
+    gpu_ms_step = sum(e[0].elapsed_time(e[3]) for e in ev) / K
+    print(f"# timed {K} calls: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events",
+          file=sys.stderr, flush=True)
+
+    alg = algorithmic_bytes(P, N, 2, comp)
+    total_alg = sum(alg.values())
+    kernels = {}
+    for k, ms in kern_ms.items():
+        kernels[k] = {"ms": round(ms, 4), "alg_bytes": int(alg[k]),
+                      "GBps": round(alg[k] / (ms * 1e-3) / 1e9, 1),
+                      "frac": round(alg[k] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    dom = max(kern_ms, key=kern_ms.get)
+    achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    workload = f"cfg5-1GiB-P{P}-bf16-{'comp' if comp else 'nocomp'}"
+    traffic = measured_traffic(dom, workload)
+
+    # a plain device copy of 2 GiB, for the achievable-bandwidth context
+    src = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+
+    wire = E.echo_wire_bytes(st)
+    value = P * 2 * N / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "1 GiB bf16 message per rank (536,870,912 elements), P=8 emulated ranks, "
+                        "group 32, absmax/7 fp32 scales, compensation " + ("on" if comp else "off") +
+                        ", same partials every call, reset -> warm-up -> reset -> timed calls",
+            "P": P, "numel_per_rank": N, "input_dtype": "bf16", "wire": "int4 codes + fp32 group scales",
+            "output_dtype": "f32", "group": 32,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "hbm_frac_whole_step": round(total_alg / (gpu_ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "alg_bytes_per_step": int(total_alg),
+        "algbw_GBps": round(2 * N / (ms_step * 1e-3) / 1e9, 2),
+        "kernels": kernels,
+        "copy_GBps_context": round(copy_gbps, 1),
+        "wire_bytes_per_rank": wire,
+    }
+    if not args.skip_cpu:
+        print(f"# CPU oracle sample: P={P} x {args.cpu_sample}", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(P, args.cpu_sample)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,59 @@
+"""Build libecho.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Usage: ``python -m error_compensated_bit_echo_amd.build`` (or call
+:func:`build_library`).  The library lands next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libecho.so")
+SOURCES = ["echo_kernels.hip", "echo_api.hip"]
+ARCH = "gfx950"
+
+# -ffp-contract=off: every multiply and add is its own IEEE operation (the
+#   kernels must reproduce a fixed sequence of binary32 roundings).
+# -packed-fp32-ops off: no v_pk_*_f32 instructions are emitted.
+# Denormals are kept (HIP's default; no fast-math, no flush-to-zero).
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libecho)")
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every HIP source into ``libecho.so``; returns its path."""
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    # the host pass does not know the gfx feature flag; that warning is expected
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    path = build_library(verbose="-v" in sys.argv)
+    print(path)

@@ -1,0 +1,301 @@
+// C-ABI host side of libecho: argument validation, workspace carving and the
+// launches of the stage kernels on the caller's stream.  See include/echo.h
+// for the contract of every entry point.
+#include <new>
+
+#include "echo.h"
+#include "echo_internal.h"
+
+struct echo_state {
+  echo_config cfg;
+  int device;
+  char* ws;
+  size_t ws_bytes;
+  uint32_t* codes1;             // stage-1 codes of all ranks
+  float* scales1;               // stage-1 scales of all ranks
+  int64_t codes1_stride_bytes;  // between ranks
+  int64_t scales1_stride_bytes;
+  uint32_t* codes2;             // broadcast payload
+  float* scales2;
+  float* m_fast[2];             // per direction
+  float* m_slow[2];
+  float* state_base;            // both directions, contiguous
+  int64_t vec_floats;           // floats per state vector (with alignment padding)
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+  size_t codes1_stride, scales1_stride;  // bytes per rank
+  size_t off_codes1, off_scales1, off_codes2, off_scales2, off_state;
+  size_t vec_bytes;                      // one fp32 state vector, aligned
+  size_t total;                          // without the base-alignment slack
+};
+
+Layout make_layout(const echo_config& c) {
+  const size_t N = static_cast<size_t>(c.numel);
+  const size_t P = static_cast<size_t>(c.P);
+  Layout L{};
+  L.codes1_stride = align_up(N / 2);
+  L.scales1_stride = align_up(N / 8);
+  L.off_codes1 = 0;
+  L.off_scales1 = L.off_codes1 + P * L.codes1_stride;
+  L.off_codes2 = L.off_scales1 + P * L.scales1_stride;
+  L.off_scales2 = L.off_codes2 + align_up(N / 2);
+  L.off_state = L.off_scales2 + align_up(N / 8);
+  L.vec_bytes = align_up(4 * N);
+  L.total = L.off_state + 4 * L.vec_bytes;
+  return L;
+}
+
+echo_status check_cfg(const echo_config* c) {
+  if (c == nullptr) return ECHO_ERR_ARG;
+  if (c->P < 1 || c->P > ECHO_MAX_RANKS) return ECHO_ERR_SHAPE;
+  if (c->numel < 0 || c->numel > ECHO_MAX_NUMEL || c->numel % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  if (c->group != ECHO_GROUP) return ECHO_ERR_SHAPE;
+  if (c->dtype != ECHO_F32 && c->dtype != ECHO_BF16) return ECHO_ERR_DTYPE;
+  if (c->compensate != 0 && c->compensate != 1) return ECHO_ERR_ARG;
+  if (!(c->beta_fast >= 0.0f && c->beta_fast <= 1.0f)) return ECHO_ERR_ARG;  // also rejects NaN
+  if (!(c->beta_slow >= 0.0f && c->beta_slow <= 1.0f)) return ECHO_ERR_ARG;
+  return ECHO_OK;
+}
+
+echo_status check_state(const echo_state* st) {
+  if (st == nullptr) return ECHO_ERR_STATE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ECHO_ERR_HIP;
+  if (dev != st->device) return ECHO_ERR_STATE;
+  return ECHO_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na != 0 && nb != 0 && x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(const echo_config& c) { return c.dtype == ECHO_BF16 ? 2 : 4; }
+
+echo_status check_partials(const void* const* partials, const echo_state* st) {
+  if (partials == nullptr) return ECHO_ERR_ARG;
+  const size_t nb = static_cast<size_t>(st->cfg.numel) * elem_bytes(st->cfg);
+  for (int r = 0; r < st->cfg.P; ++r) {
+    if (partials[r] == nullptr || !aligned16(partials[r])) return ECHO_ERR_ARG;
+    if (overlaps(partials[r], nb, st->ws, st->ws_bytes)) return ECHO_ERR_ARG;
+  }
+  return ECHO_OK;
+}
+
+echo_status check_out(const float* out, const echo_state* st, const void* const* partials) {
+  if (out == nullptr || !aligned16(out)) return ECHO_ERR_ARG;
+  const size_t no = static_cast<size_t>(st->cfg.numel) * 4;
+  if (overlaps(out, no, st->ws, st->ws_bytes)) return ECHO_ERR_ARG;
+  if (partials != nullptr) {
+    const size_t nb = static_cast<size_t>(st->cfg.numel) * elem_bytes(st->cfg);
+    for (int r = 0; r < st->cfg.P; ++r)
+      if (overlaps(out, no, partials[r], nb)) return ECHO_ERR_ARG;
+  }
+  return ECHO_OK;
+}
+
+echo_status run_stage1(const void* const* partials, echo_state* st, hipStream_t s) {
+  echo::Stage1Args a{};
+  for (int r = 0; r < echo::kMaxRanks; ++r) a.src[r] = r < st->cfg.P ? partials[r] : partials[0];
+  a.codes = st->codes1;
+  a.scales = st->scales1;
+  a.codes_stride_words = st->codes1_stride_bytes / 4;
+  a.scales_stride = st->scales1_stride_bytes / 4;
+  a.nchunk = st->cfg.numel / echo::kElemsPerLane;
+  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, s) == hipSuccess ? ECHO_OK
+                                                                                        : ECHO_ERR_HIP;
+}
+
+echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
+  echo::OwnerArgs a{};
+  a.codes1 = st->codes1;
+  a.scales1 = st->scales1;
+  a.codes_stride_words = st->codes1_stride_bytes / 4;
+  a.scales_stride = st->scales1_stride_bytes / 4;
+  a.codes2 = st->codes2;
+  a.scales2 = st->scales2;
+  a.m_fast = st->m_fast[dir];
+  a.m_slow = st->m_slow[dir];
+  a.nchunk = st->cfg.numel / echo::kElemsPerLane;
+  a.beta_fast = st->cfg.beta_fast;
+  a.omega_fast = 1.0f - st->cfg.beta_fast;  // fl(1 - beta)
+  a.beta_slow = st->cfg.beta_slow;
+  a.omega_slow = 1.0f - st->cfg.beta_slow;
+  return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, s) == hipSuccess ? ECHO_OK
+                                                                                   : ECHO_ERR_HIP;
+}
+
+echo_status run_decode(float* out, const echo_state* st, hipStream_t s) {
+  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel / echo::kElemsPerLane, s) ==
+                 hipSuccess
+             ? ECHO_OK
+             : ECHO_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t echo_workspace_bytes(const echo_config* cfg) {
+  if (check_cfg(cfg) != ECHO_OK || cfg->numel == 0) return 0;
+  return make_layout(*cfg).total + kAlign;
+}
+
+echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_bytes,
+                            echo_stream_t stream, echo_state** out) {
+  if (out == nullptr) return ECHO_ERR_ARG;
+  *out = nullptr;
+  const echo_status cs = check_cfg(cfg);
+  if (cs != ECHO_OK) return cs;
+  const size_t need = echo_workspace_bytes(cfg);
+  if (cfg->numel > 0 && (workspace == nullptr || ws_bytes < need)) return ECHO_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ECHO_ERR_HIP;
+
+  echo_state* st = new (std::nothrow) echo_state();
+  if (st == nullptr) return ECHO_ERR_ARG;
+  st->cfg = *cfg;
+  st->device = dev;
+  st->ws = static_cast<char*>(workspace);
+  st->ws_bytes = ws_bytes;
+  if (cfg->numel > 0) {
+    const Layout L = make_layout(*cfg);
+    char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
+    st->codes1 = reinterpret_cast<uint32_t*>(base + L.off_codes1);
+    st->scales1 = reinterpret_cast<float*>(base + L.off_scales1);
+    st->codes1_stride_bytes = static_cast<int64_t>(L.codes1_stride);
+    st->scales1_stride_bytes = static_cast<int64_t>(L.scales1_stride);
+    st->codes2 = reinterpret_cast<uint32_t*>(base + L.off_codes2);
+    st->scales2 = reinterpret_cast<float*>(base + L.off_scales2);
+    for (int d = 0; d < 2; ++d) {
+      st->m_fast[d] = reinterpret_cast<float*>(base + L.off_state + (2 * d) * L.vec_bytes);
+      st->m_slow[d] = reinterpret_cast<float*>(base + L.off_state + (2 * d + 1) * L.vec_bytes);
+    }
+    st->state_base = reinterpret_cast<float*>(base + L.off_state);
+    st->vec_floats = static_cast<int64_t>(L.vec_bytes / 4);
+    if (echo::launch_zero(st->state_base, 4 * st->vec_floats, static_cast<hipStream_t>(stream)) !=
+        hipSuccess) {
+      delete st;
+      return ECHO_ERR_HIP;
+    }
+  }
+  *out = st;
+  return ECHO_OK;
+}
+
+echo_status echo_stage1(const void* const* partials, echo_state* st, echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (st->cfg.numel == 0) return ECHO_OK;
+  if ((e = check_partials(partials, st)) != ECHO_OK) return e;
+  return run_stage1(partials, st, static_cast<hipStream_t>(stream));
+}
+
+echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (dir != ECHO_FWD && dir != ECHO_BWD) return ECHO_ERR_ARG;
+  if (st->cfg.numel == 0) return ECHO_OK;
+  return run_owner(st, static_cast<int>(dir), static_cast<hipStream_t>(stream));
+}
+
+echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (st->cfg.numel == 0) return ECHO_OK;
+  if ((e = check_out(out, st, nullptr)) != ECHO_OK) return e;
+  return run_decode(out, st, static_cast<hipStream_t>(stream));
+}
+
+echo_status echo_reduce(const void* const* partials, float* out, echo_state* st, echo_dir dir,
+                        echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (dir != ECHO_FWD && dir != ECHO_BWD) return ECHO_ERR_ARG;
+  if (st->cfg.numel == 0) return ECHO_OK;
+  if ((e = check_partials(partials, st)) != ECHO_OK) return e;
+  if ((e = check_out(out, st, partials)) != ECHO_OK) return e;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((e = run_stage1(partials, st, s)) != ECHO_OK) return e;
+  if ((e = run_owner(st, static_cast<int>(dir), s)) != ECHO_OK) return e;
+  return run_decode(out, st, s);
+}
+
+echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (dir_mask < 1 || dir_mask > 3) return ECHO_ERR_ARG;
+  if (st->cfg.numel == 0) return ECHO_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int d = 0; d < 2; ++d) {
+    if (!(dir_mask & (1 << d))) continue;
+    // m_fast[d] and m_slow[d] are adjacent: one fill covers both
+    if (echo::launch_zero(st->m_fast[d], 2 * st->vec_floats, s) != hipSuccess) return ECHO_ERR_HIP;
+  }
+  return ECHO_OK;
+}
+
+void echo_destroy_state(echo_state* st) { delete st; }
+
+echo_status echo_wire_bytes(const echo_state* st, uint64_t* rs_per_rank, uint64_t* ag_per_rank,
+                            uint64_t* bf16_allreduce_per_rank) {
+  if (st == nullptr) return ECHO_ERR_STATE;
+  if (rs_per_rank == nullptr || ag_per_rank == nullptr || bf16_allreduce_per_rank == nullptr)
+    return ECHO_ERR_ARG;
+  const uint64_t P = static_cast<uint64_t>(st->cfg.P);
+  const uint64_t N = static_cast<uint64_t>(st->cfg.numel);
+  const uint64_t n_g = N / ECHO_GROUP;
+  const uint64_t per = (n_g + P - 1) / P;
+  const uint64_t bytes_per_group = ECHO_GROUP / 2 + 4;  // 16 B of codes + one fp32 scale
+  uint64_t total = 0, smallest = UINT64_MAX, largest = 0;
+  for (uint64_t j = 0; j < P; ++j) {
+    const uint64_t lo = j * per < n_g ? j * per : n_g;
+    const uint64_t hi = (j + 1) * per < n_g ? (j + 1) * per : n_g;
+    const uint64_t b = (hi - lo) * bytes_per_group;
+    total += b;
+    smallest = b < smallest ? b : smallest;
+    largest = b > largest ? b : largest;
+  }
+  *rs_per_rank = total - smallest;  // a rank keeps its own segment
+  *ag_per_rank = (P - 1) * largest;
+  *bf16_allreduce_per_rank = (2 * (P - 1) * 2 * N) / P;
+  return ECHO_OK;
+}
+
+echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out) {
+  if (st == nullptr) return ECHO_ERR_STATE;
+  if (out == nullptr || (dir != ECHO_FWD && dir != ECHO_BWD)) return ECHO_ERR_ARG;
+  out->stage1_codes = st->codes1;
+  out->stage1_scales = st->scales1;
+  out->stage1_codes_stride = static_cast<size_t>(st->codes1_stride_bytes);
+  out->stage1_scales_stride = static_cast<size_t>(st->scales1_stride_bytes);
+  out->bcast_codes = st->codes2;
+  out->bcast_scales = st->scales2;
+  out->m_fast = st->m_fast[dir];
+  out->m_slow = st->m_slow[dir];
+  return ECHO_OK;
+}
+
+const char* echo_status_str(echo_status s) {
+  switch (s) {
+    case ECHO_OK: return "ok";
+    case ECHO_ERR_ARG: return "invalid argument (null, misaligned or overlapping pointer, bad enum)";
+    case ECHO_ERR_SHAPE: return "invalid shape (P outside [1,16], numel not a multiple of 32 or too large)";
+    case ECHO_ERR_DTYPE: return "invalid dtype";
+    case ECHO_ERR_WORKSPACE: return "workspace missing or too small";
+    case ECHO_ERR_STATE: return "null state, or another device is current";
+    case ECHO_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

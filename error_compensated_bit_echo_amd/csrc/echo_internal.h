@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace echo {
+
+constexpr int kMaxRanks = 16;
+constexpr int kGroup = 32;
+constexpr int kElemsPerLane = 8;   // one lane owns 8 consecutive elements
+constexpr int kLanesPerGroup = 4;  // an aligned quad of lanes owns one group
+constexpr int kBlock = 256;
+
+// Stage 1: quantize P rank partials into their payload buffers.
+struct Stage1Args {
+  const void* src[kMaxRanks];  // rank partials (bf16 or fp32), 16-byte aligned
+  uint32_t* codes;             // rank r at codes + r * codes_stride_words
+  float* scales;               // rank r at scales + r * scales_stride
+  int64_t codes_stride_words;  // uint32 words between ranks
+  int64_t scales_stride;       // floats between ranks
+  int64_t nchunk;              // N / 8
+};
+
+// Owner stage: sum, correct, re-quantize, update the compensator.
+struct OwnerArgs {
+  const uint32_t* codes1;
+  const float* scales1;
+  int64_t codes_stride_words;
+  int64_t scales_stride;
+  uint32_t* codes2;
+  float* scales2;
+  float* m_fast;
+  float* m_slow;
+  int64_t nchunk;
+  float beta_fast, omega_fast, beta_slow, omega_slow;
+};
+
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, hipStream_t s);
+hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t s);
+hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
+                         int64_t nchunk, hipStream_t s);
+hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
+
+}  // namespace echo

@@ -1,0 +1,164 @@
+/*
+ * echo.h -- C ABI of libecho: the Echo error-compensated int4 all-reduce on
+ * one AMD MI355X (gfx950), with the P tensor-parallel ranks emulated as P
+ * partial buffers in the GPU's HBM and the int4 payload buffers standing in
+ * for the wire.
+ *
+ * The method (described in prose, with no code or formulas, in the rit.work
+ * blog post "echo-4-bit-gpu-communication", sections «Почему обычное 4-битное
+ * суммирование портит модель» and «Как Echo возвращает ошибку в следующие
+ * вызовы», and in the heraldofai.com article «Come Echo permette ai modelli AI
+ * di grandi dimensioni di allenarsi più velocemente usando dati ultra-leggeri a
+ * 4 bit», section «Come Echo evita che gli errori si accumulino»):
+ *   - every rank cuts its partial sum into owner segments and sends them as
+ *     4-bit integers (here: groups of 32 elements, one fp32 scale per group);
+ *   - the owner of a segment decodes the P contributions, adds them in fp32,
+ *     adds a correction built from two smoothed estimates (fast, slow) of the
+ *     rounding error of its earlier calls, re-quantizes the sum to int4 and
+ *     broadcasts it, so an element is rounded at most twice whatever P is;
+ *   - from the fp32 sum the owner knows the error its own rounding just made
+ *     and folds it into the estimates; forward and backward keep separate
+ *     estimates.
+ *
+ * Arithmetic of one call, per element i of group g (fl = binary32 rounding):
+ *   stage 1 (every rank r):  a = max|x_r| over the group, s = fl(a/7),
+ *                            q = nearest code in [-7,7] to the exact x/s,
+ *                            ties to even (s == 0: all codes 0);
+ *   owner sum:               S = (((d_0 + d_1) + d_2) + ...), d_r = fl(q_r*s_r);
+ *   correction:              V = fl(S + fl(fl(0.5*m_fast) + fl(0.5*m_slow)));
+ *   stage 2:                 (q2, s2) = Q(V),  B = fl(q2*s2);
+ *   compensator:             e = fl(V - B),
+ *                            m <- fl(fl(beta*m) + fl((1-beta)*e)) for both;
+ *   output:                  out = B (fp32; no third rounding).
+ * With compensate == 0 the correction is zero and the state is not touched.
+ *
+ * Conventions for every entry point
+ *   - Device pointers point to the memory of the device that was current when
+ *     the state was created; that device must be current at every call.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is asynchronous; nothing synchronises the host.
+ *   - Every argument is validated before anything is enqueued: on any error
+ *     nothing is launched and the state is unchanged.  No exception crosses
+ *     the ABI; the library allocates no device memory and keeps no global
+ *     mutable state.
+ *   - A state may be used by one stream at a time (not re-entrant).
+ *   - Inputs must be finite; for NaN or Inf the results are unspecified.
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ECHO_OK = 0,
+  ECHO_ERR_ARG = 1,       /* null / misaligned / overlapping pointer, bad enum   */
+  ECHO_ERR_SHAPE = 2,     /* P outside [1,16], numel % 32 != 0 or too large      */
+  ECHO_ERR_DTYPE = 3,     /* unknown dtype                                        */
+  ECHO_ERR_WORKSPACE = 4, /* workspace missing or smaller than echo_workspace_bytes */
+  ECHO_ERR_STATE = 5,     /* null state, or called with another device current   */
+  ECHO_ERR_HIP = 6        /* a HIP runtime call or a kernel launch failed         */
+} echo_status;
+
+typedef enum { ECHO_F32 = 0, ECHO_BF16 = 1 } echo_dtype;
+typedef enum { ECHO_FWD = 0, ECHO_BWD = 1 } echo_dir;
+
+#define ECHO_MAX_RANKS 16
+#define ECHO_GROUP 32
+#define ECHO_MAX_NUMEL (((int64_t)1) << 36)
+
+typedef struct {
+  int32_t P;          /* emulated ranks, 1..ECHO_MAX_RANKS                        */
+  int64_t numel;      /* N, elements per rank partial; 0 <= N <= ECHO_MAX_NUMEL,  */
+                      /* N % 32 == 0 (N == 0 makes every call a no-op)            */
+  int32_t group;      /* quantization group, must be ECHO_GROUP (32)              */
+  echo_dtype dtype;   /* element type of every partial (fp32 or bfloat16)         */
+  int32_t compensate; /* 1 = Echo with error compensation, 0 = plain 2-rounding   */
+  float beta_fast;    /* smoothing of the fast estimate, in [0,1]; default 0.5    */
+  float beta_slow;    /* smoothing of the slow estimate, in [0,1]; default 0.95   */
+} echo_config;
+
+typedef struct echo_state echo_state; /* opaque host handle */
+
+typedef void* echo_stream_t; /* a hipStream_t */
+
+/* Bytes of device workspace a state needs: stage-1 payloads of the P ranks
+ * (codes N/2 B + scales N/8 B each), the broadcast payload, and the two
+ * compensator vectors of both directions (2 x 2 x 4N B), plus alignment
+ * slack.  Returns 0 for an invalid configuration and for N == 0. */
+size_t echo_workspace_bytes(const echo_config* cfg);
+
+/* Create a state over a caller-owned device workspace of `ws_bytes` bytes
+ * (at least echo_workspace_bytes(cfg); any alignment) and zero the
+ * compensator of both directions on `stream`.  The workspace must outlive
+ * the state; the library only carves it.  On success *out receives a host
+ * handle to free with echo_destroy_state.  Errors: ECHO_ERR_ARG (null cfg or
+ * out, bad compensate/beta), ECHO_ERR_SHAPE, ECHO_ERR_DTYPE,
+ * ECHO_ERR_WORKSPACE, ECHO_ERR_HIP. */
+echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_bytes,
+                            echo_stream_t stream, echo_state** out);
+
+/* One whole all-reduce: echo_stage1, then echo_owner on direction `dir`,
+ * then echo_decode.  partials: host array of P device pointers, each to N
+ * contiguous elements of cfg.dtype, 16-byte aligned, read-only for the call.
+ * out: device pointer to N fp32, 16-byte aligned, overlapping neither the
+ * partials nor the workspace; it receives the reduced tensor every rank would
+ * hold.  The state of `dir` advances in place.  Deterministic: identical
+ * inputs and state give bit-identical results. */
+echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
+                        echo_dir dir, echo_stream_t stream);
+
+/* Stage 1 on every rank: quantize each rank's partial to int4 codes and fp32
+ * group scales in the state's stage-1 payload buffers (the "wire"). */
+echo_status echo_stage1(const void* const* partials, echo_state* st, echo_stream_t stream);
+
+/* Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
+ * apply the correction of direction `dir`, re-quantize into the broadcast
+ * payload and update the compensator of `dir`. */
+echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream);
+
+/* Every rank's decode of the broadcast payload into `out` (N fp32). */
+echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream);
+
+/* Zero the compensator of the directions in dir_mask (1 = fwd, 2 = bwd,
+ * 3 = both), e.g. at the start of every pass over the layer stack.
+ * Uses a fill kernel (no memset node), so it may be captured in a graph. */
+echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream);
+
+/* Free the host handle (not the workspace).  NULL is accepted. */
+void echo_destroy_state(echo_state* st);
+
+/* Bytes one rank would send per call over a real interconnect: rs = the
+ * largest stage-1 payload share a rank sends to the other owners, ag = the
+ * largest broadcast an owner sends to the other ranks, bf16 = a ring
+ * all-reduce of the same message in bfloat16 (2(P-1)/P * 2N). */
+echo_status echo_wire_bytes(const echo_state* st, uint64_t* rs_per_rank, uint64_t* ag_per_rank,
+                            uint64_t* bf16_allreduce_per_rank);
+
+/* Device pointers into the workspace, for inspection, checkpoint and restore
+ * of the state (copy m_fast/m_slow out and back). */
+typedef struct {
+  const void* stage1_codes;    /* rank r: stage1_codes + r*stage1_codes_stride bytes, N/2 B  */
+  const float* stage1_scales;  /* rank r: (char*)stage1_scales + r*stage1_scales_stride, N/32 */
+  size_t stage1_codes_stride;  /* bytes between ranks                                      */
+  size_t stage1_scales_stride; /* bytes between ranks                                      */
+  const void* bcast_codes;     /* N/2 B: two's-complement nibbles, element 2k low nibble   */
+  const float* bcast_scales;   /* N/32 fp32                                                */
+  float* m_fast;               /* N fp32, compensator of the requested direction           */
+  float* m_slow;               /* N fp32                                                   */
+} echo_views;
+
+echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out);
+
+/* Static description of a status code. */
+const char* echo_status_str(echo_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECHO_H */

@@ -1,0 +1,107 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol,
+has the declared struct layout, and rejects bad arguments before touching a
+GPU.  No compute call is made here (no GPU in this environment)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from error_compensated_bit_echo_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "echo.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(echo_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("echo_workspace_bytes", "echo_init_state", "echo_reduce", "echo_stage1",
+              "echo_owner", "echo_decode", "echo_reset", "echo_destroy_state",
+              "echo_wire_bytes", "echo_debug_views", "echo_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_config_struct_layout():
+    # int32 P; (pad) int64 numel; int32 group; enum dtype; int32 compensate; float; float
+    assert ctypes.sizeof(B.EchoConfig) == 40
+    assert B.EchoConfig.numel.offset == 8
+    assert B.EchoConfig.beta_slow.offset == 32
+    assert ctypes.sizeof(B.EchoViews) == 64
+
+
+def _ws(cfg):
+    return B.load_library().echo_workspace_bytes(ctypes.byref(cfg))
+
+
+def test_workspace_bytes_formula():
+    for P, N, dt in ((2, 2048, "f32"), (8, 536870912, "bf16"), (3, 96, "bf16"), (16, 32, "bf16")):
+        cfg = B.EchoConfig.make(P, N, dt)
+        al = lambda x: (x + 255) // 256 * 256
+        want = P * (al(N // 2) + al(N // 8)) + al(N // 2) + al(N // 8) + 4 * al(4 * N) + 256
+        assert _ws(cfg) == want
+    assert _ws(B.EchoConfig.make(4, 0)) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("P", 0, B.ECHO_ERR_SHAPE), ("P", 17, B.ECHO_ERR_SHAPE),
+    ("numel", 33, B.ECHO_ERR_SHAPE), ("numel", -32, B.ECHO_ERR_SHAPE),
+    ("numel", (1 << 36) + 32, B.ECHO_ERR_SHAPE), ("group", 64, B.ECHO_ERR_SHAPE),
+    ("dtype", 7, B.ECHO_ERR_DTYPE), ("compensate", 2, B.ECHO_ERR_ARG),
+    ("beta_fast", -0.5, B.ECHO_ERR_ARG), ("beta_slow", float("nan"), B.ECHO_ERR_ARG),
+    ("beta_slow", 1.5, B.ECHO_ERR_ARG),
+])
+def test_init_rejects_bad_config_without_touching_the_gpu(field, value, status):
+    lib = B.load_library()
+    cfg = B.EchoConfig.make(4, 4096)
+    setattr(cfg, field, value)
+    assert _ws(cfg) == 0
+    h = ctypes.c_void_p()
+    assert lib.echo_init_state(ctypes.byref(cfg), None, 0, None, ctypes.byref(h)) == status
+    assert h.value is None
+
+
+def test_init_rejects_missing_or_small_workspace():
+    lib = B.load_library()
+    cfg = B.EchoConfig.make(4, 4096)
+    h = ctypes.c_void_p()
+    assert lib.echo_init_state(ctypes.byref(cfg), None, 10 ** 9, None, ctypes.byref(h)) == B.ECHO_ERR_WORKSPACE
+    assert lib.echo_init_state(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), _ws(cfg) - 1, None,
+                               ctypes.byref(h)) == B.ECHO_ERR_WORKSPACE
+    assert lib.echo_init_state(None, None, 0, None, ctypes.byref(h)) == B.ECHO_ERR_ARG
+    assert lib.echo_init_state(ctypes.byref(cfg), None, 0, None, None) == B.ECHO_ERR_ARG
+
+
+def test_calls_on_a_null_state_are_rejected():
+    lib = B.load_library()
+    assert lib.echo_owner(None, 0, None) == B.ECHO_ERR_STATE
+    assert lib.echo_reset(None, 3, None) == B.ECHO_ERR_STATE
+    assert lib.echo_decode(None, None, None) == B.ECHO_ERR_STATE
+    assert lib.echo_stage1(None, None, None) == B.ECHO_ERR_STATE
+    assert lib.echo_reduce(None, None, None, 0, None) == B.ECHO_ERR_STATE
+    x = ctypes.c_uint64()
+    assert lib.echo_wire_bytes(None, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == B.ECHO_ERR_STATE
+    assert lib.echo_debug_views(None, 0, None) == B.ECHO_ERR_STATE
+    lib.echo_destroy_state(None)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert B.echo_status_str(s)
+    assert "unknown" in B.echo_status_str(99)

@@ -1,0 +1,383 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: int4 codes and fp32 scales of both stages bit-exact; out, m_fast and
+m_slow within 1e-5 x the group's stage-2 scale (the kernels evaluate the same
+sequence of binary32 operations, so they are expected to match exactly, and
+the tests also count exact matches).
+"""
+import numpy as np
+import pytest
+
+from oracle import echo_oracle as eo
+from error_compensated_bit_echo_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+F64 = np.float64
+TOL = 1e-5
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _upload(raw, dtype, device):
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(raw, dtype=F32))
+    return [t[r].to(device).contiguous() for r in range(t.shape[0])]
+
+
+def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True):
+    torch = _torch()
+    import error_compensated_bit_echo_amd as E
+    cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1])
+    ws = torch.full((max(E.echo_workspace_bytes(cfg), 1),), 0xFF if poison else 0,
+                    dtype=torch.uint8, device=device)
+    return E.echo_init_state(cfg, ws)
+
+
+def _fetch(state, out, direction, lo=0, hi=None):
+    """Host copies of the GPU results for elements [lo, hi)."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    hi = state.numel if hi is None else hi
+    v = E.echo_debug_views(state, direction)
+    torch.cuda.synchronize()
+    g0, g1 = lo // 32, hi // 32
+    return {
+        "codes1": v["codes1"][:, lo // 2:hi // 2].cpu().numpy(),
+        "scales1": v["scales1"][:, g0:g1].cpu().numpy(),
+        "codes2": v["codes2"][lo // 2:hi // 2].cpu().numpy(),
+        "scales2": v["scales2"][g0:g1].cpu().numpy(),
+        "m_fast": v["m_fast"][lo:hi].cpu().numpy(),
+        "m_slow": v["m_slow"][lo:hi].cpu().numpy(),
+        "out": out[lo:hi].cpu().numpy(),
+    }
+
+
+def _compare(g, o, st_oracle, direction, compensate, where=""):
+    """Assert the parity bar; returns the number of float elements not bit-equal."""
+    assert np.array_equal(g["codes1"], o["codes1"]), f"stage-1 codes differ {where}"
+    assert np.array_equal(g["scales1"].view(np.uint32), o["scales1"].view(np.uint32)), \
+        f"stage-1 scales differ {where}"
+    assert np.array_equal(g["codes2"], o["codes2"]), f"stage-2 codes differ {where}"
+    assert np.array_equal(g["scales2"].view(np.uint32), o["scales2"].view(np.uint32)), \
+        f"stage-2 scales differ {where}"
+    s2 = np.repeat(o["scales2"].astype(F64), 32)
+    inexact = 0
+    pairs = [("out", o["out"])]
+    if compensate:
+        pairs += [("m_fast", st_oracle.m_fast[direction]), ("m_slow", st_oracle.m_slow[direction])]
+    for key, want in pairs:
+        got = g[key]
+        d = np.abs(got.astype(F64) - want.astype(F64))
+        assert np.all(d <= TOL * s2), f"{key} off by {d.max()} {where}"
+        inexact += int(np.count_nonzero(got != want))
+    return inexact
+
+
+# ---------------------------------------------------------------------------
+# tiny configuration: every call, every value
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_tiny_config_every_call(cuda, compensate):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.CONFIGS[1]
+    P, N = c["P"], synth.numel(1)
+    st = _state(P, N, "f32", compensate)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    inexact = 0
+    for t in range(c["calls"]):
+        raw, vals = synth.host_partials(1, 0, t)
+        E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, compensate=compensate)
+        inexact += _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}")
+    assert inexact == 0
+
+
+# ---------------------------------------------------------------------------
+# several tiles plus a ragged tail, every P, both dtypes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_multi_tile_ragged(cuda, P, dtype):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = 32 * (64 * 3 + 37) * 8 + 32 * 5  # several 2048-element tiles plus a ragged tail
+    st = _state(P, N, dtype)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(3):
+        raw, vals = synth.host_partials(2, 0, t, P=P, n=N, dtype=dtype)
+        E.echo_reduce(_upload(raw, dtype, cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"P={P} {dtype} call {t}") == 0
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def _tie_rich(P, N, rng):
+    x = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+    return x
+
+
+def _special_values(P, N, rng):
+    x = rng.standard_normal((P, N)).astype(F32)
+    g = x.reshape(P, -1, 32)
+    ng = g.shape[1]
+    g[:, 0] = 0.0                                     # all-zero group
+    g[:, 1 % ng] = -0.0                               # negative zeros
+    g[:, 2 % ng] *= F32(1e30)                         # huge
+    g[:, 3 % ng] *= F32(1e-30)                        # tiny but normal scale
+    g[:, 4 % ng] = (rng.integers(-80, 80, (P, 32)) * 2.0 ** -149).astype(F32)  # subnormal
+    g[:, 5 % ng] = (rng.integers(-3, 4, (P, 32)) * 2.0 ** -149).astype(F32)    # scale underflows
+    g[:, 6 % ng, 1:] = 0.0                            # single nonzero element
+    return g.reshape(P, N)
+
+
+@pytest.mark.parametrize("case", ["ties", "special", "one_group", "fewer_groups_than_ranks"])
+def test_edge_cases(cuda, case):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    rng = np.random.default_rng(5)
+    if case == "ties":
+        P, N, gen = 3, 32 * 300, _tie_rich
+    elif case == "special":
+        P, N, gen = 4, 32 * 64, _special_values
+    elif case == "one_group":
+        P, N, gen = 2, 32, lambda P, N, r: r.standard_normal((P, N)).astype(F32)
+    else:
+        P, N, gen = 16, 32 * 5, lambda P, N, r: r.standard_normal((P, N)).astype(F32)
+    st = _state(P, N, "f32")
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(6):
+        x = gen(P, N, rng)
+        E.echo_reduce(_upload(x, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(x, so, eo.FWD)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
+
+
+def test_empty_message_is_a_no_op(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    st = _state(4, 0, "bf16")
+    parts = [torch.empty(0, dtype=torch.bfloat16, device=cuda) for _ in range(4)]
+    out = torch.empty(0, dtype=torch.float32, device=cuda)
+    E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    E.echo_reset(st, 3)
+    assert E.echo_wire_bytes(st) == eo.wire_bytes(4, 0)
+    torch.cuda.synchronize()
+
+
+def test_beta_zero_error_feedback(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 2, 4096
+    st = _state(P, N, "bf16", beta=(0.0, 0.0))
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(5):
+        raw, vals = synth.host_partials(3, 0, t, P=P, n=N)
+        E.echo_reduce(_upload(raw, "bf16", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, beta_fast=0.0, beta_slow=0.0)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True) == 0
+
+
+# ---------------------------------------------------------------------------
+# state lifecycle: directions, reset, checkpoint/restore, determinism
+# ---------------------------------------------------------------------------
+def test_directions_reset_checkpoint_and_determinism(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 4, 32 * 1000
+    st = _state(P, N, "bf16")
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    fw = [synth.host_partials(4, 0, t, P=P, n=N) for t in range(6)]
+    bw = [synth.host_partials(4, 1, t, P=P, n=N) for t in range(6)]
+    snap = None
+    for t in range(6):
+        E.echo_reduce(_upload(fw[t][0], "bf16", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(fw[t][1], so, eo.FWD)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"fwd {t}") == 0
+        E.echo_reduce(_upload(bw[t][0], "bf16", cuda), out, st, E.ECHO_BWD)
+        o = eo.echo_call(bw[t][1], so, eo.BWD)
+        assert _compare(_fetch(st, out, 1), o, so, 1, True, f"bwd {t}") == 0
+        if t == 2:
+            v = E.echo_debug_views(st, E.ECHO_FWD)
+            snap = (v["m_fast"].clone(), v["m_slow"].clone(), so.copy())
+    # restore the forward state of call 2 and replay calls 3..5: bit-identical
+    v = E.echo_debug_views(st, E.ECHO_FWD)
+    v["m_fast"].copy_(snap[0])
+    v["m_slow"].copy_(snap[1])
+    so_r = snap[2]
+    for t in range(3, 6):
+        E.echo_reduce(_upload(fw[t][0], "bf16", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(fw[t][1], so_r, eo.FWD)
+        assert _compare(_fetch(st, out, 0), o, so_r, 0, True, f"replay {t}") == 0
+    # reset of the forward direction only
+    E.echo_reset(st, 1)
+    v = E.echo_debug_views(st, E.ECHO_FWD)
+    vb = E.echo_debug_views(st, E.ECHO_BWD)
+    torch.cuda.synchronize()
+    assert not torch.any(v["m_fast"]) and not torch.any(v["m_slow"])
+    assert np.array_equal(vb["m_fast"].cpu().numpy(), so.m_fast[1])
+    # determinism: the same call on the same state twice
+    parts = _upload(fw[0][0], "bf16", cuda)
+    E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    a = out.clone()
+    E.echo_reset(st, 1)
+    E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    assert torch.equal(a, out)
+
+
+def test_stage_entry_points_equal_reduce(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 8, 32 * 4096
+    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    parts = _upload(raw, "bf16", cuda)
+    s1, s2 = _state(P, N, "bf16"), _state(P, N, "bf16")
+    o1 = torch.empty(N, dtype=torch.float32, device=cuda)
+    o2 = torch.empty(N, dtype=torch.float32, device=cuda)
+    for _ in range(3):
+        E.echo_reduce(parts, o1, s1, E.ECHO_FWD)
+        E.echo_stage1(parts, s2)
+        E.echo_owner(s2, E.ECHO_FWD)
+        E.echo_decode(o2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(E.echo_debug_views(s1)["m_slow"], E.echo_debug_views(s2)["m_slow"])
+
+
+def test_graph_capture_replays_match_eager(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 8, 64 * 4096
+    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    parts = _upload(raw, "bf16", cuda)
+    se, sg = _state(P, N, "bf16"), _state(P, N, "bf16")
+    oe = torch.empty(N, dtype=torch.float32, device=cuda)
+    og = torch.empty(N, dtype=torch.float32, device=cuda)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.echo_reduce(parts, og, sg, E.ECHO_FWD)
+    torch.cuda.synchronize()
+    E.echo_reset(sg, 3)  # capture does not execute; start from a fresh state
+    for k in range(4):
+        E.echo_reduce(parts, oe, se, E.ECHO_FWD)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oe, og), f"replay {k}"
+        _ = (oe * 2).sum().item()  # unrelated eager work between replays
+
+
+# ---------------------------------------------------------------------------
+# argument errors are reported and launch nothing
+# ---------------------------------------------------------------------------
+def test_argument_errors_launch_nothing(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 2, 32 * 64
+    st = _state(P, N, "bf16")
+    raw, _ = synth.host_partials(1, 0, 0, P=P, n=N, dtype="bf16")
+    parts = _upload(raw, "bf16", cuda)
+    out = torch.zeros(N, dtype=torch.float32, device=cuda)
+    E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    torch.cuda.synchronize()
+    before = st.workspace.clone()
+    out_before = out.clone()
+    lib = E.load_library()
+    import ctypes
+    arr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in parts])
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    big = torch.zeros(N + 8, dtype=torch.float32, device=cuda)
+    from error_compensated_bit_echo_amd import binding as B
+    # misaligned output
+    assert lib.echo_reduce(arr, ctypes.c_void_p(big.data_ptr() + 4), st.handle, 0, s) == B.ECHO_ERR_ARG
+    # output inside the workspace
+    assert lib.echo_reduce(arr, ctypes.c_void_p(st.workspace.data_ptr() + 256), st.handle, 0, s) == B.ECHO_ERR_ARG
+    # output overlapping a partial
+    assert lib.echo_reduce(arr, ctypes.c_void_p(parts[1].data_ptr()), st.handle, 0, s) == B.ECHO_ERR_ARG
+    # a null partial, a misaligned partial, a bad direction, a bad reset mask
+    bad = (ctypes.c_void_p * P)(parts[0].data_ptr(), None)
+    assert lib.echo_reduce(bad, ctypes.c_void_p(out.data_ptr()), st.handle, 0, s) == B.ECHO_ERR_ARG
+    bad = (ctypes.c_void_p * P)(parts[0].data_ptr(), parts[1].data_ptr() + 2)
+    assert lib.echo_reduce(bad, ctypes.c_void_p(out.data_ptr()), st.handle, 0, s) == B.ECHO_ERR_ARG
+    assert lib.echo_reduce(arr, ctypes.c_void_p(out.data_ptr()), st.handle, 2, s) == B.ECHO_ERR_ARG
+    assert lib.echo_owner(st.handle, 5, s) == B.ECHO_ERR_ARG
+    assert lib.echo_reset(st.handle, 0, s) == B.ECHO_ERR_ARG
+    assert lib.echo_reset(st.handle, 4, s) == B.ECHO_ERR_ARG
+    # binding-level checks: dtype and count
+    with pytest.raises(B.EchoError):
+        E.echo_reduce([p.float() for p in parts], out, st)
+    with pytest.raises(B.EchoError):
+        E.echo_reduce(parts[:1], out, st)
+    torch.cuda.synchronize()
+    assert torch.equal(before, st.workspace)
+    assert torch.equal(out_before, out)
+
+
+def test_wire_bytes_match_the_oracle(cuda):
+    import error_compensated_bit_echo_amd as E
+    for P, N in ((2, 2048), (4, 2048 * 4096), (8, 64 * 4096), (3, 32 * 7), (16, 32 * 5)):
+        st = _state(P, N, "bf16", poison=False)
+        assert E.echo_wire_bytes(st) == eo.wire_bytes(P, N)
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations, in the launch configuration the benchmark uses:
+# sampled group-aligned windows (the numerics are independent per group and the
+# state per element, so a window of the oracle equals that window of the tensor)
+# ---------------------------------------------------------------------------
+def _windows(N, n_win, width, seed):
+    rng = np.random.default_rng(seed)
+    starts = {0, N - width}
+    while len(starts) < n_win:
+        starts.add(int(rng.integers(0, (N - width) // 32)) * 32)
+    return sorted(starts)
+
+
+def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.CONFIGS[cfg_id]
+    P, N = c["P"], synth.numel(cfg_id)
+    st = _state(P, N, c["dtype"], poison=False)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    wins = _windows(N, n_win, width, cfg_id)
+    so = {w: eo.OracleState(width) for w in wins}
+    parts = None
+    for t in range(calls):
+        for d in directions:
+            if parts is None or not same_partials:
+                parts = synth.device_partials(cfg_id, d, t, device=cuda)
+            E.echo_reduce(parts, out, st, d)
+            for w in wins:
+                host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
+                o = eo.echo_call(host, so[w], d)
+                g = _fetch(st, out, d, w, w + width)
+                assert _compare(g, o, so[w], d, True, f"cfg{cfg_id} call {t} dir {d} window {w}") == 0
+        print(f"cfg{cfg_id}: call {t} ok", flush=True)
+
+
+def test_prefill_config_full_size(cuda):
+    _windowed_run(cuda, 2, 24, (0,))
+
+
+def test_training_config_full_size_interleaved(cuda):
+    _windowed_run(cuda, 4, 12, (0, 1))
+
+
+def test_headline_config_full_size(cuda):
+    _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=8, width=1 << 15)
