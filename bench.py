@@ -62,13 +62,14 @@ def measured_traffic(kernel: str, workload: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(P: int, n_sample: int, seed_cfg: int = 5) -> dict:
-    """The CPU oracle, as it stands, timed on one call over a bounded sample."""
+def cpu_baseline(parts, n_sample: int) -> dict:
+    """The CPU oracle, as it stands, timed on one call over a bounded sample:
+    the first ``n_sample`` elements of each of the benchmark's own partials."""
     import numpy as np
-    from error_compensated_bit_echo_amd import synth
     from oracle import echo_oracle as eo
 
-    _, vals = synth.host_partials(seed_cfg, 0, 0, P=P, n=n_sample)
+    P = len(parts)
+    vals = np.stack([p[:n_sample].float().cpu().numpy() for p in parts])
     st = eo.OracleState(n_sample)
     t0 = time.perf_counter()
     eo.echo_call(vals, st, eo.FWD)
@@ -79,8 +80,8 @@ def cpu_baseline(P: int, n_sample: int, seed_cfg: int = 5) -> dict:
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"one call, P={P} x {n_sample} elements per rank ({n_sample / 536870912:.4g} of the "
-                  f"1 GiB message), same value distribution, compensation on; {dt:.2f} s; numpy "
+        "sample": f"one call, P={P} x the first {n_sample} elements of each rank's partial "
+                  f"({n_sample / 536870912:.4g} of the 1 GiB message), compensation on, fresh state; {dt:.2f} s; numpy "
                   f"elementwise ops on one core ({platform.processor() or platform.machine()}, "
                   f"os.cpu_count()={os.cpu_count()})",
     }
@@ -221,7 +222,7 @@ def main():
     }
     if not args.skip_cpu:
         print(f"# CPU oracle sample: P={P} x {args.cpu_sample}", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(P, args.cpu_sample)
+        line["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
