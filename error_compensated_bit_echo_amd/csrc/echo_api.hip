@@ -117,10 +117,13 @@ echo_status run_stage1(const void* const* partials, echo_state* st, hipStream_t 
 
 echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
   echo::OwnerArgs a{};
-  a.codes1 = st->codes1;
-  a.scales1 = st->scales1;
-  a.codes_stride_words = st->codes1_stride_bytes / 4;
-  a.scales_stride = st->scales1_stride_bytes / 4;
+  for (int r = 0; r < echo::kMaxRanks; ++r) {
+    const int rr = r < st->cfg.P ? r : 0;  // unused slots repeat rank 0
+    a.codes1[r] = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(st->codes1) +
+                                                    rr * st->codes1_stride_bytes);
+    a.scales1[r] = reinterpret_cast<const float*>(reinterpret_cast<const char*>(st->scales1) +
+                                                  rr * st->scales1_stride_bytes);
+  }
   a.codes2 = st->codes2;
   a.scales2 = st->scales2;
   a.m_fast = st->m_fast[dir];
@@ -135,7 +138,7 @@ echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
 }
 
 echo_status run_decode(float* out, const echo_state* st, hipStream_t s) {
-  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel / echo::kElemsPerLane, s) ==
+  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, s) ==
                  hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;

@@ -8,7 +8,7 @@ namespace echo {
 
 constexpr int kMaxRanks = 16;
 constexpr int kGroup = 32;
-constexpr int kElemsPerLane = 8;   // one lane owns 8 consecutive elements
+constexpr int kElemsPerLane = 8;   // stage 1 / owner: one lane owns 8 consecutive elements
 constexpr int kLanesPerGroup = 4;  // an aligned quad of lanes owns one group
 constexpr int kBlock = 256;
 
@@ -24,10 +24,8 @@ struct Stage1Args {
 
 // Owner stage: sum, correct, re-quantize, update the compensator.
 struct OwnerArgs {
-  const uint32_t* codes1;
-  const float* scales1;
-  int64_t codes_stride_words;
-  int64_t scales_stride;
+  const uint32_t* codes1[kMaxRanks];  // stage-1 codes of rank r
+  const float* scales1[kMaxRanks];    // stage-1 scales of rank r
   uint32_t* codes2;
   float* scales2;
   float* m_fast;
@@ -39,7 +37,7 @@ struct OwnerArgs {
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, hipStream_t s);
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t s);
 hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
-                         int64_t nchunk, hipStream_t s);
+                         int64_t numel, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
 }  // namespace echo

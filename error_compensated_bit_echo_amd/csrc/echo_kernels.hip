@@ -7,34 +7,50 @@
 // at most twice); heraldofai.com «Come Echo permette ai modelli AI…», section
 // «Come Echo evita che gli errori si accumulino».
 //
-// Layout shared by all kernels.  A lane owns 8 consecutive elements (a
-// "chunk"); the 4 lanes of an aligned quad own one 32-element group.  The
-// group absmax is combined across the quad with two DPP quad permutations, so
-// no LDS traffic is needed.  A chunk's 8 int4 codes are one 32-bit word
-// (element j of the chunk in bits 4j..4j+3), so a wavefront moves 256
-// contiguous bytes of codes per instruction and 1 KiB of bf16 input per
-// 128-bit load.
+// Stage-1 and owner layout.  A lane owns 8 consecutive elements (a "chunk");
+// the 4 lanes of an aligned quad own one 32-element group, whose absmax is
+// combined across the quad with two DPP quad permutations (no LDS traffic).
+// A chunk's 8 int4 codes are one 32-bit word (element j in bits 4j..4j+3).
+// Every kernel has a bounds-check-free path for whole tiles, which issues all
+// of a lane's global loads before the first use, and a guarded path that only
+// the last block of a launch takes.
 //
 // Every floating-point step is a separate IEEE binary32 operation with round
 // to nearest even: the file is compiled with contraction off (also pinned by
 // the pragma below) and with denormals preserved, so results are bit-identical
-// to any other faithful evaluation of the same sequence of operations.
-#include "echo_internal.h"
-
+// to any other faithful evaluation of the same sequence of operations.  The
+// only fused multiply-adds are those of the exact division by 7 (echo_div7.h)
+// and the sign-exact residual tests of the code choice (echo_quant.h); no value of the
+// method's arithmetic chain (sums, correction, error, estimates) is fused.
 #pragma clang fp contract(off)
+
+#include "echo_internal.h"
+#include "echo_div7.h"
+#include "echo_quant.h"
 
 namespace echo {
 namespace {
 
-// Codes whose quotient t = v * rcp(s) lies this close to a half-integer are
-// re-decided exactly.  |t - v/s| < 1.4 * 2^-20 (rcp: 1 ulp, product: 1/2 ulp,
-// |v/s| <= 7.0000005), so outside the guard band the rounded t is the correct
-// code; inside it the quotient is recomputed in binary64, where it decides
-// exactly (a non-tie quotient of two binary32 values is at least 2^-26 from a
-// half-integer, and a tie is representable).
-constexpr float kTieGuard = 0.5f - 0x1p-17f;
-// Below this scale rcp(s) may overflow; such groups take the exact path.
-constexpr float kTinyScale = 0x1p-100f;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Cache policy of a global access: plain, or non-temporal (streamed once).
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T v, T* p) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// Policy bits of the kernels' template parameter POL.
+constexpr int kNtIn = 1;         // stage 1: partials; owner: stage-1 codes; decode: codes
+constexpr int kNtStateLd = 2;    // owner: compensator loads
+constexpr int kNtStateSt = 4;    // owner: compensator stores
+constexpr int kNtOut = 8;        // decode: output stores; stage 1 / owner: code stores
 
 __device__ __forceinline__ float quad_max(float x) {
   // quad_perm(1,0,3,2) then quad_perm(2,3,0,1): all four lanes get the max.
@@ -46,7 +62,11 @@ __device__ __forceinline__ float quad_max(float x) {
   return fmaxf(x, y);
 }
 
-// Nearest code in [-7, 7] to the exact quotient v / s (s > 0), ties to even.
+// Nearest code in [-7, 7] to the exact quotient v / s (s > 0), ties to even,
+// in binary64: a quotient of two binary32 values that is not a tie lies at
+// least 2^-26 from a half-integer, far beyond binary64's rounding error, and
+// a tie is representable.  Used for the (rare) groups whose scale is nonzero
+// but below ECHO_TINY_SCALE, where rcp(s) could overflow.
 __device__ __forceinline__ int exact_code(float v, float s) {
   double q = __builtin_rint(static_cast<double>(v) / static_cast<double>(s));
   q = q > 7.0 ? 7.0 : q;
@@ -55,40 +75,35 @@ __device__ __forceinline__ int exact_code(float v, float s) {
 }
 
 // Codes of the 8 values a lane holds, for group scale s = fl(absmax / 7).
-// k receives the signed codes, the return value the packed nibbles.
-__device__ __forceinline__ uint32_t quantize8(const float (&v)[8], float s, int (&k)[8]) {
-  if (s >= kTinyScale) {
-    const float inv = __builtin_amdgcn_rcpf(s);
-    bool near_tie = false;
+// Returns the packed nibbles; kf receives the codes as floats.
+__device__ __forceinline__ uint32_t quantize8(const float (&v)[8], float s, float (&kf)[8]) {
+  uint32_t w = 0;
+  if (s >= ECHO_TINY_SCALE) {
+    const float inv = __builtin_amdgcn_rcpf(s);  // within 1 ulp of 1/s
+    const float h = 0.5f * s;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float t = v[j] * inv;
-      const float r = __builtin_rintf(t);
-      k[j] = static_cast<int>(r);
-      near_tie |= !(__builtin_fabsf(t - r) < kTieGuard);
-    }
-    if (near_tie) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float t = v[j] * inv;
-        const float r = __builtin_rintf(t);
-        if (!(__builtin_fabsf(t - r) < kTieGuard)) k[j] = exact_code(v[j], s);
-      }
+      const float f = echo_code_magic(v[j], s, inv, h);
+      kf[j] = f - ECHO_ROUND_MAGIC;  // exact
+      // shift the code's nibble in from the top: after 8 steps element j sits
+      // in bits 4j..4j+3
+      w = __builtin_amdgcn_alignbit(__float_as_uint(f), w, 4);
     }
   } else if (s > 0.0f) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) k[j] = exact_code(v[j], s);
+    for (int j = 0; j < 8; ++j) {
+      const int k = exact_code(v[j], s);
+      kf[j] = static_cast<float>(k);
+      w |= (static_cast<uint32_t>(k) & 15u) << (4 * j);
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) k[j] = 0;
+    for (int j = 0; j < 8; ++j) kf[j] = 0.0f;
   }
-  uint32_t w = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w |= (static_cast<uint32_t>(k[j]) & 15u) << (4 * j);
   return w;
 }
 
-// Signed code of element j (0..7) of a packed chunk word.
+// Signed code of element j (0..7) of a packed word.
 __device__ __forceinline__ int nibble(uint32_t w, int j) {
   return static_cast<int>(w << (28 - 4 * j)) >> 28;
 }
@@ -100,30 +115,70 @@ __device__ __forceinline__ float absmax8(const float (&v)[8]) {
   return m;
 }
 
+// A chunk of 8 input elements as loaded: 16 B of bf16 or 32 B of fp32.
 template <bool BF16>
-__device__ __forceinline__ void load_chunk(const void* base, int64_t c, float (&v)[8]) {
+struct Raw {
+  u32x4 q[BF16 ? 1 : 2];
+};
+
+template <bool BF16, bool NT>
+__device__ __forceinline__ Raw<BF16> load_raw(const void* base, int64_t c) {
+  const u32x4* p = static_cast<const u32x4*>(base) + c * (BF16 ? 1 : 2);
+  Raw<BF16> r;
+#pragma unroll
+  for (int i = 0; i < (BF16 ? 1 : 2); ++i) r.q[i] = ld<NT>(p + i);
+  return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen(const Raw<BF16>& r, float (&v)[8]) {
   if constexpr (BF16) {
-    const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + c * 16);
-    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(u[i] << 16);
-      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      v[2 * i] = __uint_as_float(r.q[0][i] << 16);
+      v[2 * i + 1] = __uint_as_float(r.q[0][i] & 0xFFFF0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const char*>(base) + c * 32);
-    const float4 a = p[0];
-    const float4 b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(r.q[i >> 2][i & 3]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Stage 1 (every rank): partial -> int4 codes + fp32 group scales.
-// grid = (ceil(nchunk / (256*U)), P); one block covers 256*U chunks of one rank.
+// grid = (ceil(nchunk / (256*U)), P); a block covers 256*U chunks of one rank,
+// chunk c0 + u*256 for lane c0.
 // ---------------------------------------------------------------------------
-template <bool BF16, int U>
+template <bool BF16, int U, int POL, bool FULL>
+__device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, float* scales,
+                                            int64_t c0, int64_t nchunk) {
+  Raw<BF16> raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
+    if (FULL || c < nchunk) {
+      raw[u] = load_raw<BF16, (POL & kNtIn) != 0>(src, c);
+    } else {
+#pragma unroll
+      for (int i = 0; i < (BF16 ? 1 : 2); ++i) raw[u].q[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
+    float v[8];
+    widen<BF16>(raw[u], v);
+    const float s = echo_div7(quad_max(absmax8(v)));
+    float kf[8];
+    const uint32_t w = quantize8(v, s, kf);
+    if (FULL || c < nchunk) {
+      st<(POL & kNtOut) != 0>(w, codes + c);
+      if ((threadIdx.x & 3) == 0) scales[c >> 2] = s;
+    }
+  }
+}
+
+template <bool BF16, int U, int POL>
 __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) {
   const int r = blockIdx.y;
   const void* src = a.src[0];
@@ -132,30 +187,12 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
     if (r == i) src = a.src[i];
   uint32_t* codes = a.codes + static_cast<int64_t>(r) * a.codes_stride_words;
   float* scales = a.scales + static_cast<int64_t>(r) * a.scales_stride;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * (kBlock * U) + threadIdx.x;
-
-  float v[U][8];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
-    if (c < a.nchunk) {
-      load_chunk<BF16>(src, c, v[u]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[u][j] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
-    const float s = quad_max(absmax8(v[u])) / 7.0f;  // IEEE division
-    int k[8];
-    const uint32_t w = quantize8(v[u], s, k);
-    if (c < a.nchunk) {
-      codes[c] = w;
-      if ((threadIdx.x & 3) == 0) scales[c >> 2] = s;
-    }
-  }
+  const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
+  const int64_t c0 = cb + threadIdx.x;
+  if (cb + kBlock * U <= a.nchunk)
+    stage1_tile<BF16, U, POL, true>(src, codes, scales, c0, a.nchunk);
+  else
+    stage1_tile<BF16, U, POL, false>(src, codes, scales, c0, a.nchunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -163,40 +200,44 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
 // order, correction, stage-2 quantization, error and both estimates.
 // grid = ceil(nchunk / 256); one lane per chunk.
 // ---------------------------------------------------------------------------
-template <int P, bool COMP>
-__global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const bool ok = c < a.nchunk;
+template <int P, bool COMP, int POL, bool FULL>
+__device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
+  const bool ok = FULL || c < a.nchunk;
   const int64_t g = c >> 2;
 
   uint32_t w[P];
   float s[P];
-  float mf[8], ms[8];
+  f32x4 mf4[2], ms4[2];
   if (ok) {
 #pragma unroll
     for (int r = 0; r < P; ++r) {
-      w[r] = a.codes1[r * a.codes_stride_words + c];
-      s[r] = a.scales1[r * a.scales_stride + g];
+      w[r] = ld<(POL & kNtIn) != 0>(a.codes1[r] + c);
+      s[r] = a.scales1[r][g];
     }
     if constexpr (COMP) {
-      const float4* pf = reinterpret_cast<const float4*>(a.m_fast + c * 8);
-      const float4* ps = reinterpret_cast<const float4*>(a.m_slow + c * 8);
-      const float4 f0 = pf[0], f1 = pf[1], s0 = ps[0], s1 = ps[1];
-      mf[0] = f0.x; mf[1] = f0.y; mf[2] = f0.z; mf[3] = f0.w;
-      mf[4] = f1.x; mf[5] = f1.y; mf[6] = f1.z; mf[7] = f1.w;
-      ms[0] = s0.x; ms[1] = s0.y; ms[2] = s0.z; ms[3] = s0.w;
-      ms[4] = s1.x; ms[5] = s1.y; ms[6] = s1.z; ms[7] = s1.w;
+      const f32x4* pf = reinterpret_cast<const f32x4*>(a.m_fast) + 2 * c;
+      const f32x4* ps = reinterpret_cast<const f32x4*>(a.m_slow) + 2 * c;
+      constexpr bool nt = (POL & kNtStateLd) != 0;
+      mf4[0] = ld<nt>(pf);
+      mf4[1] = ld<nt>(pf + 1);
+      ms4[0] = ld<nt>(ps);
+      ms4[1] = ld<nt>(ps + 1);
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < P; ++r) { w[r] = 0; s[r] = 0.0f; }
+    for (int r = 0; r < P; ++r) {
+      w[r] = 0;
+      s[r] = 0.0f;
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { mf[j] = 0.0f; ms[j] = 0.0f; }
+    for (int i = 0; i < 2; ++i) mf4[i] = ms4[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  float V[8];
+  float mf[8], ms[8], V[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    mf[j] = mf4[j >> 2][j & 3];
+    ms[j] = ms4[j >> 2][j & 3];
     float S = static_cast<float>(nibble(w[0], j)) * s[0];
 #pragma unroll
     for (int r = 1; r < P; ++r) S = S + static_cast<float>(nibble(w[r], j)) * s[r];
@@ -208,97 +249,138 @@ __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
     }
   }
 
-  const float s2 = quad_max(absmax8(V)) / 7.0f;  // IEEE division
-  int k[8];
-  const uint32_t w2 = quantize8(V, s2, k);
+  const float s2 = echo_div7(quad_max(absmax8(V)));
+  float kf[8];
+  const uint32_t w2 = quantize8(V, s2, kf);
   if (ok) {
-    a.codes2[c] = w2;
+    st<(POL & kNtOut) != 0>(w2, a.codes2 + c);
     if ((threadIdx.x & 3) == 0) a.scales2[g] = s2;
     if constexpr (COMP) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float B = static_cast<float>(k[j]) * s2;
+        const float B = kf[j] * s2;
         const float e = V[j] - B;
         mf[j] = a.beta_fast * mf[j] + a.omega_fast * e;
         ms[j] = a.beta_slow * ms[j] + a.omega_slow * e;
       }
-      float4* pf = reinterpret_cast<float4*>(a.m_fast + c * 8);
-      float4* ps = reinterpret_cast<float4*>(a.m_slow + c * 8);
-      pf[0] = make_float4(mf[0], mf[1], mf[2], mf[3]);
-      pf[1] = make_float4(mf[4], mf[5], mf[6], mf[7]);
-      ps[0] = make_float4(ms[0], ms[1], ms[2], ms[3]);
-      ps[1] = make_float4(ms[4], ms[5], ms[6], ms[7]);
+      f32x4* pf = reinterpret_cast<f32x4*>(a.m_fast) + 2 * c;
+      f32x4* ps = reinterpret_cast<f32x4*>(a.m_slow) + 2 * c;
+      constexpr bool nt = (POL & kNtStateSt) != 0;
+      st<nt>(f32x4{mf[0], mf[1], mf[2], mf[3]}, pf);
+      st<nt>(f32x4{mf[4], mf[5], mf[6], mf[7]}, pf + 1);
+      st<nt>(f32x4{ms[0], ms[1], ms[2], ms[3]}, ps);
+      st<nt>(f32x4{ms[4], ms[5], ms[6], ms[7]}, ps + 1);
     }
   }
 }
 
+template <int P, bool COMP, int POL>
+__global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
+  const int64_t cb = static_cast<int64_t>(blockIdx.x) * kBlock;
+  if (cb + kBlock <= a.nchunk)
+    owner_tile<P, COMP, POL, true>(a, cb + threadIdx.x);
+  else
+    owner_tile<P, COMP, POL, false>(a, cb + threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // Decode of the broadcast payload on every rank: out = fl(q2 * s2), fp32.
+// A lane owns 4 consecutive elements (unit i = elements 4i..4i+3, the low or
+// high half of code word i/2, group i/8), so each wavefront store writes 1 KiB
+// of contiguous output.  grid = ceil(n4 / (256*U)), unit i0 + u*256 for lane i0.
 // ---------------------------------------------------------------------------
-template <int U>
-__global__ __launch_bounds__(kBlock) void echo_unpack_k(const uint32_t* __restrict__ codes,
-                                                         const float* __restrict__ scales,
-                                                         float* __restrict__ out, int64_t nchunk) {
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * (kBlock * U) + threadIdx.x;
+template <int U, int POL, bool FULL>
+__device__ __forceinline__ void decode_tile(const uint32_t* codes, const float* scales, float* out,
+                                            int64_t i0, int64_t n4) {
   uint32_t w[U];
   float s[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
-    w[u] = 0;
-    s[u] = 0.0f;
-    if (c < nchunk) {
-      w[u] = codes[c];
-      s[u] = scales[c >> 2];
+    const int64_t i = i0 + static_cast<int64_t>(u) * kBlock;
+    if (FULL || i < n4) {
+      w[u] = ld<(POL & kNtIn) != 0>(codes + (i >> 1));
+      s[u] = scales[i >> 3];
+    } else {
+      w[u] = 0;
+      s[u] = 0.0f;
     }
   }
+  const int half = static_cast<int>(i0 & 1) * 16;  // same parity for every u
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
-    if (c < nchunk) {
-      float o[8];
+    const int64_t i = i0 + static_cast<int64_t>(u) * kBlock;
+    if (FULL || i < n4) {
+      const uint32_t h = w[u] >> half;
+      f32x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = static_cast<float>(nibble(w[u], j)) * s[u];
-      float4* p = reinterpret_cast<float4*>(out + c * 8);
-      p[0] = make_float4(o[0], o[1], o[2], o[3]);
-      p[1] = make_float4(o[4], o[5], o[6], o[7]);
+      for (int j = 0; j < 4; ++j) o[j] = static_cast<float>(nibble(h, j)) * s[u];
+      st<(POL & kNtOut) != 0>(o, reinterpret_cast<f32x4*>(out) + i);
     }
   }
+}
+
+template <int U, int POL>
+__global__ __launch_bounds__(kBlock) void echo_unpack_k(const uint32_t* __restrict__ codes,
+                                                         const float* __restrict__ scales,
+                                                         float* __restrict__ out, int64_t n4) {
+  const int64_t ib = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
+  if (ib + kBlock * U <= n4)
+    decode_tile<U, POL, true>(codes, scales, out, ib + threadIdx.x, n4);
+  else
+    decode_tile<U, POL, false>(codes, scales, out, ib + threadIdx.x, n4);
 }
 
 __global__ __launch_bounds__(kBlock) void echo_zero_k(float* __restrict__ p, int64_t n) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x) * 4;
   if (i + 4 <= n) {
-    *reinterpret_cast<float4*>(p + i) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    *reinterpret_cast<f32x4*>(p + i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   } else {
     for (int64_t t = i; t < n; ++t) p[t] = 0.0f;
   }
 }
 
+// Tuning of the launches (unroll and cache policy), chosen by measurement.
 constexpr int kStage1Unroll = 2;
+constexpr int kStage1Pol = kNtIn | kNtOut;
+constexpr int kOwnerPol = 0;
 constexpr int kDecodeUnroll = 2;
+constexpr int kDecodePol = kNtOut;
 
-template <int P>
+template <int P, int POL = kOwnerPol>
 hipError_t owner_p(const OwnerArgs& a, bool comp, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock - 1) / kBlock;
   if (comp)
-    hipLaunchKernelGGL((echo_owner_k<P, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_owner_k<P, false>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, false, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int U, int POL = kStage1Pol>
+hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
+  const int64_t blocks = (a.nchunk + kBlock * U - 1) / (kBlock * U);
+  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(P));
+  if (bf16)
+    hipLaunchKernelGGL((echo_quant_pack_k<true, U, POL>), grid, dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((echo_quant_pack_k<false, U, POL>), grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int U, int POL = kDecodePol>
+hipError_t decode_u(const uint32_t* codes, const float* scales, float* out, int64_t numel,
+                    hipStream_t s) {
+  const int64_t n4 = numel / 4;
+  const int64_t blocks = (n4 + kBlock * U - 1) / (kBlock * U);
+  hipLaunchKernelGGL((echo_unpack_k<U, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+                     codes, scales, out, n4);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
-  constexpr int U = kStage1Unroll;
-  const int64_t blocks = (a.nchunk + kBlock * U - 1) / (kBlock * U);
-  const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(P));
-  if (bf16)
-    hipLaunchKernelGGL((echo_quant_pack_k<true, U>), grid, dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL((echo_quant_pack_k<false, U>), grid, dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+  return stage1_u<kStage1Unroll>(a, P, bf16, s);
 }
 
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t s) {
@@ -323,13 +405,9 @@ hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t 
   }
 }
 
-hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out, int64_t nchunk,
+hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out, int64_t numel,
                          hipStream_t s) {
-  constexpr int U = kDecodeUnroll;
-  const int64_t blocks = (nchunk + kBlock * U - 1) / (kBlock * U);
-  hipLaunchKernelGGL((echo_unpack_k<U>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
-                     codes, scales, out, nchunk);
-  return hipGetLastError();
+  return decode_u<kDecodeUnroll>(codes, scales, out, numel, s);
 }
 
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s) {
