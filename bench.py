@@ -118,6 +118,179 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
     return rec
 
 
+# ---------------------------------------------------------------------------
+# the other workloads: latency, effective bandwidth and accuracy reports
+# ---------------------------------------------------------------------------
+CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4}
+CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+
+
+def _graph_us(E, torch, parts, out, st, direction, reps):
+    """Per-call GPU time of a captured echo_reduce, replayed ``reps`` times."""
+    E.echo_reduce(parts, out, st, direction)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.echo_reduce(parts, out, st, direction)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev], g
+
+
+def _wall_us(E, torch, parts, out, st, direction, reps):
+    """Host-clock time per call of ``reps`` back-to-back eager calls."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        E.echo_reduce(parts, out, st, direction)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / reps
+
+
+def stream_report(name, E, synth, torch, dev) -> dict:
+    """tiny / prefill / training: the configuration's calls on fresh partials,
+    each call's output added to a residual stream h (fp32) next to the exact
+    stream h* = sum of all partials (float64); compensation on and off."""
+    import numpy as np
+
+    cid = CONFIG_IDS[name]
+    c = synth.CONFIGS[cid]
+    P, N, dtype = c["P"], synth.numel(cid), c["dtype"]
+    dirs = (0, 1) if name == "training" else (0,)
+    b_in = 4 if dtype == "f32" else 2
+
+    def parts_for(d, t):
+        if dtype == "f32":
+            raw, _ = synth.host_partials(cid, d, t)
+            return [torch.from_numpy(np.ascontiguousarray(raw[r])).to(dev) for r in range(P)]
+        return synth.device_partials(cid, d, t, device=dev)
+
+    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, dtype, compensate=(m == "on")), device=dev)
+          for m in ("on", "off")}
+    out = torch.empty(N, dtype=torch.float32, device=dev)
+    h = {(m, d): torch.zeros(N, dtype=torch.float32, device=dev) for m in st for d in dirs}
+    hx = {d: torch.zeros(N, dtype=torch.float64, device=dev) for d in dirs}
+    evs = []
+    for t in range(c["calls"]):
+        for d in dirs:
+            parts = parts_for(d, t)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            E.echo_reduce(parts, out, st["on"], d)
+            b.record()
+            evs.append((a, b))
+            h[("on", d)] += out
+            E.echo_reduce(parts, out, st["off"], d)
+            h[("off", d)] += out
+            for p in parts:
+                hx[d] += p.double()
+    torch.cuda.synchronize()
+    eager = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    err = {}
+    for d in dirs:
+        ref = hx[d]
+        scale = ref.pow(2).mean().sqrt().item()
+        for m in ("on", "off"):
+            e = (h[(m, d)].double() - ref).pow(2).mean().sqrt().item()
+            err[f"{'fwd' if d == 0 else 'bwd'}_{m}"] = {"rms_err": e, "rel_rms_err": e / scale}
+    wall = _wall_us(E, torch, parts, out, st["on"], dirs[-1], 20)
+    gst = E.echo_init_state(E.EchoConfig.make(P, N, dtype), device=dev)
+    gout = torch.empty_like(out)
+    graph, _ = _graph_us(E, torch, parts, gout, gst, dirs[-1], 50)
+    alg = N * (P * (b_in + 1.25) + 21.25)
+    med = _pct(graph, 0.5)
+    return {
+        "config": name, "P": P, "numel_per_rank": N, "input_dtype": dtype,
+        "calls": c["calls"] * len(dirs), "alg_bytes_per_call": int(alg),
+        "cache_resident": bool(alg + P * N * b_in < CACHE_BYTES),
+        "us_per_call": {"eager_events_median": round(_pct(eager, 0.5), 2),
+                        "eager_events_p90": round(_pct(eager, 0.9), 2),
+                        "eager_wall_back_to_back": round(wall, 2),
+                        "graph_median": round(med, 2), "graph_p90": round(_pct(graph, 0.9), 2)},
+        "GBps_alg_graph": round(alg / (med * 1e-6) / 1e9, 1),
+        "residual_stream_error_after_all_calls": err,
+    }
+
+
+def decode_report(E, synth, torch, dev) -> dict:
+    """The decode-shaped chain: 128 layers, P = 8, [64, 4096] bf16 partials from
+    a pre-norm random map per layer; three chains from the same h_0 (Echo with
+    compensation, without, and an exact all-reduce in float64).  Per-call
+    latency of echo_reduce eager and replayed from a captured graph."""
+    c = synth.DECODE_CHAIN
+    P, rows, hd, L = 8, c["rows"], c["hidden"], c["layers"]
+    N = rows * hd
+    h0 = synth.decode_h0(dev)
+    h = {"on": h0.clone(), "off": h0.clone()}
+    hx = h0.double()
+    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=(m == "on")), device=dev)
+          for m in ("on", "off")}
+    out = torch.empty(N, dtype=torch.float32, device=dev)
+    # graph path: fixed partial buffers, its own state fed the same partials as "on"
+    pbuf = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    gst = E.echo_init_state(E.EchoConfig.make(P, N, "bf16"), device=dev)
+    gout = torch.empty_like(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.echo_reduce(pbuf, gout, gst, E.ECHO_FWD)
+    torch.cuda.synchronize()
+    E.echo_reset(gst, 3)
+    ev_e, ev_g, rel = [], [], {}
+    graph_equal = True
+    for layer in range(1, L + 1):
+        w = synth.decode_weight(layer, dev)
+        for m in ("on", "off"):
+            parts = synth.decode_partials(h[m], w, P)
+            if m == "on":
+                for b, p in zip(pbuf, parts):
+                    b.copy_(p)
+                a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a0.record()
+                g.replay()
+                a1.record()
+                ev_g.append((a0, a1))
+                b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b0.record()
+                E.echo_reduce(parts, out, st[m], E.ECHO_FWD)
+                b1.record()
+                ev_e.append((b0, b1))
+                graph_equal &= bool(torch.equal(out, gout))
+            else:
+                E.echo_reduce(parts, out, st[m], E.ECHO_FWD)
+            h[m] += out.view(rows, hd)
+        px = synth.decode_partials(hx.float(), w, P)
+        hx += sum(p.double() for p in px).view(rows, hd)
+        if layer & (layer - 1) == 0 or layer == L:
+            scale = hx.pow(2).mean().sqrt().item()
+            rel[str(layer)] = {m: round((h[m].double() - hx).pow(2).mean().sqrt().item() / scale, 8)
+                               for m in ("on", "off")}
+    torch.cuda.synchronize()
+    eager = [a.elapsed_time(b) * 1e3 for a, b in ev_e]
+    graph = [a.elapsed_time(b) * 1e3 for a, b in ev_g]
+    alg = N * (P * 3.25 + 21.25)
+    return {
+        "config": "decode", "P": P, "numel_per_rank": N, "input_dtype": "bf16", "layers": L,
+        "alg_bytes_per_call": int(alg), "cache_resident": True,
+        "us_per_call": {"eager_events_median": round(_pct(eager, 0.5), 2),
+                        "eager_events_p90": round(_pct(eager, 0.9), 2),
+                        "graph_median": round(_pct(graph, 0.5), 2),
+                        "graph_p90": round(_pct(graph, 0.9), 2)},
+        "graph_replay_equals_eager_every_layer": graph_equal,
+        "rel_rms_err_vs_exact_allreduce_chain": rel,
+    }
+
+
 def cpu_baseline(parts, n_sample: int) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
     the first ``n_sample`` elements of each of the benchmark's own partials."""
@@ -156,6 +329,9 @@ def main():
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of this benchmark, then exit")
     ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
+    ap.add_argument("--config", choices=sorted(CONFIG_IDS) + ["all"],
+                    help="instead of the 1 GiB headline, report latency, bandwidth and accuracy of "
+                         "another workload (one JSON line each)")
     args = ap.parse_args()
 
     if args.ingest_counters:
@@ -182,6 +358,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.config:
+        names = ["tiny", "prefill", "decode", "training"] if args.config == "all" else [args.config]
+        for name in names:
+            print(f"# config {name}", file=sys.stderr, flush=True)
+            rep = (decode_report(E, synth, torch, dev) if name == "decode"
+                   else stream_report(name, E, synth, torch, dev))
+            print(json.dumps(rep), flush=True)
+            torch.cuda.empty_cache()
+        return
     cfg_id = 5
     c = synth.CONFIGS[cfg_id]
     P, N = c["P"], synth.numel(cfg_id)

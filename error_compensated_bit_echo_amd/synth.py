@@ -121,3 +121,46 @@ def device_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | Non
         out.append(x if c["dtype"] == "f32" else x.to(torch.bfloat16))
         del x
     return out
+
+
+# ----------------------------------------------------------------------------
+# decode-shaped chain: 128 layers of a synthetic residual stream
+# ----------------------------------------------------------------------------
+DECODE_CHAIN = dict(rows=64, hidden=4096, layers=128, h0_std=0.02)
+
+
+def decode_h0(device="cuda"):
+    """Initial residual stream h_0 ~ N(0, 0.02^2), [64, 4096] float32."""
+    import torch
+
+    c = DECODE_CHAIN
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(3, 0, 0, 0))
+    return torch.randn(c["rows"], c["hidden"], generator=g, device=device) * c["h0_std"]
+
+
+def decode_weight(layer: int, device="cuda"):
+    """Layer map W_l ~ N(0, 1)/sqrt(4096) as bfloat16 [4096, 4096], seeded per layer."""
+    import torch
+
+    hd = DECODE_CHAIN["hidden"]
+    g = torch.Generator(device=device)
+    g.manual_seed(3 * 10**9 + 9 * 10**8 + layer)
+    w = torch.randn(hd, hd, generator=g, device=device)
+    w.mul_(1.0 / hd ** 0.5)
+    return w.to(torch.bfloat16)
+
+
+def decode_partials(h, w, P: int):
+    """The P rank partials of one layer: with a = bf16(h / rms(h)) (pre-norm, per
+    row), rank r holds bf16(gamma * (a[:, S_r] @ W[S_r, :])), S_r its slice of
+    4096/P input columns, gamma = 0.02 * sqrt(P).  The product is taken in fp32.
+    Returns P contiguous bfloat16 vectors of rows*hidden elements."""
+    import torch
+
+    a = (h / h.pow(2).mean(dim=-1, keepdim=True).sqrt()).to(torch.bfloat16).float()
+    gamma = 0.02 * P ** 0.5
+    cols = h.shape[1] // P
+    wf = w.float()
+    return [(gamma * (a[:, r * cols:(r + 1) * cols] @ wf[r * cols:(r + 1) * cols, :]))
+            .to(torch.bfloat16).reshape(-1).contiguous() for r in range(P)]
