@@ -19,9 +19,11 @@
 // to nearest even: the file is compiled with contraction off (also pinned by
 // the pragma below) and with denormals preserved, so results are bit-identical
 // to any other faithful evaluation of the same sequence of operations.  The
-// only fused multiply-adds are those of the exact division by 7 (echo_div7.h)
-// and the sign-exact residual tests of the code choice (echo_quant.h); no value of the
-// method's arithmetic chain (sums, correction, error, estimates) is fused.
+// only fused multiply-adds are those of the exact division by 7 (echo_div7.h),
+// the sign-exact residual tests of the code choice and the dequantization
+// fma((q + 8), s, -8s), which rounds once to exactly fl(q * s) (echo_quant.h);
+// no other value of the method's arithmetic chain (sums, correction, error,
+// estimates) is fused.
 #pragma clang fp contract(off)
 
 #include "echo_internal.h"
@@ -106,6 +108,39 @@ __device__ __forceinline__ uint32_t quantize8(const float (&v)[8], float s, floa
 // Signed code of element j (0..7) of a packed word.
 __device__ __forceinline__ int nibble(uint32_t w, int j) {
   return static_cast<int>(w << (28 - 4 * j)) >> 28;
+}
+
+// Each rank's contribution d[r][j] = fl(q_r,j * s_r) for the 8 elements of a
+// chunk.  Flipping the sign bit of every nibble turns code q into q + 8 in
+// [0, 15], a byte after one mask, which one conversion turns into a float;
+// echo_dequant_fma then gives fl(q * s) exactly in one instruction (two fewer
+// than extract, convert and multiply).  Scales of 2^124 and above, which only
+// inputs near the top of the binary32 range produce, take the direct product.
+template <int P>
+__device__ __forceinline__ void dequant_ranks(const uint32_t (&w)[P], const float (&s)[P],
+                                              float (&d)[P][8]) {
+  float smax = s[0];
+#pragma unroll
+  for (int r = 1; r < P; ++r) smax = fmaxf(smax, s[r]);
+  if (__builtin_expect(smax < ECHO_DEQUANT_FMA_MAX_SCALE, 1)) {
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      const uint32_t x = w[r] ^ 0x88888888u;
+      const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6
+      const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+      const float m8 = -8.0f * s[r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d[r][2 * j] = echo_dequant_fma(static_cast<float>((lo >> (8 * j)) & 0xFFu), s[r], m8);
+        d[r][2 * j + 1] = echo_dequant_fma(static_cast<float>((hi >> (8 * j)) & 0xFFu), s[r], m8);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d[r][j] = static_cast<float>(nibble(w[r], j)) * s[r];
+  }
 }
 
 __device__ __forceinline__ float absmax8(const float (&v)[8]) {
@@ -233,14 +268,16 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
     for (int i = 0; i < 2; ++i) mf4[i] = ms4[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
+  float d[P][8];
+  dequant_ranks<P>(w, s, d);
   float mf[8], ms[8], V[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     mf[j] = mf4[j >> 2][j & 3];
     ms[j] = ms4[j >> 2][j & 3];
-    float S = static_cast<float>(nibble(w[0], j)) * s[0];
+    float S = d[0][j];
 #pragma unroll
-    for (int r = 1; r < P; ++r) S = S + static_cast<float>(nibble(w[r], j)) * s[r];
+    for (int r = 1; r < P; ++r) S = S + d[r][j];
     if constexpr (COMP) {
       const float corr = 0.5f * mf[j] + 0.5f * ms[j];
       V[j] = S + corr;

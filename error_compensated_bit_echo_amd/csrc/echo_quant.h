@@ -52,4 +52,17 @@ ECHO_QUANT_QUAL float echo_code_magic(float v, float s, float inv, float h) {
   return f;
 }
 
+// Dequantization fl(q * s) of a code q in [-8, 7] given as u = q + 8 in
+// [0, 15] (which one byte-to-float conversion produces from a nibble stored
+// with its sign bit flipped): the exact value (q + 8) * s - 8 * s equals q * s,
+// so one fused multiply-add rounds it once, to exactly fl(q * s), provided
+// m8 = -8 * s is finite (s < 2^124 is enough).  The one difference is the sign
+// of a zero: with s = 0 and q < 0, fl(q * s) is -0 and the fma gives +0; a
+// zero scale only comes from an all-zero group, whose codes are all 0.
+#define ECHO_DEQUANT_FMA_MAX_SCALE 0x1p124f
+
+ECHO_QUANT_QUAL float echo_dequant_fma(float u, float s, float m8) {
+  return __builtin_fmaf(u, s, m8);
+}
+
 #endif  // ECHO_QUANT_H

@@ -173,3 +173,60 @@ def test_code_choice_matches_exact_round_half_even(tmp_path):
     nbad, n, ntie = (int(x) for x in res.stdout.split())
     assert ntie > 1_000_000 and n > 500_000_000
     assert res.returncode == 0 and nbad == 0, f"{nbad} wrong codes out of {n}"
+
+
+DEQUANT_CHECK = r"""
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+#define ECHO_QUANT_QUAL static inline
+#include "echo_quant.h"
+
+int main(void) {
+  long long bad = 0, n = 0;
+  /* every 61st non-negative binary32 below 2^124 (all binades, subnormals
+     included), every code q in [-8, 7] given as u = q + 8 */
+  const uint32_t top = 0x7D800000u; /* 2^124 */
+  #pragma omp parallel for reduction(+:bad, n) schedule(static, 1 << 16)
+  for (long long i = 0; i < (long long)top; i += 61) {
+    uint32_t b = (uint32_t)i;
+    float s;
+    memcpy(&s, &b, 4);
+    if (!(s < ECHO_DEQUANT_FMA_MAX_SCALE)) continue;
+    const float m8 = -8.0f * s;
+    for (int u = 0; u < 16; ++u) {
+      /* a zero scale only ever carries code 0 (all-zero group): -0 vs +0 */
+      if (s == 0.0f && u != 8) continue;
+      volatile float q = (float)(u - 8);
+      const float want = q * s;                /* fl(q * s): one rounding */
+      const float got = echo_dequant_fma((float)u, s, m8);
+      uint32_t x, y;
+      memcpy(&x, &want, 4);
+      memcpy(&y, &got, 4);
+      bad += (x != y);
+      n++;
+    }
+  }
+  printf("%lld %lld\n", bad, n);
+  return bad != 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_dequant_fma_equals_rounded_product(tmp_path):
+    """fma(q + 8, s, -8 s) is exactly fl(q * s) for every code and the sampled
+    scales (a zero scale is checked with code 0 only, the one code it carries)."""
+    src = tmp_path / "deq.c"
+    exe = tmp_path / "deq"
+    src.write_text(DEQUANT_CHECK)
+    flags = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", f"-I{CSRC}"]
+    if _has_fma():
+        flags.append("-mfma")
+    subprocess.run(["gcc", *flags, str(src), "-o", str(exe), "-lm"], check=True)
+    env = dict(os.environ)
+    env.setdefault("OMP_NUM_THREADS", str(min(8, os.cpu_count() or 1)))
+    res = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=600)
+    bad, n = (int(x) for x in res.stdout.split())
+    assert n > 500_000_000
+    assert res.returncode == 0 and bad == 0, f"{bad} of {n} differ"
