@@ -282,12 +282,17 @@ def _windows(N, n_win, width, seed):
     return sorted(starts)
 
 
-def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14):
+def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
+                  P=None, N=None, compensate=True):
+    """The configuration's calls at full size; the oracle checks sampled windows.
+    P and N override the configuration's rank count and message size (same
+    value distribution and dtype)."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     c = synth.CONFIGS[cfg_id]
-    P, N = c["P"], synth.numel(cfg_id)
-    st = _state(P, N, c["dtype"], poison=False)
+    P = c["P"] if P is None else P
+    N = synth.numel(cfg_id) if N is None else N
+    st = _state(P, N, c["dtype"], compensate=compensate, poison=False)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     wins = _windows(N, n_win, width, cfg_id)
     so = {w: eo.OracleState(width) for w in wins}
@@ -295,14 +300,16 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     for t in range(calls):
         for d in directions:
             if parts is None or not same_partials:
-                parts = synth.device_partials(cfg_id, d, t, device=cuda)
+                parts = None
+                parts = synth.device_partials(cfg_id, d, t, P=P, n=N, device=cuda)
             E.echo_reduce(parts, out, st, d)
             for w in wins:
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
-                o = eo.echo_call(host, so[w], d)
+                o = eo.echo_call(host, so[w], d, compensate=compensate)
                 g = _fetch(st, out, d, w, w + width)
-                assert _compare(g, o, so[w], d, True, f"cfg{cfg_id} call {t} dir {d} window {w}") == 0
-        print(f"cfg{cfg_id}: call {t} ok", flush=True)
+                assert _compare(g, o, so[w], d, compensate,
+                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}") == 0
+        print(f"cfg{cfg_id} P={P} N={N}: call {t} ok", flush=True)
 
 
 def test_prefill_config_full_size(cuda):
@@ -315,3 +322,18 @@ def test_training_config_full_size_interleaved(cuda):
 
 def test_headline_config_full_size(cuda):
     _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=8, width=1 << 15)
+
+
+def test_largest_rank_count_large_message(cuda):
+    """P = 16 (the most ranks the library takes), 2^27 bf16 elements per rank."""
+    _windowed_run(cuda, 5, 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
+
+
+def test_fp32_partials_of_2GiB(cuda):
+    """fp32 partials of 2^29 elements (2 GiB each, so byte offsets pass 2^31)."""
+    _windowed_run(cuda, 1, 3, (0,), P=2, N=1 << 29, n_win=8, width=1 << 14)
+
+
+def test_full_size_without_compensation(cuda):
+    """The plain two-rounding all-reduce (state untouched) at the prefill size."""
+    _windowed_run(cuda, 2, 4, (0,), compensate=False)
