@@ -1,0 +1,71 @@
+"""Strength of the oracle's pins: plausible mistakes planted in a copy of the
+oracle (a dropped term, a wrong sign, a swapped constant, another rounding or
+summation order, a wrong wire layout...) must each make the pin suite fail.
+
+Each mutant is written into a temporary copy of the repository's oracle and
+test files and the pins (tests/test_oracle_pins.py) run there in a child
+process; the repository's own oracle is never modified.  CPU only.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# name -> (text in oracle/echo_oracle.py, replacement)
+MUTANTS = {
+    "correction dropped": ("vv = acc + cc", "vv = acc"),
+    "error measured as S - B": ("rr = vv - bb", "rr = acc - bb"),
+    "error sign flipped": ("rr = vv - bb", "rr = bb - vv"),
+    "slow weight fl(0.05) instead of fl(1 - beta)": (
+        "wf, ws = F32(1) - bf, F32(1) - bs", "wf, ws = F32(1) - bf, F32(0.05)"),
+    "fast and slow beta swapped": (
+        "bf, bs = F32(beta_fast), F32(beta_slow)", "bf, bs = F32(beta_slow), F32(beta_fast)"),
+    "correction weights 1/2 and 1": (
+        "cc = F32(0.5) * mf[e0:e1] + F32(0.5) * ms[e0:e1]",
+        "cc = F32(0.5) * mf[e0:e1] + ms[e0:e1]"),
+    "fast estimate with the slow coefficients": (
+        "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bs * mf[e0:e1] + ws * rr"),
+    "scale absmax/8": ("s = a / F32(QMAX)", "s = a / F32(8)"),
+    "codes clipped to [-8, 8]": ("k = np.clip(k, -QMAX, QMAX)", "k = np.clip(k, -8, 8)"),
+    "ties away from zero": (
+        "k = np.rint(quot)", "k = np.sign(quot) * np.floor(np.abs(quot) + 0.5)"),
+    "code from the rounded quotient fl(v/s)": (
+        "quot = v[nz].astype(F64) / s[nz].astype(F64)[:, None]",
+        "quot = (v[nz] / s[nz][:, None]).astype(F64)"),
+    "ranks summed in reverse order": (
+        "for r in range(P):\n            d = dequantize_groups",
+        "for r in reversed(range(P)):\n            d = dequantize_groups"),
+    "nibbles in the other order": (
+        "return (u[0::2] | (u[1::2] << np.uint8(4))).astype(np.uint8)",
+        "return (u[1::2] | (u[0::2] << np.uint8(4))).astype(np.uint8)"),
+    "owner segments split by floor": (
+        "per = -(-n_groups // P) if P > 0 else 0", "per = max(1, n_groups // P) if P > 0 else 0"),
+    "zero group given a tiny scale": (
+        "s = a / F32(QMAX)  # binary32 division, round to nearest even",
+        "s = np.maximum(a / F32(QMAX), F32(1e-30))"),
+    "estimate biased by a tiny constant": (
+        "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bf * mf[e0:e1] + wf * rr + F32(1e-30)"),
+}
+# Equivalent rewrites, which no test can or should catch: fl(q*s) computed in
+# binary64 and rounded once (q*s has at most 28 significant bits, so the
+# binary64 product is exact) is fl(q*s) itself.
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(tmp_path, name):
+    src = open(os.path.join(ROOT, "oracle", "echo_oracle.py")).read()
+    old, new = MUTANTS[name]
+    assert old in src, f"mutation site not found: {old!r}"
+    for sub in ("oracle", "tests", "error_compensated_bit_echo_amd"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), tmp_path)
+    (tmp_path / "oracle" / "echo_oracle.py").write_text(src.replace(old, new, 1))
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-m", "not gpu",
+                          "tests/test_oracle_pins.py"],
+                         cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"mutant '{name}' passed every pin:\n{res.stdout[-500:]}"
