@@ -121,7 +121,7 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
 # ---------------------------------------------------------------------------
 # the other workloads: latency, effective bandwidth and accuracy reports
 # ---------------------------------------------------------------------------
-CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4}
+CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0}
 CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
 
 
@@ -305,6 +305,48 @@ def decode_report(E, synth, torch, dev) -> dict:
     }
 
 
+def tp_report(torch, dev) -> dict:
+    """Echo inside a tensor-parallel MLP stack (8 layers, P = 4, 2048 tokens,
+    hidden 4096, ffn 16384): one training step (forward + backward, 8 Echo calls
+    per direction) with Echo, Echo without compensation and exact all-reduces;
+    errors of the loss and the gradients against the exact step, step time and
+    the time of the Echo calls inside it."""
+    from error_compensated_bit_echo_amd import tp
+
+    T, H, F, P, L = 2048, 4096, 16384, 4, 8
+    model = tp.TPMLPStack(L, H, F, P, seed=21, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(22)
+    x0 = torch.randn(T, H, generator=g, device=dev)
+    target = torch.randn(T, H, generator=g, device=dev)
+    res, ms = {}, {}
+    for mode in ("exact", "echo", "echo_off"):
+        group = tp.EchoGroup(P, T * H, mode=mode, device=dev)
+        tp.train_step(model, group, x0, target)  # warm-up
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        res[mode] = tp.train_step(model, group, x0, target)
+        b.record()
+        torch.cuda.synchronize()
+        ms[mode] = a.elapsed_time(b)
+
+    def rel(x, y):
+        return float((x - y).float().norm() / y.float().norm())
+
+    errs = {}
+    for mode in ("echo", "echo_off"):
+        loss, dx, dw = res[mode]
+        errs[mode] = {"loss_rel_err": abs(float(loss - res["exact"][0])) / float(res["exact"][0]),
+                      "dx0_rel_err": rel(dx, res["exact"][1]),
+                      "dW_rel_err_mean": sum(rel(p, q) for p, q in zip(dw, res["exact"][2])) / len(dw),
+                      "dW_rel_err_max": max(rel(p, q) for p, q in zip(dw, res["exact"][2]))}
+    return {"config": "tp", "P": P, "layers": L, "tokens": T, "hidden": H, "ffn": F,
+            "echo_calls_per_step": {"fwd": L, "bwd": L},
+            "step_ms": {k: round(v, 3) for k, v in ms.items()},
+            "errors_vs_exact_allreduce": errs}
+
+
 def cpu_baseline(parts, n_sample: int) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
     the first ``n_sample`` elements of each of the benchmark's own partials."""
@@ -373,11 +415,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config:
-        names = ["tiny", "prefill", "decode", "training"] if args.config == "all" else [args.config]
+        names = ["tiny", "prefill", "decode", "training", "tp"] if args.config == "all" else [args.config]
         for name in names:
             print(f"# config {name}", file=sys.stderr, flush=True)
-            rep = (decode_report(E, synth, torch, dev) if name == "decode"
-                   else stream_report(name, E, synth, torch, dev))
+            if name == "decode":
+                rep = decode_report(E, synth, torch, dev)
+            elif name == "tp":
+                rep = tp_report(torch, dev)
+            else:
+                rep = stream_report(name, E, synth, torch, dev)
             print(json.dumps(rep), flush=True)
             torch.cuda.empty_cache()
         return

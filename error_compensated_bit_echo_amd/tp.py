@@ -1,0 +1,176 @@
+"""Echo inside tensor-parallel layers: autograd operators over one emulated TP group.
+
+A tensor-parallel block needs two collectives (rit.work blog post
+"echo-4-bit-gpu-communication", «Почему обычное 4-битное суммирование портит
+модель»: the layer's matrices are split over the GPUs, each computes a part of
+the result and an all-reduce sums the parts; in training it repeats on the
+backward pass):
+
+* ``g`` after a row-parallel product: forward sums the P partial outputs (an
+  Echo all-reduce on the forward compensator state); backward hands the
+  replicated gradient to every rank unchanged.
+* ``f`` before a column-parallel product: forward gives every rank the same
+  input; backward sums the P partial input gradients (an Echo all-reduce on
+  the backward compensator state).
+
+Forward and backward keep separate compensator state (same page, «Как Echo
+возвращает ошибку в следующие вызовы»); one state per residual stream, shared
+by all the block's calls of one pass and reset at the start of each step.
+The P ranks are P tensors on one GPU; every reduction runs in libecho's
+kernels through the C ABI.  A ``mode`` of "exact" replaces both collectives by
+a plain sum (the bf16 wire values added in fp32), for comparison.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+from . import binding as B
+
+
+class EchoGroup:
+    """P emulated ranks sharing one Echo state (forward and backward directions)
+    for messages of ``numel`` elements in bfloat16 on the wire."""
+
+    def __init__(self, P: int, numel: int, mode: str = "echo", device=None, record: bool = False):
+        import torch
+
+        if mode not in ("echo", "echo_off", "exact"):
+            raise ValueError(f"mode {mode!r}")
+        self.P, self.numel, self.mode = P, numel, mode
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.state = None
+        if mode != "exact":
+            cfg = B.EchoConfig.make(P, numel, "bf16", compensate=(mode == "echo"))
+            self.state = B.echo_init_state(cfg, device=self.device)
+        # when recording, every reduction appends (direction, [partials], out)
+        self.record = record
+        self.log: List[tuple] = []
+
+    def reset(self):
+        """Start of a step: fresh compensator for both directions."""
+        if self.state is not None:
+            B.echo_reset(self.state, 3)
+        self.log.clear()
+
+    def allreduce(self, partials, direction: int):
+        """Sum of the P bf16 partials ([..] contiguous, numel each) as fp32."""
+        import torch
+
+        parts = [p.contiguous() for p in partials]
+        if self.mode == "exact":
+            out = torch.zeros(self.numel, dtype=torch.float32, device=self.device)
+            for p in parts:
+                out += p.reshape(-1).float()
+        else:
+            out = torch.empty(self.numel, dtype=torch.float32, device=self.device)
+            B.echo_reduce([p.reshape(-1) for p in parts], out, self.state, direction)
+        if self.record:
+            self.log.append((direction, [p.detach().clone() for p in parts], out.detach().clone()))
+        return out
+
+
+def _fns():
+    import torch
+
+    class ReduceForward(torch.autograd.Function):
+        """g: forward all-reduce of the P partial outputs; backward identity per rank."""
+
+        @staticmethod
+        def forward(ctx, group: EchoGroup, shape, *partials):
+            ctx.dtypes = [p.dtype for p in partials]
+            return group.allreduce([p.to(torch.bfloat16) for p in partials], B.ECHO_FWD).view(shape)
+
+        @staticmethod
+        def backward(ctx, grad):
+            g = grad.contiguous()
+            return (None, None) + tuple(g.reshape(-1).to(dt) for dt in ctx.dtypes)
+
+    class ReduceBackward(torch.autograd.Function):
+        """f: forward replicates the input to every rank; backward all-reduces the
+        P input gradients."""
+
+        @staticmethod
+        def forward(ctx, group: EchoGroup, x):
+            ctx.group, ctx.shape, ctx.dtype = group, x.shape, x.dtype
+            return tuple(x.clone() for _ in range(group.P))
+
+        @staticmethod
+        def backward(ctx, *grads):
+            parts = [g.to(torch.bfloat16).contiguous() for g in grads]
+            out = ctx.group.allreduce(parts, B.ECHO_BWD)
+            return None, out.view(ctx.shape).to(ctx.dtype)
+
+    return ReduceForward, ReduceBackward
+
+
+_FNS = None
+
+
+def reduce_forward(group: EchoGroup, partials, shape):
+    """g(partials): all-reduce on the forward state; gradient passes through."""
+    global _FNS
+    if _FNS is None:
+        _FNS = _fns()
+    return _FNS[0].apply(group, shape, *partials)
+
+
+def replicate(group: EchoGroup, x):
+    """f(x): P copies of x; their gradients are all-reduced on the backward state."""
+    global _FNS
+    if _FNS is None:
+        _FNS = _fns()
+    return _FNS[1].apply(group, x)
+
+
+class TPMLPStack:
+    """L pre-norm MLP blocks, each split over P ranks: W1 column-parallel
+    ([H, F] in P slices of F/P columns), W2 row-parallel ([F, H] in P slices of
+    F/P rows); x <- x + g(sum_r gelu(f(a)_r @ W1_r) @ W2_r), a = rmsnorm(x).
+    Weights are fp32 and seeded; the products are taken in fp32 and each
+    rank's partial output is rounded to bf16 (the wire dtype)."""
+
+    def __init__(self, layers: int, hidden: int, ffn: int, P: int, seed: int = 0, device=None):
+        import torch
+
+        if ffn % P:
+            raise ValueError("ffn must be divisible by P")
+        self.L, self.H, self.F, self.P = layers, hidden, ffn, P
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        self.w1, self.w2 = [], []
+        for _ in range(layers):
+            w1 = torch.randn(hidden, ffn, generator=g, device=dev) / hidden ** 0.5
+            w2 = torch.randn(ffn, hidden, generator=g, device=dev) / ffn ** 0.5 * 0.5
+            self.w1.append([w1[:, r * ffn // P:(r + 1) * ffn // P].contiguous().requires_grad_()
+                            for r in range(P)])
+            self.w2.append([w2[r * ffn // P:(r + 1) * ffn // P, :].contiguous().requires_grad_()
+                            for r in range(P)])
+
+    def parameters(self):
+        return [w for layer in self.w1 + self.w2 for w in layer]
+
+    def forward(self, x, group: EchoGroup):
+        import torch
+
+        for l in range(self.L):
+            a = x * torch.rsqrt(x.pow(2).mean(dim=-1, keepdim=True) + 1e-6)
+            xs = replicate(group, a)
+            partials = [(torch.nn.functional.gelu(xs[r] @ self.w1[l][r]) @ self.w2[l][r]).to(torch.bfloat16)
+                        for r in range(self.P)]
+            x = x + reduce_forward(group, [p.reshape(-1) for p in partials], x.shape)
+        return x
+
+
+def train_step(model: TPMLPStack, group: EchoGroup, x0, target):
+    """One forward + backward; returns (loss, dL/dx0, [dL/dW...])."""
+    import torch
+
+    group.reset()
+    x = x0.detach().clone().requires_grad_()
+    for p in model.parameters():
+        p.grad = None
+    y = model.forward(x, group)
+    loss = torch.nn.functional.mse_loss(y, target)
+    loss.backward()
+    return loss.detach(), x.grad.detach(), [p.grad.detach() for p in model.parameters()]
