@@ -34,18 +34,20 @@ COPY_FLOATS = 1 << 29  # 2 GiB of fp32 for the copy kernel
 KERNEL_KEYS = {"stage1": "echo_quant_pack_k", "owner": "echo_owner_k", "decode": "echo_unpack_k"}
 
 
-def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool) -> dict:
+def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool, group: int = 32) -> dict:
     """Bytes each stage must move per call (reads + writes of HBM)."""
-    k1 = P * N * (b_in + 0.625)                # read partials; write codes + scales
-    k2 = N * (0.625 * P + 0.625)               # read P payload segments; write broadcast payload
+    pl = 0.5 + 4.0 / group                     # payload bytes per element: codes + scales
+    k1 = P * N * (b_in + pl)                   # read partials; write codes + scales
+    k2 = N * (pl * P + pl)                     # read P payload segments; write broadcast payload
     if compensate:
         k2 += 16.0 * N                         # read and write m_fast, m_slow
-    k3 = N * (0.625 + 4.0)                     # read broadcast payload; write fp32 out
+    k3 = N * (pl + 4.0)                        # read broadcast payload; write fp32 out
     return {"stage1": k1, "owner": k2, "decode": k3}
 
 
-def workload_tag(comp: bool) -> str:
-    return f"1GiB-P8-bf16-{'comp' if comp else 'nocomp'}"
+def workload_tag(comp: bool, group: int = 32) -> str:
+    tag = f"1GiB-P8-bf16-{'comp' if comp else 'nocomp'}"
+    return tag if group == 32 else f"{tag}-g{group}"
 
 
 def kernel_source_hash() -> str:
@@ -378,6 +380,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-comp", action="store_true", help="plain two-rounding int4 all-reduce")
+    ap.add_argument("--group", type=int, default=32, choices=(32, 64, 128),
+                    help="elements per scale (32; 64 and 128 are variants)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 25,
                     help="elements per rank in the CPU oracle's timed sample")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle leg")
@@ -391,7 +395,7 @@ def main():
     args = ap.parse_args()
 
     if args.ingest_counters:
-        rec = ingest_counters(*args.ingest_counters, workload=workload_tag(not args.no_comp),
+        rec = ingest_counters(*args.ingest_counters, workload=workload_tag(not args.no_comp, args.group),
                               command=args.counter_command)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
@@ -433,7 +437,8 @@ def main():
     comp = not args.no_comp
     print(f"# generating {P} x {N} bf16 partials on the device", file=sys.stderr, flush=True)
     parts = synth.device_partials(cfg_id, 0, 0, device=dev)
-    cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp)
+    G = args.group
+    cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp, group=G)
     st = E.echo_init_state(cfg, device=dev)
     out = torch.empty(N, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -470,7 +475,7 @@ def main():
     print(f"# timed {K} calls: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
-    alg = algorithmic_bytes(P, N, 2, comp)
+    alg = algorithmic_bytes(P, N, 2, comp, G)
     total_alg = sum(alg.values())
     kernels = {}
     for k, ms in kern_ms.items():
@@ -479,7 +484,7 @@ def main():
                       "frac": round(alg[k] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     dom = max(kern_ms, key=kern_ms.get)
     achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    workload = workload_tag(comp)
+    workload = workload_tag(comp, G)
     traffic = measured_traffic(dom, workload)
 
     # a plain streaming copy kernel of 2 GiB (torch's elementwise x*1, read 2 GiB,
@@ -516,10 +521,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "1 GiB bf16 message per rank (536,870,912 elements), P=8 emulated ranks, "
-                        "group 32, absmax/7 fp32 scales, compensation " + ("on" if comp else "off") +
+                        f"group {G}, absmax/7 fp32 scales, compensation " + ("on" if comp else "off") +
                         ", same partials every call, reset -> warm-up -> reset -> timed calls",
             "P": P, "numel_per_rank": N, "input_dtype": "bf16", "wire": "int4 codes + fp32 group scales",
-            "output_dtype": "f32", "group": 32,
+            "output_dtype": "f32", "group": G,
         },
         "roofline": {
             "bound": "hbm",

@@ -42,11 +42,11 @@ class EchoConfig(ctypes.Structure):
 
     @classmethod
     def make(cls, P: int, numel: int, dtype: str = "bf16", compensate: bool = True,
-             beta_fast: float = 0.5, beta_slow: float = 0.95) -> "EchoConfig":
+             beta_fast: float = 0.5, beta_slow: float = 0.95, group: int = ECHO_GROUP) -> "EchoConfig":
         d = {"f32": ECHO_F32, "float32": ECHO_F32, "bf16": ECHO_BF16, "bfloat16": ECHO_BF16}
         if dtype not in d:
             raise EchoError(ECHO_ERR_DTYPE, f"dtype {dtype!r}")
-        return cls(P, numel, ECHO_GROUP, d[dtype], int(bool(compensate)), beta_fast, beta_slow)
+        return cls(P, numel, group, d[dtype], int(bool(compensate)), beta_fast, beta_slow)
 
 
 class EchoViews(ctypes.Structure):
@@ -249,15 +249,15 @@ def echo_wire_bytes(state: EchoState) -> dict:
 
 
 def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
-    """Views (no copies) into the workspace: stage-1 codes [P, N/2] and scales [P, N/32],
-    broadcast codes [N/2] and scales [N/32], and the m_fast / m_slow vectors of ``direction``."""
+    """Views (no copies) into the workspace: stage-1 codes [P, N/2] and scales [P, N/group],
+    broadcast codes [N/2] and scales [N/group], and the m_fast / m_slow vectors of ``direction``."""
     import torch
     v = EchoViews()
     _check(load_library().echo_debug_views(state.handle, int(direction), ctypes.byref(v)),
            "echo_debug_views")
     ws = state.workspace
     base = ws.data_ptr()
-    N, P = state.cfg.numel, state.cfg.P
+    N, P, G = state.cfg.numel, state.cfg.P, state.cfg.group
     if N == 0:
         e8 = torch.empty(0, dtype=torch.uint8, device=state.device)
         e32 = torch.empty(0, dtype=torch.float32, device=state.device)
@@ -270,12 +270,12 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
 
     cs, ss = v.stage1_codes_stride, v.stage1_scales_stride
     codes1 = sl(v.stage1_codes, P * cs).view(P, cs)[:, :N // 2]
-    scales1 = sl(v.stage1_scales, P * ss).view(torch.float32).view(P, ss // 4)[:, :N // 32]
+    scales1 = sl(v.stage1_scales, P * ss).view(torch.float32).view(P, ss // 4)[:, :N // G]
     return {
         "codes1": codes1,
         "scales1": scales1,
         "codes2": sl(v.bcast_codes, N // 2),
-        "scales2": sl(v.bcast_scales, N // 8).view(torch.float32),
+        "scales2": sl(v.bcast_scales, 4 * (N // G)).view(torch.float32),
         "m_fast": sl(v.m_fast, 4 * N).view(torch.float32),
         "m_slow": sl(v.m_slow, 4 * N).view(torch.float32),
     }

@@ -41,12 +41,13 @@ Layout make_layout(const echo_config& c) {
   const size_t P = static_cast<size_t>(c.P);
   Layout L{};
   L.codes1_stride = align_up(N / 2);
-  L.scales1_stride = align_up(N / 8);
+  const size_t scale_bytes = 4 * (N / static_cast<size_t>(c.group));
+  L.scales1_stride = align_up(scale_bytes);
   L.off_codes1 = 0;
   L.off_scales1 = L.off_codes1 + P * L.codes1_stride;
   L.off_codes2 = L.off_scales1 + P * L.scales1_stride;
   L.off_scales2 = L.off_codes2 + align_up(N / 2);
-  L.off_state = L.off_scales2 + align_up(N / 8);
+  L.off_state = L.off_scales2 + align_up(scale_bytes);
   L.vec_bytes = align_up(4 * N);
   L.total = L.off_state + 4 * L.vec_bytes;
   return L;
@@ -55,8 +56,8 @@ Layout make_layout(const echo_config& c) {
 echo_status check_cfg(const echo_config* c) {
   if (c == nullptr) return ECHO_ERR_ARG;
   if (c->P < 1 || c->P > ECHO_MAX_RANKS) return ECHO_ERR_SHAPE;
-  if (c->numel < 0 || c->numel > ECHO_MAX_NUMEL || c->numel % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
-  if (c->group != ECHO_GROUP) return ECHO_ERR_SHAPE;
+  if (c->group != 32 && c->group != 64 && c->group != 128) return ECHO_ERR_SHAPE;
+  if (c->numel < 0 || c->numel > ECHO_MAX_NUMEL || c->numel % c->group != 0) return ECHO_ERR_SHAPE;
   if (c->dtype != ECHO_F32 && c->dtype != ECHO_BF16) return ECHO_ERR_DTYPE;
   if (c->compensate != 0 && c->compensate != 1) return ECHO_ERR_ARG;
   if (!(c->beta_fast >= 0.0f && c->beta_fast <= 1.0f)) return ECHO_ERR_ARG;  // also rejects NaN
@@ -111,8 +112,9 @@ echo_status run_stage1(const void* const* partials, echo_state* st, hipStream_t 
   a.codes_stride_words = st->codes1_stride_bytes / 4;
   a.scales_stride = st->scales1_stride_bytes / 4;
   a.nchunk = st->cfg.numel / echo::kElemsPerLane;
-  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, s) == hipSuccess ? ECHO_OK
-                                                                                        : ECHO_ERR_HIP;
+  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, s) == hipSuccess
+             ? ECHO_OK
+             : ECHO_ERR_HIP;
 }
 
 echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
@@ -133,12 +135,13 @@ echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
   a.omega_fast = 1.0f - st->cfg.beta_fast;  // fl(1 - beta)
   a.beta_slow = st->cfg.beta_slow;
   a.omega_slow = 1.0f - st->cfg.beta_slow;
-  return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, s) == hipSuccess ? ECHO_OK
-                                                                                   : ECHO_ERR_HIP;
+  return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, st->cfg.group, s) == hipSuccess
+             ? ECHO_OK
+             : ECHO_ERR_HIP;
 }
 
 echo_status run_decode(float* out, const echo_state* st, hipStream_t s) {
-  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, s) ==
+  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, st->cfg.group, s) ==
                  hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
@@ -256,9 +259,10 @@ echo_status echo_wire_bytes(const echo_state* st, uint64_t* rs_per_rank, uint64_
     return ECHO_ERR_ARG;
   const uint64_t P = static_cast<uint64_t>(st->cfg.P);
   const uint64_t N = static_cast<uint64_t>(st->cfg.numel);
-  const uint64_t n_g = N / ECHO_GROUP;
+  const uint64_t G = static_cast<uint64_t>(st->cfg.group);
+  const uint64_t n_g = N / G;
   const uint64_t per = (n_g + P - 1) / P;
-  const uint64_t bytes_per_group = ECHO_GROUP / 2 + 4;  // 16 B of codes + one fp32 scale
+  const uint64_t bytes_per_group = G / 2 + 4;  // codes + one fp32 scale
   uint64_t total = 0, smallest = UINT64_MAX, largest = 0;
   for (uint64_t j = 0; j < P; ++j) {
     const uint64_t lo = j * per < n_g ? j * per : n_g;
@@ -292,7 +296,8 @@ const char* echo_status_str(echo_status s) {
   switch (s) {
     case ECHO_OK: return "ok";
     case ECHO_ERR_ARG: return "invalid argument (null, misaligned or overlapping pointer, bad enum)";
-    case ECHO_ERR_SHAPE: return "invalid shape (P outside [1,16], numel not a multiple of 32 or too large)";
+    case ECHO_ERR_SHAPE:
+      return "invalid shape (P outside [1,16], group not 32/64/128, numel not a multiple of the group or too large)";
     case ECHO_ERR_DTYPE: return "invalid dtype";
     case ECHO_ERR_WORKSPACE: return "workspace missing or too small";
     case ECHO_ERR_STATE: return "null state, or another device is current";

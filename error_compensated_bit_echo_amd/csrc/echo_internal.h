@@ -9,7 +9,6 @@ namespace echo {
 constexpr int kMaxRanks = 16;
 constexpr int kGroup = 32;
 constexpr int kElemsPerLane = 8;   // stage 1 / owner: one lane owns 8 consecutive elements
-constexpr int kLanesPerGroup = 4;  // an aligned quad of lanes owns one group
 constexpr int kBlock = 256;
 
 // Stage 1: quantize P rank partials into their payload buffers.
@@ -34,10 +33,11 @@ struct OwnerArgs {
   float beta_fast, omega_fast, beta_slow, omega_slow;
 };
 
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, hipStream_t s);
-hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t s);
+// group: 32, 64 or 128 elements per scale
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s);
+hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, hipStream_t s);
 hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
-                         int64_t numel, hipStream_t s);
+                         int64_t numel, int group, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
 }  // namespace echo

@@ -8,8 +8,9 @@
 // «Come Echo evita che gli errori si accumulino».
 //
 // Stage-1 and owner layout.  A lane owns 8 consecutive elements (a "chunk");
-// the 4 lanes of an aligned quad own one 32-element group, whose absmax is
-// combined across the quad with two DPP quad permutations (no LDS traffic).
+// the LPG = group/8 aligned lanes of a group (4 for the default group of 32;
+// 8 and 16 for the group-size variants 64 and 128) combine its absmax with
+// DPP lane permutations (no LDS traffic).
 // A chunk's 8 int4 codes are one 32-bit word (element j in bits 4j..4j+3).
 // Every kernel has a bounds-check-free path for whole tiles, which issues all
 // of a lane's global loads before the first use, and a guarded path that only
@@ -63,6 +64,27 @@ __device__ __forceinline__ float quad_max(float x) {
   y = __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, 0x4E, 0xF, 0xF, false));
   return fmaxf(x, y);
 }
+
+// Max over the LPG lanes of an aligned group (LPG = 4, 8 or 16): the quad
+// first, then row_half_mirror (lane i and 7 - i of each 8 lanes) and row_mirror
+// (lane i and 15 - i of each 16 lanes) bring in the other quad and the other
+// half-row.
+template <int LPG>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(LPG == 4 || LPG == 8 || LPG == 16, "4, 8 or 16 lanes per group");
+  x = quad_max(x);
+  if constexpr (LPG >= 8) {
+    const int xi = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, 0x141, 0xF, 0xF, false)));
+  }
+  if constexpr (LPG >= 16) {
+    const int xi = __float_as_int(x);
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(xi, xi, 0x140, 0xF, 0xF, false)));
+  }
+  return x;
+}
+
+constexpr int log2i(int x) { return x <= 1 ? 0 : 1 + log2i(x / 2); }
 
 // Nearest code in [-7, 7] to the exact quotient v / s (s > 0), ties to even,
 // in binary64: a quotient of two binary32 values that is not a tie lies at
@@ -184,7 +206,7 @@ __device__ __forceinline__ void widen(const Raw<BF16>& r, float (&v)[8]) {
 // grid = (ceil(nchunk / (256*U)), P); a block covers 256*U chunks of one rank,
 // chunk c0 + u*256 for lane c0.
 // ---------------------------------------------------------------------------
-template <bool BF16, int U, int POL, bool FULL>
+template <bool BF16, int U, int POL, int LPG, bool FULL>
 __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, float* scales,
                                             int64_t c0, int64_t nchunk) {
   Raw<BF16> raw[U];
@@ -203,17 +225,17 @@ __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, fl
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
     float v[8];
     widen<BF16>(raw[u], v);
-    const float s = echo_div7(quad_max(absmax8(v)));
+    const float s = echo_div7(group_max<LPG>(absmax8(v)));
     float kf[8];
     const uint32_t w = quantize8(v, s, kf);
     if (FULL || c < nchunk) {
       st<(POL & kNtOut) != 0>(w, codes + c);
-      if ((threadIdx.x & 3) == 0) scales[c >> 2] = s;
+      if ((threadIdx.x & (LPG - 1)) == 0) scales[c >> log2i(LPG)] = s;
     }
   }
 }
 
-template <bool BF16, int U, int POL>
+template <bool BF16, int U, int POL, int LPG>
 __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) {
   const int r = blockIdx.y;
   const void* src = a.src[0];
@@ -225,9 +247,9 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
   const int64_t c0 = cb + threadIdx.x;
   if (cb + kBlock * U <= a.nchunk)
-    stage1_tile<BF16, U, POL, true>(src, codes, scales, c0, a.nchunk);
+    stage1_tile<BF16, U, POL, LPG, true>(src, codes, scales, c0, a.nchunk);
   else
-    stage1_tile<BF16, U, POL, false>(src, codes, scales, c0, a.nchunk);
+    stage1_tile<BF16, U, POL, LPG, false>(src, codes, scales, c0, a.nchunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,10 +257,10 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
 // order, correction, stage-2 quantization, error and both estimates.
 // grid = ceil(nchunk / 256); one lane per chunk.
 // ---------------------------------------------------------------------------
-template <int P, bool COMP, int POL, bool FULL>
+template <int P, bool COMP, int POL, int LPG, bool FULL>
 __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
   const bool ok = FULL || c < a.nchunk;
-  const int64_t g = c >> 2;
+  const int64_t g = c >> log2i(LPG);
 
   uint32_t w[P];
   float s[P];
@@ -286,12 +308,12 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
     }
   }
 
-  const float s2 = echo_div7(quad_max(absmax8(V)));
+  const float s2 = echo_div7(group_max<LPG>(absmax8(V)));
   float kf[8];
   const uint32_t w2 = quantize8(V, s2, kf);
   if (ok) {
     st<(POL & kNtOut) != 0>(w2, a.codes2 + c);
-    if ((threadIdx.x & 3) == 0) a.scales2[g] = s2;
+    if ((threadIdx.x & (LPG - 1)) == 0) a.scales2[g] = s2;
     if constexpr (COMP) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -311,13 +333,13 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
   }
 }
 
-template <int P, bool COMP, int POL>
+template <int P, bool COMP, int POL, int LPG>
 __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * kBlock;
   if (cb + kBlock <= a.nchunk)
-    owner_tile<P, COMP, POL, true>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, true>(a, cb + threadIdx.x);
   else
-    owner_tile<P, COMP, POL, false>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, false>(a, cb + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -326,9 +348,10 @@ __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
 // high half of code word i/2, group i/8), so each wavefront store writes 1 KiB
 // of contiguous output.  grid = ceil(n4 / (256*U)), unit i0 + u*256 for lane i0.
 // ---------------------------------------------------------------------------
-template <int U, int POL, bool FULL>
+template <int U, int POL, int LPG, bool FULL>
 __device__ __forceinline__ void decode_tile(const uint32_t* codes, const float* scales, float* out,
                                             int64_t i0, int64_t n4) {
+  constexpr int kUnitsPerGroupLog2 = log2i(2 * LPG);  // 4-element units per group
   uint32_t w[U];
   float s[U];
 #pragma unroll
@@ -336,7 +359,7 @@ __device__ __forceinline__ void decode_tile(const uint32_t* codes, const float* 
     const int64_t i = i0 + static_cast<int64_t>(u) * kBlock;
     if (FULL || i < n4) {
       w[u] = ld<(POL & kNtIn) != 0>(codes + (i >> 1));
-      s[u] = scales[i >> 3];
+      s[u] = scales[i >> kUnitsPerGroupLog2];
     } else {
       w[u] = 0;
       s[u] = 0.0f;
@@ -356,15 +379,15 @@ __device__ __forceinline__ void decode_tile(const uint32_t* codes, const float* 
   }
 }
 
-template <int U, int POL>
+template <int U, int POL, int LPG>
 __global__ __launch_bounds__(kBlock) void echo_unpack_k(const uint32_t* __restrict__ codes,
                                                          const float* __restrict__ scales,
                                                          float* __restrict__ out, int64_t n4) {
   const int64_t ib = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
   if (ib + kBlock * U <= n4)
-    decode_tile<U, POL, true>(codes, scales, out, ib + threadIdx.x, n4);
+    decode_tile<U, POL, LPG, true>(codes, scales, out, ib + threadIdx.x, n4);
   else
-    decode_tile<U, POL, false>(codes, scales, out, ib + threadIdx.x, n4);
+    decode_tile<U, POL, LPG, false>(codes, scales, out, ib + threadIdx.x, n4);
 }
 
 __global__ __launch_bounds__(kBlock) void echo_zero_k(float* __restrict__ p, int64_t n) {
@@ -383,68 +406,88 @@ constexpr int kOwnerPol = 0;
 constexpr int kDecodeUnroll = 2;
 constexpr int kDecodePol = kNtOut;
 
-template <int P, int POL = kOwnerPol>
-hipError_t owner_p(const OwnerArgs& a, bool comp, hipStream_t s) {
+template <int P, int LPG, int POL = kOwnerPol>
+hipError_t owner_pg(const OwnerArgs& a, bool comp, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock - 1) / kBlock;
   if (comp)
-    hipLaunchKernelGGL((echo_owner_k<P, true, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_owner_k<P, false, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, false, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-template <int U, int POL = kStage1Pol>
+template <int P>
+hipError_t owner_p(const OwnerArgs& a, bool comp, int group, hipStream_t s) {
+  switch (group) {
+    case 32: return owner_pg<P, 4>(a, comp, s);
+    case 64: return owner_pg<P, 8>(a, comp, s);
+    case 128: return owner_pg<P, 16>(a, comp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int U, int POL = kStage1Pol, int LPG = 4>
 hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock * U - 1) / (kBlock * U);
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(P));
   if (bf16)
-    hipLaunchKernelGGL((echo_quant_pack_k<true, U, POL>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_quant_pack_k<true, U, POL, LPG>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_quant_pack_k<false, U, POL>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_quant_pack_k<false, U, POL, LPG>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-template <int U, int POL = kDecodePol>
+template <int U, int POL = kDecodePol, int LPG = 4>
 hipError_t decode_u(const uint32_t* codes, const float* scales, float* out, int64_t numel,
                     hipStream_t s) {
   const int64_t n4 = numel / 4;
   const int64_t blocks = (n4 + kBlock * U - 1) / (kBlock * U);
-  hipLaunchKernelGGL((echo_unpack_k<U, POL>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
+  hipLaunchKernelGGL((echo_unpack_k<U, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
                      codes, scales, out, n4);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
-  return stage1_u<kStage1Unroll>(a, P, bf16, s);
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s) {
+  switch (group) {
+    case 32: return stage1_u<kStage1Unroll, kStage1Pol, 4>(a, P, bf16, s);
+    case 64: return stage1_u<kStage1Unroll, kStage1Pol, 8>(a, P, bf16, s);
+    case 128: return stage1_u<kStage1Unroll, kStage1Pol, 16>(a, P, bf16, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, hipStream_t s) {
+hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, hipStream_t s) {
   switch (P) {
-    case 1: return owner_p<1>(a, compensate, s);
-    case 2: return owner_p<2>(a, compensate, s);
-    case 3: return owner_p<3>(a, compensate, s);
-    case 4: return owner_p<4>(a, compensate, s);
-    case 5: return owner_p<5>(a, compensate, s);
-    case 6: return owner_p<6>(a, compensate, s);
-    case 7: return owner_p<7>(a, compensate, s);
-    case 8: return owner_p<8>(a, compensate, s);
-    case 9: return owner_p<9>(a, compensate, s);
-    case 10: return owner_p<10>(a, compensate, s);
-    case 11: return owner_p<11>(a, compensate, s);
-    case 12: return owner_p<12>(a, compensate, s);
-    case 13: return owner_p<13>(a, compensate, s);
-    case 14: return owner_p<14>(a, compensate, s);
-    case 15: return owner_p<15>(a, compensate, s);
-    case 16: return owner_p<16>(a, compensate, s);
+    case 1: return owner_p<1>(a, compensate, group, s);
+    case 2: return owner_p<2>(a, compensate, group, s);
+    case 3: return owner_p<3>(a, compensate, group, s);
+    case 4: return owner_p<4>(a, compensate, group, s);
+    case 5: return owner_p<5>(a, compensate, group, s);
+    case 6: return owner_p<6>(a, compensate, group, s);
+    case 7: return owner_p<7>(a, compensate, group, s);
+    case 8: return owner_p<8>(a, compensate, group, s);
+    case 9: return owner_p<9>(a, compensate, group, s);
+    case 10: return owner_p<10>(a, compensate, group, s);
+    case 11: return owner_p<11>(a, compensate, group, s);
+    case 12: return owner_p<12>(a, compensate, group, s);
+    case 13: return owner_p<13>(a, compensate, group, s);
+    case 14: return owner_p<14>(a, compensate, group, s);
+    case 15: return owner_p<15>(a, compensate, group, s);
+    case 16: return owner_p<16>(a, compensate, group, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out, int64_t numel,
-                         hipStream_t s) {
-  return decode_u<kDecodeUnroll>(codes, scales, out, numel, s);
+                         int group, hipStream_t s) {
+  switch (group) {
+    case 32: return decode_u<kDecodeUnroll, kDecodePol, 4>(codes, scales, out, numel, s);
+    case 64: return decode_u<kDecodeUnroll, kDecodePol, 8>(codes, scales, out, numel, s);
+    case 128: return decode_u<kDecodeUnroll, kDecodePol, 16>(codes, scales, out, numel, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s) {

@@ -11,7 +11,8 @@
  * di grandi dimensioni di allenarsi più velocemente usando dati ultra-leggeri a
  * 4 bit», section «Come Echo evita che gli errori si accumulino»):
  *   - every rank cuts its partial sum into owner segments and sends them as
- *     4-bit integers (here: groups of 32 elements, one fp32 scale per group);
+ *     4-bit integers (here: groups of 32 elements, one fp32 scale per group;
+ *     groups of 64 or 128 are a configurable variant);
  *   - the owner of a segment decodes the P contributions, adds them in fp32,
  *     adds a correction built from two smoothed estimates (fast, slow) of the
  *     rounding error of its earlier calls, re-quantizes the sum to int4 and
@@ -57,7 +58,7 @@ extern "C" {
 typedef enum {
   ECHO_OK = 0,
   ECHO_ERR_ARG = 1,       /* null / misaligned / overlapping pointer, bad enum   */
-  ECHO_ERR_SHAPE = 2,     /* P outside [1,16], numel % 32 != 0 or too large      */
+  ECHO_ERR_SHAPE = 2,     /* P outside [1,16], group not 32/64/128, numel % group != 0 or too large */
   ECHO_ERR_DTYPE = 3,     /* unknown dtype                                        */
   ECHO_ERR_WORKSPACE = 4, /* workspace missing or smaller than echo_workspace_bytes */
   ECHO_ERR_STATE = 5,     /* null state, or called with another device current   */
@@ -74,8 +75,8 @@ typedef enum { ECHO_FWD = 0, ECHO_BWD = 1 } echo_dir;
 typedef struct {
   int32_t P;          /* emulated ranks, 1..ECHO_MAX_RANKS                        */
   int64_t numel;      /* N, elements per rank partial; 0 <= N <= ECHO_MAX_NUMEL,  */
-                      /* N % 32 == 0 (N == 0 makes every call a no-op)            */
-  int32_t group;      /* quantization group, must be ECHO_GROUP (32)              */
+                      /* N % group == 0 (N == 0 makes every call a no-op)         */
+  int32_t group;      /* elements per scale: ECHO_GROUP (32), or 64 / 128 (variants) */
   echo_dtype dtype;   /* element type of every partial (fp32 or bfloat16)         */
   int32_t compensate; /* 1 = Echo with error compensation, 0 = plain 2-rounding   */
   float beta_fast;    /* smoothing of the fast estimate, in [0,1]; default 0.5    */
@@ -87,7 +88,7 @@ typedef struct echo_state echo_state; /* opaque host handle */
 typedef void* echo_stream_t; /* a hipStream_t */
 
 /* Bytes of device workspace a state needs: stage-1 payloads of the P ranks
- * (codes N/2 B + scales N/8 B each), the broadcast payload, and the two
+ * (codes N/2 B + scales 4N/group B each), the broadcast payload, and the two
  * compensator vectors of both directions (2 x 2 x 4N B), plus alignment
  * slack.  Returns 0 for an invalid configuration and for N == 0. */
 size_t echo_workspace_bytes(const echo_config* cfg);
@@ -143,11 +144,11 @@ echo_status echo_wire_bytes(const echo_state* st, uint64_t* rs_per_rank, uint64_
  * of the state (copy m_fast/m_slow out and back). */
 typedef struct {
   const void* stage1_codes;    /* rank r: stage1_codes + r*stage1_codes_stride bytes, N/2 B  */
-  const float* stage1_scales;  /* rank r: (char*)stage1_scales + r*stage1_scales_stride, N/32 */
+  const float* stage1_scales;  /* rank r: (char*)stage1_scales + r*stage1_scales_stride, N/group */
   size_t stage1_codes_stride;  /* bytes between ranks                                      */
   size_t stage1_scales_stride; /* bytes between ranks                                      */
   const void* bcast_codes;     /* N/2 B: two's-complement nibbles, element 2k low nibble   */
-  const float* bcast_scales;   /* N/32 fp32                                                */
+  const float* bcast_scales;   /* N/group fp32                                             */
   float* m_fast;               /* N fp32, compensator of the requested direction           */
   float* m_slow;               /* N fp32                                                   */
 } echo_views;

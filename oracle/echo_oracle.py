@@ -34,7 +34,8 @@ pair (m_fast, m_slow) of fp32 vectors of length N:
      separate pairs [rit.work, «Как Echo возвращает ошибку…»].
   7. Output: out = B in fp32.
 
-Q(v) for one group v[0..31] of fp32 values:
+Q(v) for one group v of fp32 values (32 consecutive elements by default; the
+group sizes 64 and 128 are variants the pages leave open):
   a = max |v_i|;  s = fl(a / 7)  (IEEE binary32 division);
   if s == 0: every code is 0;
   else: q_i = the code k in [-7, 7] nearest to the exact real quotient v_i / s,
@@ -77,13 +78,13 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # the quantizer Q
 # ----------------------------------------------------------------------------
-def quantize_groups(v: np.ndarray):
-    """Q applied to every group of 32 consecutive elements of ``v``.
+def quantize_groups(v: np.ndarray, group: int = GROUP):
+    """Q applied to every group of ``group`` consecutive elements of ``v``.
 
     Returns ``(codes, scales)``: int8 codes in [-7, 7] with the shape of ``v``
-    flattened to ``(-1, 32)`` and one float32 scale per group.
+    flattened to ``(-1, group)`` and one float32 scale per group.
     """
-    v = np.ascontiguousarray(v, dtype=F32).reshape(-1, GROUP)
+    v = np.ascontiguousarray(v, dtype=F32).reshape(-1, group)
     a = np.max(np.abs(v), axis=1)
     s = a / F32(QMAX)  # binary32 division, round to nearest even
     codes = np.zeros(v.shape, dtype=np.int8)
@@ -96,9 +97,9 @@ def quantize_groups(v: np.ndarray):
     return codes, s.astype(F32)
 
 
-def dequantize_groups(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """fl(q * s) per element, as float32 of shape ``(-1, 32)``."""
-    codes = np.asarray(codes, dtype=np.int8).reshape(-1, GROUP)
+def dequantize_groups(codes: np.ndarray, scales: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """fl(q * s) per element, as float32 of shape ``(-1, group)``."""
+    codes = np.asarray(codes, dtype=np.int8).reshape(-1, group)
     scales = np.asarray(scales, dtype=F32).reshape(-1)
     return codes.astype(F32) * scales[:, None]
 
@@ -136,20 +137,20 @@ def owner_segments(n_groups: int, P: int):
     return segs
 
 
-def payload_bytes(n_elems: int) -> int:
+def payload_bytes(n_elems: int, group: int = GROUP) -> int:
     """Bytes one int4 payload of ``n_elems`` occupies: codes plus fp32 scales."""
-    return n_elems // 2 + 4 * (n_elems // GROUP)
+    return n_elems // 2 + 4 * (n_elems // group)
 
 
-def wire_bytes(P: int, N: int):
+def wire_bytes(P: int, N: int, group: int = GROUP):
     """Bytes each rank would put on the wire for one call.
 
     rs: largest over ranks of what a rank sends to the other owners;
     ag: largest over owners of what an owner broadcasts to the other ranks;
     bf16: a ring all-reduce of the same message in bfloat16, 2(P-1)/P * 2N.
     """
-    segs = owner_segments(N // GROUP, P)
-    seg_b = [payload_bytes((hi - lo) * GROUP) for lo, hi in segs]
+    segs = owner_segments(N // group, P)
+    seg_b = [payload_bytes((hi - lo) * group, group) for lo, hi in segs]
     rs = max((sum(seg_b) - seg_b[r] for r in range(P)), default=0)
     ag = max(((P - 1) * b for b in seg_b), default=0)
     bf16 = (2 * (P - 1) * 2 * N) // P if P > 0 else 0
@@ -186,7 +187,7 @@ class OracleState:
 # ----------------------------------------------------------------------------
 def echo_call(partials, state: OracleState | None, direction: int = FWD,
               compensate: bool = True, beta_fast: float = 0.5,
-              beta_slow: float = 0.95):
+              beta_slow: float = 0.95, group: int = GROUP):
     """One Echo all-reduce of ``partials`` ([P, N] float32).
 
     Advances ``state`` (direction ``direction``) in place when compensating and
@@ -196,17 +197,17 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     if x.ndim != 2:
         raise ValueError("partials must be [P, N]")
     P, N = x.shape
-    if N % GROUP:
-        raise ValueError("N must be a multiple of 32")
+    if N % group:
+        raise ValueError(f"N must be a multiple of the group size {group}")
     if not np.all(np.isfinite(x)):
         raise ValueError("partials must be finite")
-    n_g = N // GROUP
+    n_g = N // group
 
     # 1. stage 1 on every rank
     q1 = np.empty((P, N), np.int8)
     s1 = np.empty((P, n_g), F32)
     for r in range(P):
-        q, s = quantize_groups(x[r])
+        q, s = quantize_groups(x[r], group)
         q1[r] = q.reshape(-1)
         s1[r] = s
 
@@ -226,11 +227,11 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     for g0, g1 in owner_segments(n_g, P):
         if g1 <= g0:
             continue
-        e0, e1 = g0 * GROUP, g1 * GROUP
+        e0, e1 = g0 * group, g1 * group
         # 3. dequantize every rank's contribution and add in rank order
         acc = None
         for r in range(P):
-            d = dequantize_groups(q1[r, e0:e1], s1[r, g0:g1]).reshape(-1)
+            d = dequantize_groups(q1[r, e0:e1], s1[r, g0:g1], group).reshape(-1)
             acc = d if acc is None else acc + d
         S[e0:e1] = acc
         # 4. correction from the two smoothed error estimates
@@ -242,10 +243,10 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
             vv = acc
         V[e0:e1] = vv
         # 5. stage 2
-        qq, ss = quantize_groups(vv)
+        qq, ss = quantize_groups(vv, group)
         q2[e0:e1] = qq.reshape(-1)
         s2[g0:g1] = ss
-        bb = dequantize_groups(qq, ss).reshape(-1)
+        bb = dequantize_groups(qq, ss, group).reshape(-1)
         B[e0:e1] = bb
         # 6. error of this rounding, then the two estimates
         if compensate:
@@ -256,7 +257,7 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
 
     # 7. every rank decodes the broadcast payload
     codes2 = pack_nibbles(q2)
-    out = dequantize_groups(unpack_nibbles(codes2), s2).reshape(-1)
+    out = dequantize_groups(unpack_nibbles(codes2), s2, group).reshape(-1)
     return {
         "codes1": np.stack([pack_nibbles(q1[r]) for r in range(P)]) if P else np.zeros((0, N // 2), np.uint8),
         "scales1": s1,
@@ -278,7 +279,7 @@ def plain_sum(partials) -> np.ndarray:
     return np.sum(np.asarray(partials, dtype=F64), axis=0)
 
 
-def naive_ring_int4(partials) -> np.ndarray:
+def naive_ring_int4(partials, group: int = GROUP) -> np.ndarray:
     """Comparator: ring reduce that re-quantizes the running sum at every hop.
 
     Rank 0 quantizes its partial and sends it on; every later rank decodes what
@@ -288,9 +289,9 @@ def naive_ring_int4(partials) -> np.ndarray:
     Echo with [rit.work, «Почему обычное 4-битное суммирование портит модель»].
     """
     x = np.asarray(partials, dtype=F32)
-    q, s = quantize_groups(x[0])
-    acc = dequantize_groups(q, s).reshape(-1)
+    q, s = quantize_groups(x[0], group)
+    acc = dequantize_groups(q, s, group).reshape(-1)
     for r in range(1, x.shape[0]):
-        q, s = quantize_groups(acc + x[r])
-        acc = dequantize_groups(q, s).reshape(-1)
+        q, s = quantize_groups(acc + x[r], group)
+        acc = dequantize_groups(q, s, group).reshape(-1)
     return acc

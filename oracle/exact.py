@@ -96,7 +96,7 @@ def nearest_code(v: Fraction, s: Fraction) -> int:
 
 
 def quantize_group(v):
-    """Q of one group (list of 32 exact binary32 values) -> (codes, scale)."""
+    """Q of one group (list of exact binary32 values) -> (codes, scale)."""
     a = max(abs(t) for t in v)
     s = div(a, Fraction(QMAX))
     if s == 0:
@@ -104,21 +104,21 @@ def quantize_group(v):
     return [nearest_code(t, s) for t in v], s
 
 
-def quantize(v):
+def quantize(v, group=GROUP):
     codes, scales = [], []
-    for g in range(0, len(v), GROUP):
-        q, s = quantize_group(v[g:g + GROUP])
+    for g in range(0, len(v), group):
+        q, s = quantize_group(v[g:g + group])
         codes.extend(q)
         scales.append(s)
     return codes, scales
 
 
-def dequantize(codes, scales):
-    return [mul(Fraction(q), scales[i // GROUP]) for i, q in enumerate(codes)]
+def dequantize(codes, scales, group=GROUP):
+    return [mul(Fraction(q), scales[i // group]) for i, q in enumerate(codes)]
 
 
 def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
-              beta_slow=0.95):
+              beta_slow=0.95, group=GROUP):
     """One call on exact binary32 values.
 
     ``partials`` is a list of P lists of Fractions (each a binary32 value);
@@ -129,14 +129,14 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
     N = len(partials[0])
     q1, s1 = [], []
     for r in range(P):
-        q, s = quantize(partials[r])
+        q, s = quantize(partials[r], group)
         q1.append(q)
         s1.append(s)
     S = []
     for i in range(N):
         acc = None
         for r in range(P):
-            d = mul(Fraction(q1[r][i]), s1[r][i // GROUP])
+            d = mul(Fraction(q1[r][i]), s1[r][i // group])
             acc = d if acc is None else add(acc, d)
         S.append(acc)
     if compensate:
@@ -145,8 +145,8 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
     else:
         c = [Fraction(0)] * N
         V = list(S)
-    q2, s2 = quantize(V)
-    B = dequantize(q2, s2)
+    q2, s2 = quantize(V, group)
+    B = dequantize(q2, s2, group)
     err = [Fraction(0)] * N
     if compensate:
         bf, bs = f32(beta_fast), f32(beta_slow)

@@ -27,10 +27,10 @@ def _upload(raw, dtype, device):
     return [t[r].to(device).contiguous() for r in range(t.shape[0])]
 
 
-def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True):
+def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True, group=32):
     torch = _torch()
     import error_compensated_bit_echo_amd as E
-    cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1])
+    cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1], group=group)
     ws = torch.full((max(E.echo_workspace_bytes(cfg), 1),), 0xFF if poison else 0,
                     dtype=torch.uint8, device=device)
     return E.echo_init_state(cfg, ws)
@@ -43,7 +43,8 @@ def _fetch(state, out, direction, lo=0, hi=None):
     hi = state.numel if hi is None else hi
     v = E.echo_debug_views(state, direction)
     torch.cuda.synchronize()
-    g0, g1 = lo // 32, hi // 32
+    G = state.cfg.group
+    g0, g1 = lo // G, hi // G
     return {
         "codes1": v["codes1"][:, lo // 2:hi // 2].cpu().numpy(),
         "scales1": v["scales1"][:, g0:g1].cpu().numpy(),
@@ -63,7 +64,7 @@ def _compare(g, o, st_oracle, direction, compensate, where=""):
     assert np.array_equal(g["codes2"], o["codes2"]), f"stage-2 codes differ {where}"
     assert np.array_equal(g["scales2"].view(np.uint32), o["scales2"].view(np.uint32)), \
         f"stage-2 scales differ {where}"
-    s2 = np.repeat(o["scales2"].astype(F64), 32)
+    s2 = np.repeat(o["scales2"].astype(F64), o["q2"].size // max(o["scales2"].size, 1) if o["scales2"].size else 1)
     inexact = 0
     pairs = [("out", o["out"])]
     if compensate:

@@ -51,10 +51,12 @@ def _ws(cfg):
 
 
 def test_workspace_bytes_formula():
-    for P, N, dt in ((2, 2048, "f32"), (8, 536870912, "bf16"), (3, 96, "bf16"), (16, 32, "bf16")):
-        cfg = B.EchoConfig.make(P, N, dt)
+    for P, N, dt, G in ((2, 2048, "f32", 32), (8, 536870912, "bf16", 32), (3, 96, "bf16", 32),
+                        (16, 32, "bf16", 32), (8, 536870912, "bf16", 64), (3, 384, "f32", 128)):
+        cfg = B.EchoConfig.make(P, N, dt, group=G)
         al = lambda x: (x + 255) // 256 * 256
-        want = P * (al(N // 2) + al(N // 8)) + al(N // 2) + al(N // 8) + 4 * al(4 * N) + 256
+        sc = 4 * (N // G)
+        want = P * (al(N // 2) + al(sc)) + al(N // 2) + al(sc) + 4 * al(4 * N) + 256
         assert _ws(cfg) == want
     assert _ws(B.EchoConfig.make(4, 0)) == 0
 
@@ -62,14 +64,15 @@ def test_workspace_bytes_formula():
 @pytest.mark.parametrize("field,value,status", [
     ("P", 0, B.ECHO_ERR_SHAPE), ("P", 17, B.ECHO_ERR_SHAPE),
     ("numel", 33, B.ECHO_ERR_SHAPE), ("numel", -32, B.ECHO_ERR_SHAPE),
-    ("numel", (1 << 36) + 32, B.ECHO_ERR_SHAPE), ("group", 64, B.ECHO_ERR_SHAPE),
+    ("numel", (1 << 36) + 32, B.ECHO_ERR_SHAPE), ("group", 48, B.ECHO_ERR_SHAPE),
+    ("group", 16, B.ECHO_ERR_SHAPE), ("group", 256, B.ECHO_ERR_SHAPE), ("numel", 4096 + 32 * 3, B.ECHO_ERR_SHAPE),
     ("dtype", 7, B.ECHO_ERR_DTYPE), ("compensate", 2, B.ECHO_ERR_ARG),
     ("beta_fast", -0.5, B.ECHO_ERR_ARG), ("beta_slow", float("nan"), B.ECHO_ERR_ARG),
     ("beta_slow", 1.5, B.ECHO_ERR_ARG),
 ])
 def test_init_rejects_bad_config_without_touching_the_gpu(field, value, status):
     lib = B.load_library()
-    cfg = B.EchoConfig.make(4, 4096)
+    cfg = B.EchoConfig.make(4, 4096, group=64 if (field, value) == ("numel", 4096 + 96) else 32)
     setattr(cfg, field, value)
     assert _ws(cfg) == 0
     h = ctypes.c_void_p()

@@ -55,6 +55,29 @@ def test_multi_tile_ragged(cuda, P, dtype):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"P={P} {dtype} call {t}") == 0
 
 
+@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("P,dtype", [(1, "bf16"), (3, "f32"), (8, "bf16"), (16, "bf16")])
+def test_larger_groups_multi_tile_ragged(cuda, P, dtype, group):
+    """The group-size variants: 8 or 16 lanes per group, several tiles and a
+    ragged tail, tie-rich and normal data, compensation on."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = 2048 * 7 + group * 3
+    st = _state(P, N, dtype, group=group)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    rng = np.random.default_rng(group + P)
+    for t in range(4):
+        if t % 2:
+            vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+            raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
+        else:
+            raw, vals = synth.host_partials(2, 0, t, P=P, n=N, dtype=dtype)
+        E.echo_reduce(_upload(raw, dtype, cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, group=group)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"G={group} P={P} {dtype} call {t}") == 0
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
@@ -267,6 +290,10 @@ def test_wire_bytes_match_the_oracle(cuda):
     for P, N in ((2, 2048), (4, 2048 * 4096), (8, 64 * 4096), (3, 32 * 7), (16, 32 * 5)):
         st = _state(P, N, "bf16", poison=False)
         assert E.echo_wire_bytes(st) == eo.wire_bytes(P, N)
+    for group in (64, 128):
+        for P, N in ((8, 64 * 4096), (3, 128 * 7), (16, 128 * 5)):
+            st = _state(P, N, "bf16", poison=False, group=group)
+            assert E.echo_wire_bytes(st) == eo.wire_bytes(P, N, group)
 
 
 # ---------------------------------------------------------------------------

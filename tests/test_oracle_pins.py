@@ -52,17 +52,17 @@ def test_exact_rounding_matches_float64_to_float32_cast():
 # ---------------------------------------------------------------------------
 # P1: the quantizer against brute force in exact rationals
 # ---------------------------------------------------------------------------
-def _tie_groups(rng, n_groups):
+def _tie_groups(rng, n_groups, group=32):
     """Groups whose scale is exact and whose members are exact half-integer ties."""
     groups = []
     for _ in range(n_groups):
         m = int(rng.integers(1, 2 ** 12)) | 1
         e = int(rng.integers(-20, 20))
         s = F64(m) * 2.0 ** e
-        g = np.empty(32, F64)
+        g = np.empty(group, F64)
         g[0] = 7 * s * (1 if rng.random() < 0.5 else -1)
-        k = rng.integers(-7, 7, 31)
-        half = rng.random(31) < 0.7
+        k = rng.integers(-7, 7, group - 1)
+        half = rng.random(group - 1) < 0.7
         g[1:] = (k + np.where(half, 0.5, 0.0)) * s
         g = g.astype(F32)
         assert np.all(g.astype(F64) == np.concatenate([[g[0]], (k + np.where(half, 0.5, 0.0)) * s]))
@@ -70,11 +70,12 @@ def _tie_groups(rng, n_groups):
     return np.concatenate(groups)
 
 
+@pytest.mark.parametrize("group", [32, 64, 128])
 @pytest.mark.parametrize("kind", ["normal", "tiny", "huge", "ties", "subnormal", "sparse"])
-def test_quantizer_matches_brute_force(kind):
+def test_quantizer_matches_brute_force(kind, group):
     rng = np.random.default_rng({"normal": 1, "tiny": 2, "huge": 3, "ties": 4,
-                                 "subnormal": 5, "sparse": 6}[kind])
-    n = 32 * 24
+                                 "subnormal": 5, "sparse": 6}[kind] + group)
+    n = group * 24
     if kind == "normal":
         v = rng.standard_normal(n).astype(F32)
     elif kind == "tiny":
@@ -82,21 +83,21 @@ def test_quantizer_matches_brute_force(kind):
     elif kind == "huge":
         v = (rng.standard_normal(n) * 1e30).astype(F32)
     elif kind == "ties":
-        v = _tie_groups(rng, 24)
+        v = _tie_groups(rng, 24, group)
     elif kind == "subnormal":
         v = (rng.integers(-80, 80, n) * 2.0 ** -149).astype(F32)
-        v[:32] = (rng.integers(-3, 4, 32) * 2.0 ** -149).astype(F32)  # s underflows to 0
+        v[:group] = (rng.integers(-3, 4, group) * 2.0 ** -149).astype(F32)  # s underflows to 0
     else:
         v = rng.standard_normal(n).astype(F32)
         v[rng.random(n) < 0.8] = 0
-        v[:32] = 0
-        v[32:64] = -0.0
-    q, s = eo.quantize_groups(v)
-    qx, sx = ex.quantize(_fr(v))
+        v[:group] = 0
+        v[group:2 * group] = -0.0
+    q, s = eo.quantize_groups(v, group)
+    qx, sx = ex.quantize(_fr(v), group)
     assert np.array_equal(q.reshape(-1), np.array(qx, np.int8))
     assert np.array_equal(s, _as_f32(sx))
     # the scale is the binary32 quotient of the group absmax by 7
-    a = np.max(np.abs(v.reshape(-1, 32)), axis=1)
+    a = np.max(np.abs(v.reshape(-1, group)), axis=1)
     assert np.array_equal(s, _as_f32([ex.div(Fraction(float(t)), Fraction(7)) for t in a]))
 
 
@@ -205,6 +206,15 @@ def test_payload_is_about_a_quarter_of_bf16():
         assert np.all(owned == 1)
     o = eo.echo_call(np.zeros((3, 64), F32), eo.OracleState(64))
     assert o["codes2"].nbytes + o["scales2"].nbytes == eo.payload_bytes(64)
+    # larger groups (variants): one fp32 scale per 64 or 128 elements
+    for group, ratio in ((64, 0.28125), (128, 0.265625)):
+        N = 128 * 1024
+        assert eo.payload_bytes(N, group) == N // 2 + 4 * N // group
+        assert eo.payload_bytes(N, group) / (2 * N) == ratio
+        o = eo.echo_call(np.ones((2, N), F32), eo.OracleState(N), group=group)
+        assert o["codes2"].nbytes + o["scales2"].nbytes == eo.payload_bytes(N, group)
+        w = eo.wire_bytes(8, N, group)
+        assert w["rs_per_rank"] == 7 * eo.payload_bytes(N, group) // 8
 
 
 # ---------------------------------------------------------------------------
@@ -306,15 +316,16 @@ def test_two_roundings_for_every_P(P):
 # ---------------------------------------------------------------------------
 # P8: the whole call against the exact-rational implementation
 # ---------------------------------------------------------------------------
-def _compare_exact(x, T, compensate, beta=(0.5, 0.95)):
+def _compare_exact(x, T, compensate, beta=(0.5, 0.95), group=32):
     P, N = x[0].shape
     st = eo.OracleState(N)
     mf = [Fraction(0)] * N
     ms = [Fraction(0)] * N
     for t in range(T):
-        o = eo.echo_call(x[t], st, compensate=compensate, beta_fast=beta[0], beta_slow=beta[1])
+        o = eo.echo_call(x[t], st, compensate=compensate, beta_fast=beta[0], beta_slow=beta[1],
+                         group=group)
         e = ex.echo_call([_fr(x[t][r]) for r in range(P)], mf, ms, compensate=compensate,
-                         beta_fast=beta[0], beta_slow=beta[1])
+                         beta_fast=beta[0], beta_slow=beta[1], group=group)
         for r in range(P):
             assert np.array_equal(o["q1"][r], np.array(e["q1"][r], np.int8))
             assert np.array_equal(o["scales1"][r], _as_f32(e["scales1"][r]))
@@ -331,6 +342,15 @@ def _compare_exact(x, T, compensate, beta=(0.5, 0.95)):
 def test_whole_call_matches_exact_rationals(compensate):
     xs = [synth.host_partials(1, 0, t, P=2, n=64)[1] for t in range(16)]
     _compare_exact(xs, 16, compensate)
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_whole_call_matches_exact_rationals_larger_groups(group):
+    xs = [synth.host_partials(2, 0, t, P=3, n=256)[1] for t in range(6)]
+    _compare_exact(xs, 6, True, group=group)
+    rng = np.random.default_rng(group)
+    xs = [(rng.integers(-12, 13, (2, 256)) * 0.25).astype(F32) for _ in range(4)]
+    _compare_exact(xs, 4, False, group=group)
 
 
 def test_whole_call_matches_exact_rationals_tie_rich():
