@@ -123,7 +123,7 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
 # ---------------------------------------------------------------------------
 # the other workloads: latency, effective bandwidth and accuracy reports
 # ---------------------------------------------------------------------------
-CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0}
+CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2}
 CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
 
 
@@ -166,7 +166,7 @@ def _wall_us(E, torch, parts, out, st, direction, reps):
     return (time.perf_counter() - t0) * 1e6 / reps
 
 
-def stream_report(name, E, synth, torch, dev) -> dict:
+def stream_report(name, E, synth, torch, dev, group: int = 32) -> dict:
     """tiny / prefill / training: the configuration's calls on fresh partials,
     each call's output added to a residual stream h (fp32) next to the exact
     stream h* = sum of all partials (float64); compensation on and off."""
@@ -184,7 +184,8 @@ def stream_report(name, E, synth, torch, dev) -> dict:
             return [torch.from_numpy(np.ascontiguousarray(raw[r])).to(dev) for r in range(P)]
         return synth.device_partials(cid, d, t, device=dev)
 
-    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, dtype, compensate=(m == "on")), device=dev)
+    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, dtype, compensate=(m == "on"), group=group),
+                               device=dev)
           for m in ("on", "off")}
     out = torch.empty(N, dtype=torch.float32, device=dev)
     h = {(m, d): torch.zeros(N, dtype=torch.float32, device=dev) for m in st for d in dirs}
@@ -213,13 +214,16 @@ def stream_report(name, E, synth, torch, dev) -> dict:
             e = (h[(m, d)].double() - ref).pow(2).mean().sqrt().item()
             err[f"{'fwd' if d == 0 else 'bwd'}_{m}"] = {"rms_err": e, "rel_rms_err": e / scale}
     wall = _wall_us(E, torch, parts, out, st["on"], dirs[-1], 20)
-    gst = E.echo_init_state(E.EchoConfig.make(P, N, dtype), device=dev)
+    gst = E.echo_init_state(E.EchoConfig.make(P, N, dtype, group=group), device=dev)
     gout = torch.empty_like(out)
     graph, _ = _graph_us(E, torch, parts, gout, gst, dirs[-1], 20)
-    alg = N * (P * (b_in + 1.25) + 21.25)
+    pl = 0.5 + 4.0 / group
+    alg = N * (P * (b_in + pl) + pl * (P + 2) + 4 + 16)
     med = _pct(graph, 0.5)
     return {
-        "config": name, "P": P, "numel_per_rank": N, "input_dtype": dtype,
+        "config": name if group == 32 else f"{name}-g{group}", "group": group,
+        "P": P, "numel_per_rank": N, "input_dtype": dtype,
+        "payload_bytes_per_element": pl,
         "calls": c["calls"] * len(dirs), "alg_bytes_per_call": int(alg),
         "cache_resident": bool(alg + P * N * b_in < CACHE_BYTES),
         "us_per_call": {"eager_events_median": round(_pct(eager, 0.5), 2),
@@ -419,9 +423,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config:
-        names = ["tiny", "prefill", "decode", "training", "tp"] if args.config == "all" else [args.config]
+        names = ["tiny", "prefill", "decode", "training", "tp", "groups"] if args.config == "all" \
+            else [args.config]
         for name in names:
             print(f"# config {name}", file=sys.stderr, flush=True)
+            if name == "groups":
+                # the group-size variants on the prefill workload: bytes against accuracy
+                for G in (32, 64, 128):
+                    print(json.dumps(stream_report("prefill", E, synth, torch, dev, group=G)), flush=True)
+                    torch.cuda.empty_cache()
+                continue
             if name == "decode":
                 rep = decode_report(E, synth, torch, dev)
             elif name == "tp":
