@@ -38,15 +38,18 @@ class EchoConfig(ctypes.Structure):
         ("compensate", ctypes.c_int32),
         ("beta_fast", ctypes.c_float),
         ("beta_slow", ctypes.c_float),
+        ("sender_feedback", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, P: int, numel: int, dtype: str = "bf16", compensate: bool = True,
-             beta_fast: float = 0.5, beta_slow: float = 0.95, group: int = ECHO_GROUP) -> "EchoConfig":
+             beta_fast: float = 0.5, beta_slow: float = 0.95, group: int = ECHO_GROUP,
+             sender_feedback: bool = False) -> "EchoConfig":
         d = {"f32": ECHO_F32, "float32": ECHO_F32, "bf16": ECHO_BF16, "bfloat16": ECHO_BF16}
         if dtype not in d:
             raise EchoError(ECHO_ERR_DTYPE, f"dtype {dtype!r}")
-        return cls(P, numel, group, d[dtype], int(bool(compensate)), beta_fast, beta_slow)
+        return cls(P, numel, group, d[dtype], int(bool(compensate)), beta_fast, beta_slow,
+                   int(bool(sender_feedback)))
 
 
 class EchoViews(ctypes.Structure):
@@ -59,6 +62,8 @@ class EchoViews(ctypes.Structure):
         ("bcast_scales", ctypes.c_void_p),
         ("m_fast", ctypes.c_void_p),
         ("m_slow", ctypes.c_void_p),
+        ("sender_err", ctypes.c_void_p),
+        ("sender_err_stride", ctypes.c_size_t),
     ]
 
 
@@ -92,7 +97,7 @@ def load_library():
         "echo_workspace_bytes": (sz, [cfgp]),
         "echo_init_state": (i32, [cfgp, vp, sz, vp, ctypes.POINTER(vp)]),
         "echo_reduce": (i32, [ctypes.POINTER(vp), vp, vp, i32, vp]),
-        "echo_stage1": (i32, [ctypes.POINTER(vp), vp, vp]),
+        "echo_stage1": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
         "echo_owner": (i32, [vp, i32, vp]),
         "echo_decode": (i32, [vp, vp, vp]),
         "echo_reset": (i32, [vp, i32, vp]),
@@ -214,10 +219,10 @@ def echo_reduce(partials: Sequence, out, state: EchoState, direction: int = ECHO
     return out
 
 
-def echo_stage1(partials: Sequence, state: EchoState, stream=None):
+def echo_stage1(partials: Sequence, state: EchoState, direction: int = ECHO_FWD, stream=None):
     arr = _partials_array(partials, state)
-    _check(load_library().echo_stage1(arr, state.handle, _stream_handle(stream, state.device)),
-           "echo_stage1")
+    _check(load_library().echo_stage1(arr, state.handle, int(direction),
+                                      _stream_handle(stream, state.device)), "echo_stage1")
 
 
 def echo_owner(state: EchoState, direction: int = ECHO_FWD, stream=None):
@@ -250,7 +255,8 @@ def echo_wire_bytes(state: EchoState) -> dict:
 
 def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
     """Views (no copies) into the workspace: stage-1 codes [P, N/2] and scales [P, N/group],
-    broadcast codes [N/2] and scales [N/group], and the m_fast / m_slow vectors of ``direction``."""
+    broadcast codes [N/2] and scales [N/group], the m_fast / m_slow vectors of ``direction``
+    and, with sender feedback, the ranks' stage-1 errors [P, N] of ``direction``."""
     import torch
     v = EchoViews()
     _check(load_library().echo_debug_views(state.handle, int(direction), ctypes.byref(v)),
@@ -262,7 +268,7 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
         e8 = torch.empty(0, dtype=torch.uint8, device=state.device)
         e32 = torch.empty(0, dtype=torch.float32, device=state.device)
         return {"codes1": e8.view(0, 0).expand(P, 0), "scales1": e32.view(0, 0).expand(P, 0),
-                "codes2": e8, "scales2": e32, "m_fast": e32, "m_slow": e32}
+                "codes2": e8, "scales2": e32, "m_fast": e32, "m_slow": e32, "sender_err": None}
 
     def sl(ptr, nbytes):
         off = ptr - base
@@ -278,4 +284,8 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
         "scales2": sl(v.bcast_scales, 4 * (N // G)).view(torch.float32),
         "m_fast": sl(v.m_fast, 4 * N).view(torch.float32),
         "m_slow": sl(v.m_slow, 4 * N).view(torch.float32),
+        # sender feedback: [P, N] stage-1 errors of the ranks for ``direction``
+        "sender_err": None if not v.sender_err else
+        sl(v.sender_err, P * v.sender_err_stride).view(torch.float32)
+        .view(P, v.sender_err_stride // 4)[:, :N],
     }

@@ -19,8 +19,10 @@ struct echo_state {
   float* scales2;
   float* m_fast[2];             // per direction
   float* m_slow[2];
-  float* state_base;            // both directions, contiguous
+  float* state_base;            // both directions, contiguous, then the sender errors
   int64_t vec_floats;           // floats per state vector (with alignment padding)
+  float* sender_err[2];         // sender feedback: rank r of direction d at
+                                // sender_err[d] + r * vec_floats; nullptr when off
 };
 
 namespace {
@@ -31,7 +33,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
   size_t codes1_stride, scales1_stride;  // bytes per rank
-  size_t off_codes1, off_scales1, off_codes2, off_scales2, off_state;
+  size_t off_codes1, off_scales1, off_codes2, off_scales2, off_state, off_sender;
   size_t vec_bytes;                      // one fp32 state vector, aligned
   size_t total;                          // without the base-alignment slack
 };
@@ -49,7 +51,9 @@ Layout make_layout(const echo_config& c) {
   L.off_scales2 = L.off_codes2 + align_up(N / 2);
   L.off_state = L.off_scales2 + align_up(scale_bytes);
   L.vec_bytes = align_up(4 * N);
-  L.total = L.off_state + 4 * L.vec_bytes;
+  L.off_sender = L.off_state + 4 * L.vec_bytes;
+  // sender feedback: every rank's stage-1 error, per direction, after the state
+  L.total = L.off_sender + (c.sender_feedback ? 2 * P * L.vec_bytes : 0);
   return L;
 }
 
@@ -62,6 +66,7 @@ echo_status check_cfg(const echo_config* c) {
   if (c->compensate != 0 && c->compensate != 1) return ECHO_ERR_ARG;
   if (!(c->beta_fast >= 0.0f && c->beta_fast <= 1.0f)) return ECHO_ERR_ARG;  // also rejects NaN
   if (!(c->beta_slow >= 0.0f && c->beta_slow <= 1.0f)) return ECHO_ERR_ARG;
+  if (c->sender_feedback != 0 && c->sender_feedback != 1) return ECHO_ERR_ARG;
   return ECHO_OK;
 }
 
@@ -104,7 +109,7 @@ echo_status check_out(const float* out, const echo_state* st, const void* const*
   return ECHO_OK;
 }
 
-echo_status run_stage1(const void* const* partials, echo_state* st, hipStream_t s) {
+echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hipStream_t s) {
   echo::Stage1Args a{};
   for (int r = 0; r < echo::kMaxRanks; ++r) a.src[r] = r < st->cfg.P ? partials[r] : partials[0];
   a.codes = st->codes1;
@@ -112,6 +117,8 @@ echo_status run_stage1(const void* const* partials, echo_state* st, hipStream_t 
   a.codes_stride_words = st->codes1_stride_bytes / 4;
   a.scales_stride = st->scales1_stride_bytes / 4;
   a.nchunk = st->cfg.numel / echo::kElemsPerLane;
+  a.err = st->sender_err[dir];
+  a.err_stride = st->vec_floats;
   return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
@@ -188,8 +195,14 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
     }
     st->state_base = reinterpret_cast<float*>(base + L.off_state);
     st->vec_floats = static_cast<int64_t>(L.vec_bytes / 4);
-    if (echo::launch_zero(st->state_base, 4 * st->vec_floats, static_cast<hipStream_t>(stream)) !=
-        hipSuccess) {
+    const int64_t sender_floats = cfg->sender_feedback ? 2 * cfg->P * st->vec_floats : 0;
+    for (int d = 0; d < 2; ++d)
+      st->sender_err[d] = cfg->sender_feedback
+                              ? reinterpret_cast<float*>(base + L.off_sender) + d * cfg->P * st->vec_floats
+                              : nullptr;
+    // the compensator vectors and the sender errors are contiguous: one fill
+    if (echo::launch_zero(st->state_base, 4 * st->vec_floats + sender_floats,
+                          static_cast<hipStream_t>(stream)) != hipSuccess) {
       delete st;
       return ECHO_ERR_HIP;
     }
@@ -198,12 +211,14 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
   return ECHO_OK;
 }
 
-echo_status echo_stage1(const void* const* partials, echo_state* st, echo_stream_t stream) {
+echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir dir,
+                        echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
+  if (dir != ECHO_FWD && dir != ECHO_BWD) return ECHO_ERR_ARG;
   if (st->cfg.numel == 0) return ECHO_OK;
   if ((e = check_partials(partials, st)) != ECHO_OK) return e;
-  return run_stage1(partials, st, static_cast<hipStream_t>(stream));
+  return run_stage1(partials, st, static_cast<int>(dir), static_cast<hipStream_t>(stream));
 }
 
 echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream) {
@@ -231,7 +246,7 @@ echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
   if ((e = check_partials(partials, st)) != ECHO_OK) return e;
   if ((e = check_out(out, st, partials)) != ECHO_OK) return e;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((e = run_stage1(partials, st, s)) != ECHO_OK) return e;
+  if ((e = run_stage1(partials, st, static_cast<int>(dir), s)) != ECHO_OK) return e;
   if ((e = run_owner(st, static_cast<int>(dir), s)) != ECHO_OK) return e;
   return run_decode(out, st, s);
 }
@@ -246,6 +261,9 @@ echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream) {
     if (!(dir_mask & (1 << d))) continue;
     // m_fast[d] and m_slow[d] are adjacent: one fill covers both
     if (echo::launch_zero(st->m_fast[d], 2 * st->vec_floats, s) != hipSuccess) return ECHO_ERR_HIP;
+    if (st->sender_err[d] != nullptr &&
+        echo::launch_zero(st->sender_err[d], st->cfg.P * st->vec_floats, s) != hipSuccess)
+      return ECHO_ERR_HIP;
   }
   return ECHO_OK;
 }
@@ -289,6 +307,8 @@ echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out
   out->bcast_scales = st->scales2;
   out->m_fast = st->m_fast[dir];
   out->m_slow = st->m_slow[dir];
+  out->sender_err = st->sender_err[dir];
+  out->sender_err_stride = st->sender_err[dir] != nullptr ? static_cast<size_t>(4 * st->vec_floats) : 0;
   return ECHO_OK;
 }
 

@@ -19,6 +19,8 @@ struct Stage1Args {
   int64_t codes_stride_words;  // uint32 words between ranks
   int64_t scales_stride;       // floats between ranks
   int64_t nchunk;              // N / 8
+  float* err;                  // sender feedback: rank r's stage-1 error at err + r * err_stride
+  int64_t err_stride;          // floats between ranks (err == nullptr: no sender feedback)
 };
 
 // Owner stage: sum, correct, re-quantize, update the compensator.

@@ -206,18 +206,24 @@ __device__ __forceinline__ void widen(const Raw<BF16>& r, float (&v)[8]) {
 // grid = (ceil(nchunk / (256*U)), P); a block covers 256*U chunks of one rank,
 // chunk c0 + u*256 for lane c0.
 // ---------------------------------------------------------------------------
-template <bool BF16, int U, int POL, int LPG, bool FULL>
+template <bool BF16, int U, int POL, int LPG, bool SFB, bool FULL>
 __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, float* scales,
-                                            int64_t c0, int64_t nchunk) {
+                                            float* err, int64_t c0, int64_t nchunk) {
   Raw<BF16> raw[U];
+  f32x4 ev[SFB ? U : 1][2];  // sender feedback: the rank's stage-1 error of these elements
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
     if (FULL || c < nchunk) {
       raw[u] = load_raw<BF16, (POL & kNtIn) != 0>(src, c);
+      if constexpr (SFB) {
+        ev[u][0] = reinterpret_cast<const f32x4*>(err)[2 * c];
+        ev[u][1] = reinterpret_cast<const f32x4*>(err)[2 * c + 1];
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < (BF16 ? 1 : 2); ++i) raw[u].q[i] = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (SFB) ev[u][0] = ev[u][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
 #pragma unroll
@@ -225,17 +231,28 @@ __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, fl
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
     float v[8];
     widen<BF16>(raw[u], v);
+    if constexpr (SFB) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v[j] + ev[u][j >> 2][j & 3];  // x' = fl(x + e)
+    }
     const float s = echo_div7(group_max<LPG>(absmax8(v)));
     float kf[8];
     const uint32_t w = quantize8(v, s, kf);
     if (FULL || c < nchunk) {
       st<(POL & kNtOut) != 0>(w, codes + c);
       if ((threadIdx.x & (LPG - 1)) == 0) scales[c >> log2i(LPG)] = s;
+      if constexpr (SFB) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = v[j] - kf[j] * s;  // e = x' - fl(q*s), exact
+        reinterpret_cast<f32x4*>(err)[2 * c] = f32x4{e[0], e[1], e[2], e[3]};
+        reinterpret_cast<f32x4*>(err)[2 * c + 1] = f32x4{e[4], e[5], e[6], e[7]};
+      }
     }
   }
 }
 
-template <bool BF16, int U, int POL, int LPG>
+template <bool BF16, int U, int POL, int LPG, bool SFB>
 __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) {
   const int r = blockIdx.y;
   const void* src = a.src[0];
@@ -244,12 +261,13 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
     if (r == i) src = a.src[i];
   uint32_t* codes = a.codes + static_cast<int64_t>(r) * a.codes_stride_words;
   float* scales = a.scales + static_cast<int64_t>(r) * a.scales_stride;
+  float* err = SFB ? a.err + static_cast<int64_t>(r) * a.err_stride : nullptr;
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
   const int64_t c0 = cb + threadIdx.x;
   if (cb + kBlock * U <= a.nchunk)
-    stage1_tile<BF16, U, POL, LPG, true>(src, codes, scales, c0, a.nchunk);
+    stage1_tile<BF16, U, POL, LPG, SFB, true>(src, codes, scales, err, c0, a.nchunk);
   else
-    stage1_tile<BF16, U, POL, LPG, false>(src, codes, scales, c0, a.nchunk);
+    stage1_tile<BF16, U, POL, LPG, SFB, false>(src, codes, scales, err, c0, a.nchunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,15 +444,21 @@ hipError_t owner_p(const OwnerArgs& a, bool comp, int group, hipStream_t s) {
   }
 }
 
-template <int U, int POL = kStage1Pol, int LPG = 4>
+template <int U, int POL = kStage1Pol, int LPG = 4, bool SFB = false>
 hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock * U - 1) / (kBlock * U);
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(P));
   if (bf16)
-    hipLaunchKernelGGL((echo_quant_pack_k<true, U, POL, LPG>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_quant_pack_k<true, U, POL, LPG, SFB>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_quant_pack_k<false, U, POL, LPG>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_quant_pack_k<false, U, POL, LPG, SFB>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
+}
+
+template <int LPG>
+hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
+  if (a.err != nullptr) return stage1_u<kStage1Unroll, kStage1Pol, LPG, true>(a, P, bf16, s);
+  return stage1_u<kStage1Unroll, kStage1Pol, LPG, false>(a, P, bf16, s);
 }
 
 template <int U, int POL = kDecodePol, int LPG = 4>
@@ -451,9 +475,9 @@ hipError_t decode_u(const uint32_t* codes, const float* scales, float* out, int6
 
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s) {
   switch (group) {
-    case 32: return stage1_u<kStage1Unroll, kStage1Pol, 4>(a, P, bf16, s);
-    case 64: return stage1_u<kStage1Unroll, kStage1Pol, 8>(a, P, bf16, s);
-    case 128: return stage1_u<kStage1Unroll, kStage1Pol, 16>(a, P, bf16, s);
+    case 32: return stage1_g<4>(a, P, bf16, s);
+    case 64: return stage1_g<8>(a, P, bf16, s);
+    case 128: return stage1_g<16>(a, P, bf16, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,6 +81,9 @@ typedef struct {
   int32_t compensate; /* 1 = Echo with error compensation, 0 = plain 2-rounding   */
   float beta_fast;    /* smoothing of the fast estimate, in [0,1]; default 0.5    */
   float beta_slow;    /* smoothing of the slow estimate, in [0,1]; default 0.95   */
+  int32_t sender_feedback; /* 1 = variant: every rank also feeds its own stage-1 */
+                      /* rounding error into its next call (x' = x + e, e <- x' - */
+                      /* fl(q*s), per rank and direction); 0 = off (default)       */
 } echo_config;
 
 typedef struct echo_state echo_state; /* opaque host handle */
@@ -88,9 +91,10 @@ typedef struct echo_state echo_state; /* opaque host handle */
 typedef void* echo_stream_t; /* a hipStream_t */
 
 /* Bytes of device workspace a state needs: stage-1 payloads of the P ranks
- * (codes N/2 B + scales 4N/group B each), the broadcast payload, and the two
- * compensator vectors of both directions (2 x 2 x 4N B), plus alignment
- * slack.  Returns 0 for an invalid configuration and for N == 0. */
+ * (codes N/2 B + scales 4N/group B each), the broadcast payload, the two
+ * compensator vectors of both directions (2 x 2 x 4N B) and, with
+ * sender_feedback, every rank's stage-1 error for both directions
+ * (2 x P x 4N B), plus alignment slack.  Returns 0 for an invalid configuration and for N == 0. */
 size_t echo_workspace_bytes(const echo_config* cfg);
 
 /* Create a state over a caller-owned device workspace of `ws_bytes` bytes
@@ -114,8 +118,11 @@ echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
                         echo_dir dir, echo_stream_t stream);
 
 /* Stage 1 on every rank: quantize each rank's partial to int4 codes and fp32
- * group scales in the state's stage-1 payload buffers (the "wire"). */
-echo_status echo_stage1(const void* const* partials, echo_state* st, echo_stream_t stream);
+ * group scales in the state's stage-1 payload buffers (the "wire").  `dir`
+ * selects the ranks' stage-1 errors when sender_feedback is on (otherwise it
+ * is only validated). */
+echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir dir,
+                        echo_stream_t stream);
 
 /* Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
  * apply the correction of direction `dir`, re-quantize into the broadcast
@@ -125,8 +132,9 @@ echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream);
 /* Every rank's decode of the broadcast payload into `out` (N fp32). */
 echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream);
 
-/* Zero the compensator of the directions in dir_mask (1 = fwd, 2 = bwd,
- * 3 = both), e.g. at the start of every pass over the layer stack.
+/* Zero the compensator (and, with sender_feedback, the ranks' stage-1 errors)
+ * of the directions in dir_mask (1 = fwd, 2 = bwd, 3 = both), e.g. at the
+ * start of every pass over the layer stack.
  * Uses a fill kernel (no memset node), so it may be captured in a graph. */
 echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream);
 
@@ -151,6 +159,8 @@ typedef struct {
   const float* bcast_scales;   /* N/group fp32                                             */
   float* m_fast;               /* N fp32, compensator of the requested direction           */
   float* m_slow;               /* N fp32                                                   */
+  float* sender_err;           /* rank r: (char*)sender_err + r*sender_err_stride, N fp32, */
+  size_t sender_err_stride;    /* the requested direction; NULL without sender_feedback   */
 } echo_views;
 
 echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out);

@@ -161,24 +161,30 @@ def wire_bytes(P: int, N: int, group: int = GROUP):
 # compensator state
 # ----------------------------------------------------------------------------
 class OracleState:
-    """(m_fast, m_slow) per direction, fp32, all zero after a reset."""
+    """(m_fast, m_slow) per direction, fp32, all zero after a reset; with the
+    sender-feedback variant also every rank's stage-1 error per direction
+    (``sender_err[d]``, [P, N] fp32, created zero on first use)."""
 
     def __init__(self, N: int):
         self.N = N
         self.m_fast = {FWD: np.zeros(N, F32), BWD: np.zeros(N, F32)}
         self.m_slow = {FWD: np.zeros(N, F32), BWD: np.zeros(N, F32)}
+        self.sender_err = {FWD: None, BWD: None}
 
     def reset(self, mask: int = 3):
         for d in (FWD, BWD):
             if mask & (1 << d):
                 self.m_fast[d][:] = 0
                 self.m_slow[d][:] = 0
+                if self.sender_err[d] is not None:
+                    self.sender_err[d][:] = 0
 
     def copy(self) -> "OracleState":
         o = OracleState(self.N)
         for d in (FWD, BWD):
             o.m_fast[d] = self.m_fast[d].copy()
             o.m_slow[d] = self.m_slow[d].copy()
+            o.sender_err[d] = None if self.sender_err[d] is None else self.sender_err[d].copy()
         return o
 
 
@@ -187,11 +193,18 @@ class OracleState:
 # ----------------------------------------------------------------------------
 def echo_call(partials, state: OracleState | None, direction: int = FWD,
               compensate: bool = True, beta_fast: float = 0.5,
-              beta_slow: float = 0.95, group: int = GROUP):
+              beta_slow: float = 0.95, group: int = GROUP,
+              sender_feedback: bool = False):
     """One Echo all-reduce of ``partials`` ([P, N] float32).
 
     Advances ``state`` (direction ``direction``) in place when compensating and
     returns a dict with every intermediate the GPU path exposes.
+
+    ``sender_feedback`` is a variant the pages leave open: every rank also
+    feeds the error of its own stage-1 rounding into its next call (classic
+    error feedback): x' = fl(x + e), (q, s) = Q(x'), e <- fl(x' - fl(q * s)),
+    the last difference exact.  The stage-1 errors then telescope, so the
+    accumulated end-to-end error stays bounded too.
     """
     x = np.ascontiguousarray(partials, dtype=F32)
     if x.ndim != 2:
@@ -203,13 +216,22 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         raise ValueError("partials must be finite")
     n_g = N // group
 
-    # 1. stage 1 on every rank
+    # 1. stage 1 on every rank (with sender feedback: on x + e, then the new e)
     q1 = np.empty((P, N), np.int8)
     s1 = np.empty((P, n_g), F32)
+    if sender_feedback:
+        if state.sender_err[direction] is None or state.sender_err[direction].shape != (P, N):
+            state.sender_err[direction] = np.zeros((P, N), F32)
+        e1 = state.sender_err[direction]
+        xs = x + e1
+    else:
+        xs = x
     for r in range(P):
-        q, s = quantize_groups(x[r], group)
+        q, s = quantize_groups(xs[r], group)
         q1[r] = q.reshape(-1)
         s1[r] = s
+        if sender_feedback:
+            e1[r] = xs[r] - dequantize_groups(q, s, group).reshape(-1)
 
     # 2.-6. each owner works on its own segment of every rank's payload
     S = np.empty(N, F32)
@@ -262,6 +284,7 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         "codes1": np.stack([pack_nibbles(q1[r]) for r in range(P)]) if P else np.zeros((0, N // 2), np.uint8),
         "scales1": s1,
         "q1": q1,
+        "x1": xs,
         "S": S,
         "c": c,
         "V": V,

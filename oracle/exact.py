@@ -118,20 +118,27 @@ def dequantize(codes, scales, group=GROUP):
 
 
 def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
-              beta_slow=0.95, group=GROUP):
+              beta_slow=0.95, group=GROUP, sender_err=None):
     """One call on exact binary32 values.
 
     ``partials`` is a list of P lists of Fractions (each a binary32 value);
     ``m_fast``/``m_slow`` are lists of Fractions, updated in place when
-    compensating.  Returns a dict of lists of Fractions / ints.
+    compensating; ``sender_err``, if given, is the P ranks' stage-1 error
+    lists (the sender-feedback variant), updated in place.  Returns a dict of
+    lists of Fractions / ints.
     """
     P = len(partials)
     N = len(partials[0])
     q1, s1 = [], []
     for r in range(P):
-        q, s = quantize(partials[r], group)
+        # sender feedback (a variant): quantize x + e and keep the new error
+        x = partials[r] if sender_err is None else [add(a, b) for a, b in zip(partials[r], sender_err[r])]
+        q, s = quantize(x, group)
         q1.append(q)
         s1.append(s)
+        if sender_err is not None:
+            deq = dequantize(q, s, group)
+            sender_err[r][:] = [sub(a, b) for a, b in zip(x, deq)]
     S = []
     for i in range(N):
         acc = None

@@ -27,10 +27,12 @@ def _upload(raw, dtype, device):
     return [t[r].to(device).contiguous() for r in range(t.shape[0])]
 
 
-def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True, group=32):
+def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True, group=32,
+           sender_feedback=False):
     torch = _torch()
     import error_compensated_bit_echo_amd as E
-    cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1], group=group)
+    cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1], group=group,
+                            sender_feedback=sender_feedback)
     ws = torch.full((max(E.echo_workspace_bytes(cfg), 1),), 0xFF if poison else 0,
                     dtype=torch.uint8, device=device)
     return E.echo_init_state(cfg, ws)
@@ -53,6 +55,7 @@ def _fetch(state, out, direction, lo=0, hi=None):
         "m_fast": v["m_fast"][lo:hi].cpu().numpy(),
         "m_slow": v["m_slow"][lo:hi].cpu().numpy(),
         "out": out[lo:hi].cpu().numpy(),
+        "sender_err": None if v["sender_err"] is None else v["sender_err"][:, lo:hi].cpu().numpy(),
     }
 
 
@@ -73,6 +76,14 @@ def _compare(g, o, st_oracle, direction, compensate, where=""):
         got = g[key]
         d = np.abs(got.astype(F64) - want.astype(F64))
         assert np.all(d <= TOL * s2), f"{key} off by {d.max()} {where}"
+        inexact += int(np.count_nonzero(got != want))
+    if g.get("sender_err") is not None:
+        # the ranks' stage-1 errors (sender-feedback variant), against each rank's scales
+        want = st_oracle.sender_err[direction]
+        got = g["sender_err"]
+        s1 = np.repeat(o["scales1"].astype(F64), got.shape[1] // o["scales1"].shape[1], axis=1)
+        d = np.abs(got.astype(F64) - want.astype(F64))
+        assert np.all(d <= TOL * s1), f"sender_err off by {d.max()} {where}"
         inexact += int(np.count_nonzero(got != want))
     return inexact
 

@@ -43,7 +43,8 @@ def test_config_struct_layout():
     assert ctypes.sizeof(B.EchoConfig) == 40
     assert B.EchoConfig.numel.offset == 8
     assert B.EchoConfig.beta_slow.offset == 32
-    assert ctypes.sizeof(B.EchoViews) == 64
+    assert ctypes.sizeof(B.EchoViews) == 80
+    assert B.EchoConfig.sender_feedback.offset == 36
 
 
 def _ws(cfg):
@@ -58,6 +59,9 @@ def test_workspace_bytes_formula():
         sc = 4 * (N // G)
         want = P * (al(N // 2) + al(sc)) + al(N // 2) + al(sc) + 4 * al(4 * N) + 256
         assert _ws(cfg) == want
+        # sender feedback adds every rank's stage-1 error vector for both directions
+        cfg = B.EchoConfig.make(P, N, dt, group=G, sender_feedback=True)
+        assert _ws(cfg) == want + 2 * P * al(4 * N)
     assert _ws(B.EchoConfig.make(4, 0)) == 0
 
 
@@ -68,7 +72,7 @@ def test_workspace_bytes_formula():
     ("group", 16, B.ECHO_ERR_SHAPE), ("group", 256, B.ECHO_ERR_SHAPE), ("numel", 4096 + 32 * 3, B.ECHO_ERR_SHAPE),
     ("dtype", 7, B.ECHO_ERR_DTYPE), ("compensate", 2, B.ECHO_ERR_ARG),
     ("beta_fast", -0.5, B.ECHO_ERR_ARG), ("beta_slow", float("nan"), B.ECHO_ERR_ARG),
-    ("beta_slow", 1.5, B.ECHO_ERR_ARG),
+    ("beta_slow", 1.5, B.ECHO_ERR_ARG), ("sender_feedback", 2, B.ECHO_ERR_ARG),
 ])
 def test_init_rejects_bad_config_without_touching_the_gpu(field, value, status):
     lib = B.load_library()
@@ -96,7 +100,7 @@ def test_calls_on_a_null_state_are_rejected():
     assert lib.echo_owner(None, 0, None) == B.ECHO_ERR_STATE
     assert lib.echo_reset(None, 3, None) == B.ECHO_ERR_STATE
     assert lib.echo_decode(None, None, None) == B.ECHO_ERR_STATE
-    assert lib.echo_stage1(None, None, None) == B.ECHO_ERR_STATE
+    assert lib.echo_stage1(None, None, 0, None) == B.ECHO_ERR_STATE
     assert lib.echo_reduce(None, None, None, 0, None) == B.ECHO_ERR_STATE
     x = ctypes.c_uint64()
     assert lib.echo_wire_bytes(None, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x)) == B.ECHO_ERR_STATE

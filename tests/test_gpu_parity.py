@@ -310,7 +310,7 @@ def _windows(N, n_win, width, seed):
 
 
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
-                  P=None, N=None, compensate=True):
+                  P=None, N=None, compensate=True, sender_feedback=False):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
     value distribution and dtype)."""
@@ -319,7 +319,7 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     c = synth.CONFIGS[cfg_id]
     P = c["P"] if P is None else P
     N = synth.numel(cfg_id) if N is None else N
-    st = _state(P, N, c["dtype"], compensate=compensate, poison=False)
+    st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     wins = _windows(N, n_win, width, cfg_id)
     so = {w: eo.OracleState(width) for w in wins}
@@ -332,7 +332,7 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
             E.echo_reduce(parts, out, st, d)
             for w in wins:
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
-                o = eo.echo_call(host, so[w], d, compensate=compensate)
+                o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback)
                 g = _fetch(st, out, d, w, w + width)
                 assert _compare(g, o, so[w], d, compensate,
                                 f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}") == 0
@@ -364,3 +364,75 @@ def test_fp32_partials_of_2GiB(cuda):
 def test_full_size_without_compensation(cuda):
     """The plain two-rounding all-reduce (state untouched) at the prefill size."""
     _windowed_run(cuda, 2, 4, (0,), compensate=False)
+
+
+# ---------------------------------------------------------------------------
+# sender-side error feedback (a variant): every rank feeds its own stage-1
+# rounding error into its next call
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_sender_feedback_tiny_config_every_call(cuda, compensate):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.CONFIGS[1]
+    P, N = c["P"], synth.numel(1)
+    st = _state(P, N, "f32", compensate, sender_feedback=True)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(c["calls"]):
+        raw, vals = synth.host_partials(1, 0, t)
+        E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, sender_feedback=True)
+        assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}") == 0
+
+
+@pytest.mark.parametrize("P,dtype,group", [(1, "bf16", 32), (3, "f32", 32), (8, "bf16", 32),
+                                           (16, "bf16", 64), (4, "bf16", 128)])
+def test_sender_feedback_multi_tile_both_directions(cuda, P, dtype, group):
+    """Ragged tiles, tie-rich and normal data, forward and backward calls
+    interleaved (separate sender errors per direction), a forward reset midway."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = 2048 * 5 + group * 3
+    st = _state(P, N, dtype, group=group, sender_feedback=True)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    rng = np.random.default_rng(P * 1000 + group)
+    for t in range(6):
+        if t == 3:
+            E.echo_reset(st, 1)
+            so.reset(1)
+        for d in (0, 1):
+            if (t + d) % 2:
+                vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+                raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
+            else:
+                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+            E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, group=group, sender_feedback=True)
+            assert _compare(_fetch(st, out, d), o, so, d, True, f"G={group} P={P} call {t} dir {d}") == 0
+
+
+def test_sender_feedback_stage_entry_points_equal_reduce(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 8, 32 * 4096
+    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    parts = _upload(raw, "bf16", cuda)
+    s1 = _state(P, N, "bf16", sender_feedback=True)
+    s2 = _state(P, N, "bf16", sender_feedback=True)
+    o1 = torch.empty(N, dtype=torch.float32, device=cuda)
+    o2 = torch.empty(N, dtype=torch.float32, device=cuda)
+    for d in (0, 1, 1, 0):
+        E.echo_reduce(parts, o1, s1, d)
+        E.echo_stage1(parts, s2, d)
+        E.echo_owner(s2, d)
+        E.echo_decode(o2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for d in (0, 1):
+        assert torch.equal(E.echo_debug_views(s1, d)["sender_err"], E.echo_debug_views(s2, d)["sender_err"])
+
+
+def test_sender_feedback_full_size(cuda):
+    _windowed_run(cuda, 2, 4, (0,), sender_feedback=True)

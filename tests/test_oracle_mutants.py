@@ -47,6 +47,10 @@ MUTANTS = {
     "zero group given a tiny scale": (
         "s = a / F32(QMAX)  # binary32 division, round to nearest even",
         "s = np.maximum(a / F32(QMAX), F32(1e-30))"),
+    "sender error from the partial, not from x + e": (
+        "e1[r] = xs[r] - dequantize_groups(q, s, group).reshape(-1)",
+        "e1[r] = x[r] - dequantize_groups(q, s, group).reshape(-1)"),
+    "sender error added with the wrong sign": ("xs = x + e1", "xs = x - e1"),
     "estimate biased by a tiny constant": (
         "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bf * mf[e0:e1] + wf * rr + F32(1e-30)"),
 }

@@ -474,3 +474,73 @@ def test_synth_recipe_is_deterministic_and_rounds_to_bf16():
     err = np.abs(vals.astype(F64) - raw.astype(F64))
     ulp = np.abs(np.spacing(vals.astype(F32))).astype(F64) * 2 ** 16
     assert np.all(err <= ulp / 2)
+
+
+# ---------------------------------------------------------------------------
+# sender-side error feedback (a variant): exact rationals, telescoping,
+# bounded end-to-end error
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_sender_feedback_matches_exact_rationals(compensate):
+    P, N, T = 3, 64, 8
+    st = eo.OracleState(N)
+    mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
+    se = [[Fraction(0)] * N for _ in range(P)]
+    for t in range(T):
+        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        o = eo.echo_call(x, st, compensate=compensate, sender_feedback=True)
+        e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, sender_err=se)
+        for r in range(P):
+            assert np.array_equal(o["q1"][r], np.array(e["q1"][r], np.int8)), (t, r)
+            assert np.array_equal(o["scales1"][r], _as_f32(e["scales1"][r]))
+            assert np.array_equal(st.sender_err[0][r], _as_f32(se[r])), (t, r)
+        for key in ("S", "V", "B", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+
+
+def test_sender_feedback_telescopes():
+    """Sum over calls and ranks of (dequantized stage-1 value - partial) equals
+    minus the final sender errors plus the binary32 roundings of x + e, exactly."""
+    P, N, T = 2, 64, 12
+    st = eo.OracleState(N)
+    lhs = [Fraction(0)] * N
+    rounding = [Fraction(0)] * N
+    for t in range(T):
+        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        e_before = st.sender_err[0].copy() if st.sender_err[0] is not None else np.zeros((P, N), F32)
+        o = eo.echo_call(x, st, sender_feedback=True)
+        deq = eo.dequantize_groups(o["q1"].reshape(P, -1), o["scales1"].reshape(-1)).reshape(P, N)
+        for r in range(P):
+            for i in range(N):
+                lhs[i] += Fraction(float(deq[r, i])) - Fraction(float(x[r, i]))
+                exact_sum = Fraction(float(x[r, i])) + Fraction(float(e_before[r, i]))
+                rounding[i] += Fraction(float(o["x1"][r, i])) - exact_sum
+    for i in range(N):
+        final = sum(Fraction(float(st.sender_err[0][r, i])) for r in range(P))
+        assert lhs[i] == -final + rounding[i]
+
+
+def test_sender_feedback_bounds_end_to_end_error():
+    """With sender feedback and compensation the accumulated end-to-end error
+    sum_t (out_t - sum_r x_t,r) stays flat; without sender feedback it grows
+    like a random walk (stage-1 roundings are not compensated then)."""
+    P, N = 2, 2048
+
+    def run(T, sfb):
+        st = eo.OracleState(N)
+        acc = np.zeros(N, F64)
+        rms = []
+        for t in range(T):
+            _, x = synth.host_partials(1, 0, t, P=P, n=N)
+            o = eo.echo_call(x, st, sender_feedback=sfb)
+            acc += o["out"].astype(F64) - eo.plain_sum(x)
+            rms.append(np.sqrt(np.mean(acc ** 2)))
+        return np.array(rms)
+
+    with_fb, without = run(256, True), run(256, False)
+    # flat with feedback: no growth between the first 16 and the last 16 calls
+    assert with_fb[-16:].mean() < 1.3 * with_fb[:16].mean()
+    assert with_fb.max() < 3.0 * with_fb[:16].mean()
+    # a random walk without: sqrt(256/16) = 4 times larger at the end
+    assert without[-16:].mean() > 2.5 * without[:16].mean()
+    assert without[-1] > 3.0 * with_fb[-1]
