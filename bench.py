@@ -35,7 +35,7 @@ KERNEL_KEYS = {"stage1": "echo_quant_pack_k", "owner": "echo_owner_k", "decode":
 
 
 def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool, group: int = 32,
-                      sender_feedback: bool = False) -> dict:
+                      sender_feedback: bool = False, state_bf16: bool = False) -> dict:
     """Bytes each stage must move per call (reads + writes of HBM)."""
     pl = 0.5 + 4.0 / group                     # payload bytes per element: codes + scales
     k1 = P * N * (b_in + pl)                   # read partials; write codes + scales
@@ -43,16 +43,17 @@ def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool, group: int = 
         k1 += P * N * 8.0                      # read and write every rank's stage-1 error
     k2 = N * (pl * P + pl)                     # read P payload segments; write broadcast payload
     if compensate:
-        k2 += 16.0 * N                         # read and write m_fast, m_slow
+        k2 += (8.0 if state_bf16 else 16.0) * N  # read and write m_fast, m_slow
     k3 = N * (pl + 4.0)                        # read broadcast payload; write fp32 out
     return {"stage1": k1, "owner": k2, "decode": k3}
 
 
-def workload_tag(comp: bool, group: int = 32, sender_feedback: bool = False) -> str:
+def workload_tag(comp: bool, group: int = 32, sender_feedback: bool = False,
+                 state_bf16: bool = False) -> str:
     tag = f"1GiB-P8-bf16-{'comp' if comp else 'nocomp'}"
     if group != 32:
         tag += f"-g{group}"
-    return tag + ("-sfb" if sender_feedback else "")
+    return tag + ("-sfb" if sender_feedback else "") + ("-sb16" if state_bf16 else "")
 
 
 def kernel_source_hash() -> str:
@@ -128,7 +129,7 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
 # ---------------------------------------------------------------------------
 # the other workloads: latency, effective bandwidth and accuracy reports
 # ---------------------------------------------------------------------------
-CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2, "sender": 2}
+CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2, "variants": 2}
 CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
 
 
@@ -359,19 +360,26 @@ def tp_report(torch, dev) -> dict:
 
 
 def sender_report(E, synth, torch, dev) -> dict:
-    """The sender-feedback variant on the prefill workload (P = 4, bf16
-    [2048, 4096], 72 calls, fresh partials per call): error of the residual
-    stream h_T = sum of all outputs against the exact stream, by call count T,
-    with sender feedback and compensation each on and off; per-call latency."""
+    """The variants on the prefill workload (P = 4, bf16 [2048, 4096], 72 calls,
+    fresh partials per call): error of the residual stream h_T = sum of all
+    outputs against the exact stream, by call count T, for compensation on/off,
+    sender feedback on/off and fp32 or bf16 state; per-call latency of each."""
     c = synth.CONFIGS[2]
     P, N, calls = c["P"], synth.numel(2), c["calls"]
-    modes = {(sfb, comp): E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=comp,
-                                                              sender_feedback=sfb), device=dev)
-             for sfb in (True, False) for comp in (True, False)}
+    # (compensate, sender feedback, bf16 state)
+    combos = [(True, False, False), (False, False, False), (True, True, False), (False, True, False),
+              (True, False, True), (True, True, True)]
+
+    def name(k):
+        return (f"comp_{'on' if k[0] else 'off'}_sfb_{'on' if k[1] else 'off'}"
+                f"_state_{'bf16' if k[2] else 'fp32'}")
+
+    modes = {k: E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=k[0], sender_feedback=k[1],
+                                                   state_bf16=k[2]), device=dev) for k in combos}
     out = torch.empty(N, dtype=torch.float32, device=dev)
     h = {k: torch.zeros(N, dtype=torch.float64, device=dev) for k in modes}
     hx = torch.zeros(N, dtype=torch.float64, device=dev)
-    err = {f"sfb_{'on' if k[0] else 'off'}_comp_{'on' if k[1] else 'off'}": {} for k in modes}
+    err = {name(k): {} for k in modes}
     for t in range(calls):
         parts = synth.device_partials(2, 0, t, device=dev)
         for k, st in modes.items():
@@ -382,17 +390,16 @@ def sender_report(E, synth, torch, dev) -> dict:
         T = t + 1
         if T & (T - 1) == 0 or T == calls:
             for k in modes:
-                e = (h[k] - hx).pow(2).mean().sqrt().item()
-                err[f"sfb_{'on' if k[0] else 'off'}_comp_{'on' if k[1] else 'off'}"][str(T)] = e
+                err[name(k)][str(T)] = (h[k] - hx).pow(2).mean().sqrt().item()
     lat = {}
-    for sfb in (True, False):
-        gst = E.echo_init_state(E.EchoConfig.make(P, N, "bf16", sender_feedback=sfb), device=dev)
+    for k in combos:
+        gst = E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=k[0], sender_feedback=k[1],
+                                                 state_bf16=k[2]), device=dev)
         g, _ = _graph_us(E, torch, parts, torch.empty_like(out), gst, E.ECHO_FWD, 20)
-        lat[f"sfb_{'on' if sfb else 'off'}"] = round(_pct(g, 0.5), 2)
-    return {"config": "sender", "P": P, "numel_per_rank": N, "calls": calls,
+        lat[name(k)] = round(_pct(g, 0.5), 2)
+    return {"config": "variants", "P": P, "numel_per_rank": N, "calls": calls,
             "rms_err_of_accumulated_output_vs_exact_by_calls": err,
             "us_per_call_graph_32_calls": lat}
-
 
 def cpu_baseline(parts, n_sample: int) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
@@ -429,6 +436,8 @@ def main():
                     help="elements per scale (32; 64 and 128 are variants)")
     ap.add_argument("--sender-feedback", action="store_true",
                     help="variant: every rank feeds its stage-1 rounding error into its next call")
+    ap.add_argument("--bf16-state", action="store_true",
+                    help="variant: the compensator's two estimates stored in bfloat16")
     ap.add_argument("--cpu-sample", type=int, default=1 << 25,
                     help="elements per rank in the CPU oracle's timed sample")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle leg")
@@ -443,7 +452,8 @@ def main():
 
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters,
-                              workload=workload_tag(not args.no_comp, args.group, args.sender_feedback),
+                              workload=workload_tag(not args.no_comp, args.group, args.sender_feedback,
+                                                    args.bf16_state),
                               command=args.counter_command)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
@@ -467,7 +477,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config:
-        names = ["tiny", "prefill", "decode", "training", "tp", "groups", "sender"] if args.config == "all" \
+        names = ["tiny", "prefill", "decode", "training", "tp", "groups", "variants"] if args.config == "all" \
             else [args.config]
         for name in names:
             print(f"# config {name}", file=sys.stderr, flush=True)
@@ -479,7 +489,7 @@ def main():
                 continue
             if name == "decode":
                 rep = decode_report(E, synth, torch, dev)
-            elif name == "sender":
+            elif name == "variants":
                 rep = sender_report(E, synth, torch, dev)
             elif name == "tp":
                 rep = tp_report(torch, dev)
@@ -495,8 +505,9 @@ def main():
     print(f"# generating {P} x {N} bf16 partials on the device", file=sys.stderr, flush=True)
     parts = synth.device_partials(cfg_id, 0, 0, device=dev)
     G = args.group
-    SFB = args.sender_feedback
-    cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp, group=G, sender_feedback=SFB)
+    SFB, SB16 = args.sender_feedback, args.bf16_state
+    cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp, group=G, sender_feedback=SFB,
+                            state_bf16=SB16)
     st = E.echo_init_state(cfg, device=dev)
     out = torch.empty(N, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -533,7 +544,7 @@ def main():
     print(f"# timed {K} calls: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
-    alg = algorithmic_bytes(P, N, 2, comp, G, SFB)
+    alg = algorithmic_bytes(P, N, 2, comp, G, SFB, SB16)
     total_alg = sum(alg.values())
     kernels = {}
     for k, ms in kern_ms.items():
@@ -542,7 +553,7 @@ def main():
                       "frac": round(alg[k] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     dom = max(kern_ms, key=kern_ms.get)
     achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    workload = workload_tag(comp, G, SFB)
+    workload = workload_tag(comp, G, SFB, SB16)
     traffic = measured_traffic(dom, workload)
 
     # a plain streaming copy kernel of 2 GiB (torch's elementwise x*1, read 2 GiB,
@@ -580,7 +591,7 @@ def main():
         "config": {
             "workload": "1 GiB bf16 message per rank (536,870,912 elements), P=8 emulated ranks, "
                         f"group {G}, absmax/7 fp32 scales, compensation " + ("on" if comp else "off") +
-                        (", sender feedback" if SFB else "") +
+                        (", sender feedback" if SFB else "") + (", bf16 state" if SB16 else "") +
                         ", same partials every call, reset -> warm-up -> reset -> timed calls",
             "P": P, "numel_per_rank": N, "input_dtype": "bf16", "wire": "int4 codes + fp32 group scales",
             "output_dtype": "f32", "group": G,

@@ -39,17 +39,18 @@ class EchoConfig(ctypes.Structure):
         ("beta_fast", ctypes.c_float),
         ("beta_slow", ctypes.c_float),
         ("sender_feedback", ctypes.c_int32),
+        ("state_bf16", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, P: int, numel: int, dtype: str = "bf16", compensate: bool = True,
              beta_fast: float = 0.5, beta_slow: float = 0.95, group: int = ECHO_GROUP,
-             sender_feedback: bool = False) -> "EchoConfig":
+             sender_feedback: bool = False, state_bf16: bool = False) -> "EchoConfig":
         d = {"f32": ECHO_F32, "float32": ECHO_F32, "bf16": ECHO_BF16, "bfloat16": ECHO_BF16}
         if dtype not in d:
             raise EchoError(ECHO_ERR_DTYPE, f"dtype {dtype!r}")
         return cls(P, numel, group, d[dtype], int(bool(compensate)), beta_fast, beta_slow,
-                   int(bool(sender_feedback)))
+                   int(bool(sender_feedback)), int(bool(state_bf16)))
 
 
 class EchoViews(ctypes.Structure):
@@ -275,6 +276,7 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
         return ws[off:off + nbytes]
 
     cs, ss = v.stage1_codes_stride, v.stage1_scales_stride
+    sb, sdt = (2, torch.bfloat16) if state.cfg.state_bf16 else (4, torch.float32)
     codes1 = sl(v.stage1_codes, P * cs).view(P, cs)[:, :N // 2]
     scales1 = sl(v.stage1_scales, P * ss).view(torch.float32).view(P, ss // 4)[:, :N // G]
     return {
@@ -282,8 +284,9 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
         "scales1": scales1,
         "codes2": sl(v.bcast_codes, N // 2),
         "scales2": sl(v.bcast_scales, 4 * (N // G)).view(torch.float32),
-        "m_fast": sl(v.m_fast, 4 * N).view(torch.float32),
-        "m_slow": sl(v.m_slow, 4 * N).view(torch.float32),
+        # bfloat16 vectors with the state_bf16 variant, fp32 otherwise
+        "m_fast": sl(v.m_fast, sb * N).view(sdt),
+        "m_slow": sl(v.m_slow, sb * N).view(sdt),
         # sender feedback: [P, N] stage-1 errors of the ranks for ``direction``
         "sender_err": None if not v.sender_err else
         sl(v.sender_err, P * v.sender_err_stride).view(torch.float32)

@@ -20,9 +20,10 @@ struct echo_state {
   float* m_fast[2];             // per direction
   float* m_slow[2];
   float* state_base;            // both directions, contiguous, then the sender errors
-  int64_t vec_floats;           // floats per state vector (with alignment padding)
+  int64_t vec_words;            // 4-byte words per compensator vector (fp32 or bf16, padded)
+  int64_t err_floats;           // floats per sender-error vector (padded)
   float* sender_err[2];         // sender feedback: rank r of direction d at
-                                // sender_err[d] + r * vec_floats; nullptr when off
+                                // sender_err[d] + r * err_floats; nullptr when off
 };
 
 namespace {
@@ -34,7 +35,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Layout {
   size_t codes1_stride, scales1_stride;  // bytes per rank
   size_t off_codes1, off_scales1, off_codes2, off_scales2, off_state, off_sender;
-  size_t vec_bytes;                      // one fp32 state vector, aligned
+  size_t vec_bytes;                      // one compensator vector (fp32 or bf16), aligned
+  size_t err_bytes;                      // one rank's fp32 sender-error vector, aligned
   size_t total;                          // without the base-alignment slack
 };
 
@@ -50,10 +52,11 @@ Layout make_layout(const echo_config& c) {
   L.off_codes2 = L.off_scales1 + P * L.scales1_stride;
   L.off_scales2 = L.off_codes2 + align_up(N / 2);
   L.off_state = L.off_scales2 + align_up(scale_bytes);
-  L.vec_bytes = align_up(4 * N);
+  L.vec_bytes = align_up((c.state_bf16 ? 2 : 4) * N);
+  L.err_bytes = align_up(4 * N);
   L.off_sender = L.off_state + 4 * L.vec_bytes;
   // sender feedback: every rank's stage-1 error, per direction, after the state
-  L.total = L.off_sender + (c.sender_feedback ? 2 * P * L.vec_bytes : 0);
+  L.total = L.off_sender + (c.sender_feedback ? 2 * P * L.err_bytes : 0);
   return L;
 }
 
@@ -67,6 +70,7 @@ echo_status check_cfg(const echo_config* c) {
   if (!(c->beta_fast >= 0.0f && c->beta_fast <= 1.0f)) return ECHO_ERR_ARG;  // also rejects NaN
   if (!(c->beta_slow >= 0.0f && c->beta_slow <= 1.0f)) return ECHO_ERR_ARG;
   if (c->sender_feedback != 0 && c->sender_feedback != 1) return ECHO_ERR_ARG;
+  if (c->state_bf16 != 0 && c->state_bf16 != 1) return ECHO_ERR_ARG;
   return ECHO_OK;
 }
 
@@ -118,7 +122,7 @@ echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hip
   a.scales_stride = st->scales1_stride_bytes / 4;
   a.nchunk = st->cfg.numel / echo::kElemsPerLane;
   a.err = st->sender_err[dir];
-  a.err_stride = st->vec_floats;
+  a.err_stride = st->err_floats;
   return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
@@ -142,7 +146,8 @@ echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
   a.omega_fast = 1.0f - st->cfg.beta_fast;  // fl(1 - beta)
   a.beta_slow = st->cfg.beta_slow;
   a.omega_slow = 1.0f - st->cfg.beta_slow;
-  return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, st->cfg.group, s) == hipSuccess
+  return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, st->cfg.group,
+                            st->cfg.state_bf16 != 0, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
@@ -194,14 +199,16 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
       st->m_slow[d] = reinterpret_cast<float*>(base + L.off_state + (2 * d + 1) * L.vec_bytes);
     }
     st->state_base = reinterpret_cast<float*>(base + L.off_state);
-    st->vec_floats = static_cast<int64_t>(L.vec_bytes / 4);
-    const int64_t sender_floats = cfg->sender_feedback ? 2 * cfg->P * st->vec_floats : 0;
+    st->vec_words = static_cast<int64_t>(L.vec_bytes / 4);
+    st->err_floats = static_cast<int64_t>(L.err_bytes / 4);
+    const int64_t sender_floats = cfg->sender_feedback ? 2 * cfg->P * st->err_floats : 0;
     for (int d = 0; d < 2; ++d)
       st->sender_err[d] = cfg->sender_feedback
-                              ? reinterpret_cast<float*>(base + L.off_sender) + d * cfg->P * st->vec_floats
+                              ? reinterpret_cast<float*>(base + L.off_sender) + d * cfg->P * st->err_floats
                               : nullptr;
     // the compensator vectors and the sender errors are contiguous: one fill
-    if (echo::launch_zero(st->state_base, 4 * st->vec_floats + sender_floats,
+    // (zero bits are +0 in fp32 and in bf16)
+    if (echo::launch_zero(st->state_base, 4 * st->vec_words + sender_floats,
                           static_cast<hipStream_t>(stream)) != hipSuccess) {
       delete st;
       return ECHO_ERR_HIP;
@@ -260,9 +267,9 @@ echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream) {
   for (int d = 0; d < 2; ++d) {
     if (!(dir_mask & (1 << d))) continue;
     // m_fast[d] and m_slow[d] are adjacent: one fill covers both
-    if (echo::launch_zero(st->m_fast[d], 2 * st->vec_floats, s) != hipSuccess) return ECHO_ERR_HIP;
+    if (echo::launch_zero(st->m_fast[d], 2 * st->vec_words, s) != hipSuccess) return ECHO_ERR_HIP;
     if (st->sender_err[d] != nullptr &&
-        echo::launch_zero(st->sender_err[d], st->cfg.P * st->vec_floats, s) != hipSuccess)
+        echo::launch_zero(st->sender_err[d], st->cfg.P * st->err_floats, s) != hipSuccess)
       return ECHO_ERR_HIP;
   }
   return ECHO_OK;
@@ -308,7 +315,7 @@ echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out
   out->m_fast = st->m_fast[dir];
   out->m_slow = st->m_slow[dir];
   out->sender_err = st->sender_err[dir];
-  out->sender_err_stride = st->sender_err[dir] != nullptr ? static_cast<size_t>(4 * st->vec_floats) : 0;
+  out->sender_err_stride = st->sender_err[dir] != nullptr ? static_cast<size_t>(4 * st->err_floats) : 0;
   return ECHO_OK;
 }
 

@@ -29,7 +29,7 @@ struct OwnerArgs {
   const float* scales1[kMaxRanks];    // stage-1 scales of rank r
   uint32_t* codes2;
   float* scales2;
-  float* m_fast;
+  float* m_fast;  // fp32, or bfloat16 bits when the kernel's SB16 switch is on
   float* m_slow;
   int64_t nchunk;
   float beta_fast, omega_fast, beta_slow, omega_slow;
@@ -37,7 +37,9 @@ struct OwnerArgs {
 
 // group: 32, 64 or 128 elements per scale
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s);
-hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, hipStream_t s);
+// state_bf16: m_fast / m_slow hold bfloat16 (the variant), else fp32
+hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                        hipStream_t s);
 hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
                          int64_t numel, int group, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);

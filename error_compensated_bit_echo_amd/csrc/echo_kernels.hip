@@ -275,7 +275,23 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
 // order, correction, stage-2 quantization, error and both estimates.
 // grid = ceil(nchunk / 256); one lane per chunk.
 // ---------------------------------------------------------------------------
-template <int P, bool COMP, int POL, int LPG, bool FULL>
+// Eight fp32 values rounded to bfloat16 (nearest, ties to even: adding
+// 0x7FFF plus the lowest kept bit to the binary32 pattern carries into the
+// top 16 bits exactly when the dropped part is above half, or half with an
+// odd kept part) and packed two per word by one byte permutation.
+__device__ __forceinline__ u32x4 pack_bf16x8(const float (&m)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = __float_as_uint(m[2 * i]), hi = __float_as_uint(m[2 * i + 1]);
+    lo += 0x7FFFu + ((lo >> 16) & 1u);
+    hi += 0x7FFFu + ((hi >> 16) & 1u);
+    w[i] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // hi's top half : lo's top half
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int P, bool COMP, int POL, int LPG, bool SB16, bool FULL>
 __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
   const bool ok = FULL || c < a.nchunk;
   const int64_t g = c >> log2i(LPG);
@@ -290,13 +306,27 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
       s[r] = a.scales1[r][g];
     }
     if constexpr (COMP) {
-      const f32x4* pf = reinterpret_cast<const f32x4*>(a.m_fast) + 2 * c;
-      const f32x4* ps = reinterpret_cast<const f32x4*>(a.m_slow) + 2 * c;
       constexpr bool nt = (POL & kNtStateLd) != 0;
-      mf4[0] = ld<nt>(pf);
-      mf4[1] = ld<nt>(pf + 1);
-      ms4[0] = ld<nt>(ps);
-      ms4[1] = ld<nt>(ps + 1);
+      if constexpr (SB16) {
+        // 8 bfloat16 per vector and lane: one 16-byte load each, widened exactly
+        Raw<true> rf, rs;
+        rf.q[0] = ld<nt>(reinterpret_cast<const u32x4*>(a.m_fast) + c);
+        rs.q[0] = ld<nt>(reinterpret_cast<const u32x4*>(a.m_slow) + c);
+        float f[8], g[8];
+        widen<true>(rf, f);
+        widen<true>(rs, g);
+        mf4[0] = f32x4{f[0], f[1], f[2], f[3]};
+        mf4[1] = f32x4{f[4], f[5], f[6], f[7]};
+        ms4[0] = f32x4{g[0], g[1], g[2], g[3]};
+        ms4[1] = f32x4{g[4], g[5], g[6], g[7]};
+      } else {
+        const f32x4* pf = reinterpret_cast<const f32x4*>(a.m_fast) + 2 * c;
+        const f32x4* ps = reinterpret_cast<const f32x4*>(a.m_slow) + 2 * c;
+        mf4[0] = ld<nt>(pf);
+        mf4[1] = ld<nt>(pf + 1);
+        ms4[0] = ld<nt>(ps);
+        ms4[1] = ld<nt>(ps + 1);
+      }
     }
   } else {
 #pragma unroll
@@ -340,24 +370,29 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
         mf[j] = a.beta_fast * mf[j] + a.omega_fast * e;
         ms[j] = a.beta_slow * ms[j] + a.omega_slow * e;
       }
-      f32x4* pf = reinterpret_cast<f32x4*>(a.m_fast) + 2 * c;
-      f32x4* ps = reinterpret_cast<f32x4*>(a.m_slow) + 2 * c;
       constexpr bool nt = (POL & kNtStateSt) != 0;
-      st<nt>(f32x4{mf[0], mf[1], mf[2], mf[3]}, pf);
-      st<nt>(f32x4{mf[4], mf[5], mf[6], mf[7]}, pf + 1);
-      st<nt>(f32x4{ms[0], ms[1], ms[2], ms[3]}, ps);
-      st<nt>(f32x4{ms[4], ms[5], ms[6], ms[7]}, ps + 1);
+      if constexpr (SB16) {
+        st<nt>(pack_bf16x8(mf), reinterpret_cast<u32x4*>(a.m_fast) + c);
+        st<nt>(pack_bf16x8(ms), reinterpret_cast<u32x4*>(a.m_slow) + c);
+      } else {
+        f32x4* pf = reinterpret_cast<f32x4*>(a.m_fast) + 2 * c;
+        f32x4* ps = reinterpret_cast<f32x4*>(a.m_slow) + 2 * c;
+        st<nt>(f32x4{mf[0], mf[1], mf[2], mf[3]}, pf);
+        st<nt>(f32x4{mf[4], mf[5], mf[6], mf[7]}, pf + 1);
+        st<nt>(f32x4{ms[0], ms[1], ms[2], ms[3]}, ps);
+        st<nt>(f32x4{ms[4], ms[5], ms[6], ms[7]}, ps + 1);
+      }
     }
   }
 }
 
-template <int P, bool COMP, int POL, int LPG>
+template <int P, bool COMP, int POL, int LPG, bool SB16>
 __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * kBlock;
   if (cb + kBlock <= a.nchunk)
-    owner_tile<P, COMP, POL, LPG, true>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, SB16, true>(a, cb + threadIdx.x);
   else
-    owner_tile<P, COMP, POL, LPG, false>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, SB16, false>(a, cb + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -425,21 +460,24 @@ constexpr int kDecodeUnroll = 2;
 constexpr int kDecodePol = kNtOut;
 
 template <int P, int LPG, int POL = kOwnerPol>
-hipError_t owner_pg(const OwnerArgs& a, bool comp, hipStream_t s) {
-  const int64_t blocks = (a.nchunk + kBlock - 1) / kBlock;
-  if (comp)
-    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+hipError_t owner_pg(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.nchunk + kBlock - 1) / kBlock));
+  // without compensation the state is not touched, so its dtype does not matter
+  if (!comp)
+    hipLaunchKernelGGL((echo_owner_k<P, false, POL, LPG, false>), grid, dim3(kBlock), 0, s, a);
+  else if (sb16)
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, true>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_owner_k<P, false, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, false>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template <int P>
-hipError_t owner_p(const OwnerArgs& a, bool comp, int group, hipStream_t s) {
+hipError_t owner_p(const OwnerArgs& a, bool comp, int group, bool sb16, hipStream_t s) {
   switch (group) {
-    case 32: return owner_pg<P, 4>(a, comp, s);
-    case 64: return owner_pg<P, 8>(a, comp, s);
-    case 128: return owner_pg<P, 16>(a, comp, s);
+    case 32: return owner_pg<P, 4>(a, comp, sb16, s);
+    case 64: return owner_pg<P, 8>(a, comp, sb16, s);
+    case 128: return owner_pg<P, 16>(a, comp, sb16, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -482,24 +520,25 @@ hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipSt
   }
 }
 
-hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, hipStream_t s) {
+hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool sb16,
+                        hipStream_t s) {
   switch (P) {
-    case 1: return owner_p<1>(a, compensate, group, s);
-    case 2: return owner_p<2>(a, compensate, group, s);
-    case 3: return owner_p<3>(a, compensate, group, s);
-    case 4: return owner_p<4>(a, compensate, group, s);
-    case 5: return owner_p<5>(a, compensate, group, s);
-    case 6: return owner_p<6>(a, compensate, group, s);
-    case 7: return owner_p<7>(a, compensate, group, s);
-    case 8: return owner_p<8>(a, compensate, group, s);
-    case 9: return owner_p<9>(a, compensate, group, s);
-    case 10: return owner_p<10>(a, compensate, group, s);
-    case 11: return owner_p<11>(a, compensate, group, s);
-    case 12: return owner_p<12>(a, compensate, group, s);
-    case 13: return owner_p<13>(a, compensate, group, s);
-    case 14: return owner_p<14>(a, compensate, group, s);
-    case 15: return owner_p<15>(a, compensate, group, s);
-    case 16: return owner_p<16>(a, compensate, group, s);
+    case 1: return owner_p<1>(a, compensate, group, sb16, s);
+    case 2: return owner_p<2>(a, compensate, group, sb16, s);
+    case 3: return owner_p<3>(a, compensate, group, sb16, s);
+    case 4: return owner_p<4>(a, compensate, group, sb16, s);
+    case 5: return owner_p<5>(a, compensate, group, sb16, s);
+    case 6: return owner_p<6>(a, compensate, group, sb16, s);
+    case 7: return owner_p<7>(a, compensate, group, sb16, s);
+    case 8: return owner_p<8>(a, compensate, group, sb16, s);
+    case 9: return owner_p<9>(a, compensate, group, sb16, s);
+    case 10: return owner_p<10>(a, compensate, group, sb16, s);
+    case 11: return owner_p<11>(a, compensate, group, sb16, s);
+    case 12: return owner_p<12>(a, compensate, group, sb16, s);
+    case 13: return owner_p<13>(a, compensate, group, sb16, s);
+    case 14: return owner_p<14>(a, compensate, group, sb16, s);
+    case 15: return owner_p<15>(a, compensate, group, sb16, s);
+    case 16: return owner_p<16>(a, compensate, group, sb16, s);
     default: return hipErrorInvalidValue;
   }
 }

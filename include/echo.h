@@ -84,6 +84,8 @@ typedef struct {
   int32_t sender_feedback; /* 1 = variant: every rank also feeds its own stage-1 */
                       /* rounding error into its next call (x' = x + e, e <- x' - */
                       /* fl(q*s), per rank and direction); 0 = off (default)       */
+  int32_t state_bf16; /* 1 = variant: m_fast / m_slow stored in bfloat16 (each   */
+                      /* fp32 update rounded to nearest, ties to even); 0 = fp32  */
 } echo_config;
 
 typedef struct echo_state echo_state; /* opaque host handle */
@@ -92,7 +94,8 @@ typedef void* echo_stream_t; /* a hipStream_t */
 
 /* Bytes of device workspace a state needs: stage-1 payloads of the P ranks
  * (codes N/2 B + scales 4N/group B each), the broadcast payload, the two
- * compensator vectors of both directions (2 x 2 x 4N B) and, with
+ * compensator vectors of both directions (2 x 2 x 4N B, or 2 x 2 x 2N B with
+ * state_bf16) and, with
  * sender_feedback, every rank's stage-1 error for both directions
  * (2 x P x 4N B), plus alignment slack.  Returns 0 for an invalid configuration and for N == 0. */
 size_t echo_workspace_bytes(const echo_config* cfg);
@@ -157,8 +160,8 @@ typedef struct {
   size_t stage1_scales_stride; /* bytes between ranks                                      */
   const void* bcast_codes;     /* N/2 B: two's-complement nibbles, element 2k low nibble   */
   const float* bcast_scales;   /* N/group fp32                                             */
-  float* m_fast;               /* N fp32, compensator of the requested direction           */
-  float* m_slow;               /* N fp32                                                   */
+  void* m_fast;                /* N fp32 (N bf16 with state_bf16), compensator of the dir  */
+  void* m_slow;                /* N fp32 (N bf16 with state_bf16)                          */
   float* sender_err;           /* rank r: (char*)sender_err + r*sender_err_stride, N fp32, */
   size_t sender_err_stride;    /* the requested direction; NULL without sender_feedback   */
 } echo_views;

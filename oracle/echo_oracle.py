@@ -75,6 +75,20 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(F32)
 
 
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of every float32 (ties to even), as float32.
+
+    bfloat16 keeps binary32's exponent range with an 8-bit significand: a
+    normal value x = m * 2**e (0.5 <= |m| < 1) becomes rint(m * 2**8) * 2**(e-8);
+    below 2**-126 the step is fixed at 2**-133 (gradual underflow)."""
+    x = np.asarray(x, dtype=F32).astype(F64)
+    m, e = np.frexp(x)
+    normal = np.abs(x) >= 2.0 ** -126
+    r = np.where(normal, np.ldexp(np.rint(np.ldexp(m, 8)), e - 8),
+                 np.rint(x * 2.0 ** 133) * 2.0 ** -133)
+    return r.astype(F32)
+
+
 # ----------------------------------------------------------------------------
 # the quantizer Q
 # ----------------------------------------------------------------------------
@@ -194,7 +208,7 @@ class OracleState:
 def echo_call(partials, state: OracleState | None, direction: int = FWD,
               compensate: bool = True, beta_fast: float = 0.5,
               beta_slow: float = 0.95, group: int = GROUP,
-              sender_feedback: bool = False):
+              sender_feedback: bool = False, state_bf16: bool = False):
     """One Echo all-reduce of ``partials`` ([P, N] float32).
 
     Advances ``state`` (direction ``direction``) in place when compensating and
@@ -205,6 +219,10 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     error feedback): x' = fl(x + e), (q, s) = Q(x'), e <- fl(x' - fl(q * s)),
     the last difference exact.  The stage-1 errors then telescope, so the
     accumulated end-to-end error stays bounded too.
+
+    ``state_bf16`` is another variant: the two estimates are stored in
+    bfloat16, i.e. every update m <- fl(fl(beta*m) + fl(omega*r)) is rounded
+    to the nearest bfloat16 before it is kept.
     """
     x = np.ascontiguousarray(partials, dtype=F32)
     if x.ndim != 2:
@@ -276,6 +294,9 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
             err[e0:e1] = rr
             mf[e0:e1] = bf * mf[e0:e1] + wf * rr
             ms[e0:e1] = bs * ms[e0:e1] + ws * rr
+            if state_bf16:
+                mf[e0:e1] = round_to_bf16(mf[e0:e1])
+                ms[e0:e1] = round_to_bf16(ms[e0:e1])
 
     # 7. every rank decodes the broadcast payload
     codes2 = pack_nibbles(q2)

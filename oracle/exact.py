@@ -48,20 +48,33 @@ def _floor_log2(m: Fraction) -> int:
     return e
 
 
-def round_to_binary32(x) -> Fraction:
-    """Round an exact rational to the nearest binary32 value (ties to even)."""
+def round_to_format(x, prec: int, emin: int = _EMIN, emax: int = 127) -> Fraction:
+    """Round an exact rational to the nearest value of a binary format with a
+    ``prec``-bit significand (hidden bit included), normal exponents down to
+    ``emin`` and gradual underflow below, ties to even."""
     x = Fraction(x)
     if x == 0:
         return Fraction(0)
     sign = -1 if x < 0 else 1
     m = abs(x)
     e = _floor_log2(m)
-    quantum = Fraction(2) ** (e - (_PREC - 1)) if e >= _EMIN else _TINY
+    quantum = Fraction(2) ** ((e if e >= emin else emin) - (prec - 1))
     k = _round_half_even_int(m / quantum)
     r = k * quantum
-    if r >= _OVER:
-        raise OverflowError("result exceeds the binary32 range")
+    if r >= Fraction(2) ** (emax + 1):
+        raise OverflowError("result exceeds the format's range")
     return sign * r
+
+
+def round_to_binary32(x) -> Fraction:
+    """Round an exact rational to the nearest binary32 value (ties to even)."""
+    return round_to_format(x, _PREC)
+
+
+def round_to_bfloat16(x) -> Fraction:
+    """Round an exact rational to the nearest bfloat16 value (8-bit significand,
+    binary32's exponent range, subnormals down to 2**-133; ties to even)."""
+    return round_to_format(x, 8)
 
 
 def f32(x) -> Fraction:
@@ -118,7 +131,7 @@ def dequantize(codes, scales, group=GROUP):
 
 
 def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
-              beta_slow=0.95, group=GROUP, sender_err=None):
+              beta_slow=0.95, group=GROUP, sender_err=None, state_bf16=False):
     """One call on exact binary32 values.
 
     ``partials`` is a list of P lists of Fractions (each a binary32 value);
@@ -162,5 +175,8 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
             err[i] = sub(V[i], B[i])
             m_fast[i] = add(mul(bf, m_fast[i]), mul(wf, err[i]))
             m_slow[i] = add(mul(bs, m_slow[i]), mul(ws, err[i]))
+            if state_bf16:  # variant: the estimates are stored in bfloat16
+                m_fast[i] = round_to_bfloat16(m_fast[i])
+                m_slow[i] = round_to_bfloat16(m_slow[i])
     return {"q1": q1, "scales1": s1, "S": S, "c": c, "V": V, "q2": q2,
             "scales2": s2, "B": B, "r": err, "out": B}

@@ -28,11 +28,11 @@ def _upload(raw, dtype, device):
 
 
 def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True, group=32,
-           sender_feedback=False):
+           sender_feedback=False, state_bf16=False):
     torch = _torch()
     import error_compensated_bit_echo_amd as E
     cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1], group=group,
-                            sender_feedback=sender_feedback)
+                            sender_feedback=sender_feedback, state_bf16=state_bf16)
     ws = torch.full((max(E.echo_workspace_bytes(cfg), 1),), 0xFF if poison else 0,
                     dtype=torch.uint8, device=device)
     return E.echo_init_state(cfg, ws)
@@ -52,8 +52,8 @@ def _fetch(state, out, direction, lo=0, hi=None):
         "scales1": v["scales1"][:, g0:g1].cpu().numpy(),
         "codes2": v["codes2"][lo // 2:hi // 2].cpu().numpy(),
         "scales2": v["scales2"][g0:g1].cpu().numpy(),
-        "m_fast": v["m_fast"][lo:hi].cpu().numpy(),
-        "m_slow": v["m_slow"][lo:hi].cpu().numpy(),
+        "m_fast": v["m_fast"][lo:hi].float().cpu().numpy(),  # bf16 state widens exactly
+        "m_slow": v["m_slow"][lo:hi].float().cpu().numpy(),
         "out": out[lo:hi].cpu().numpy(),
         "sender_err": None if v["sender_err"] is None else v["sender_err"][:, lo:hi].cpu().numpy(),
     }

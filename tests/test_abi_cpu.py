@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_config_struct_layout():
     # int32 P; (pad) int64 numel; int32 group; enum dtype; int32 compensate; float; float
-    assert ctypes.sizeof(B.EchoConfig) == 40
+    assert ctypes.sizeof(B.EchoConfig) == 48
+    assert B.EchoConfig.state_bf16.offset == 40
     assert B.EchoConfig.numel.offset == 8
     assert B.EchoConfig.beta_slow.offset == 32
     assert ctypes.sizeof(B.EchoViews) == 80
@@ -62,6 +63,9 @@ def test_workspace_bytes_formula():
         # sender feedback adds every rank's stage-1 error vector for both directions
         cfg = B.EchoConfig.make(P, N, dt, group=G, sender_feedback=True)
         assert _ws(cfg) == want + 2 * P * al(4 * N)
+        # bf16 state: four compensator vectors of 2N bytes instead of 4N
+        cfg = B.EchoConfig.make(P, N, dt, group=G, state_bf16=True)
+        assert _ws(cfg) == want - 4 * al(4 * N) + 4 * al(2 * N)
     assert _ws(B.EchoConfig.make(4, 0)) == 0
 
 
@@ -73,6 +77,7 @@ def test_workspace_bytes_formula():
     ("dtype", 7, B.ECHO_ERR_DTYPE), ("compensate", 2, B.ECHO_ERR_ARG),
     ("beta_fast", -0.5, B.ECHO_ERR_ARG), ("beta_slow", float("nan"), B.ECHO_ERR_ARG),
     ("beta_slow", 1.5, B.ECHO_ERR_ARG), ("sender_feedback", 2, B.ECHO_ERR_ARG),
+    ("state_bf16", 3, B.ECHO_ERR_ARG),
 ])
 def test_init_rejects_bad_config_without_touching_the_gpu(field, value, status):
     lib = B.load_library()

@@ -310,7 +310,7 @@ def _windows(N, n_win, width, seed):
 
 
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
-                  P=None, N=None, compensate=True, sender_feedback=False):
+                  P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
     value distribution and dtype)."""
@@ -319,7 +319,8 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     c = synth.CONFIGS[cfg_id]
     P = c["P"] if P is None else P
     N = synth.numel(cfg_id) if N is None else N
-    st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback)
+    st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback,
+                state_bf16=state_bf16)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     wins = _windows(N, n_win, width, cfg_id)
     so = {w: eo.OracleState(width) for w in wins}
@@ -332,7 +333,8 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
             E.echo_reduce(parts, out, st, d)
             for w in wins:
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
-                o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback)
+                o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
+                                 state_bf16=state_bf16)
                 g = _fetch(st, out, d, w, w + width)
                 assert _compare(g, o, so[w], d, compensate,
                                 f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}") == 0
@@ -436,3 +438,49 @@ def test_sender_feedback_stage_entry_points_equal_reduce(cuda):
 
 def test_sender_feedback_full_size(cuda):
     _windowed_run(cuda, 2, 4, (0,), sender_feedback=True)
+
+
+# ---------------------------------------------------------------------------
+# bf16 compensator state (a variant): every estimate update rounded to bf16
+# ---------------------------------------------------------------------------
+def test_bf16_state_tiny_config_every_call(cuda):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.CONFIGS[1]
+    P, N = c["P"], synth.numel(1)
+    st = _state(P, N, "f32", state_bf16=True)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(c["calls"]):
+        raw, vals = synth.host_partials(1, 0, t)
+        E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, state_bf16=True)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
+
+
+@pytest.mark.parametrize("P,dtype,group,sfb", [(2, "bf16", 32, False), (5, "f32", 32, False),
+                                               (8, "bf16", 64, False), (4, "bf16", 32, True),
+                                               (16, "bf16", 128, True)])
+def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = 2048 * 5 + group * 3
+    st = _state(P, N, dtype, group=group, sender_feedback=sfb, state_bf16=True)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    rng = np.random.default_rng(P * 100 + group)
+    for t in range(5):
+        for d in (0, 1):
+            if (t + d) % 2:
+                vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+                raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
+            else:
+                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+            E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, group=group, sender_feedback=sfb, state_bf16=True)
+            assert _compare(_fetch(st, out, d), o, so, d, True,
+                            f"G={group} P={P} sfb={sfb} call {t} dir {d}") == 0
+
+
+def test_bf16_state_full_size(cuda):
+    _windowed_run(cuda, 2, 6, (0,), state_bf16=True)

@@ -544,3 +544,39 @@ def test_sender_feedback_bounds_end_to_end_error():
     # a random walk without: sqrt(256/16) = 4 times larger at the end
     assert without[-16:].mean() > 2.5 * without[:16].mean()
     assert without[-1] > 3.0 * with_fb[-1]
+
+
+# ---------------------------------------------------------------------------
+# bf16 compensator state (a variant)
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_matches_exact_rounding():
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(F32)
+    x = x[np.isfinite(x) & (np.abs(x) < 3e38)]
+    # exact ties: the lower 16 bits are exactly half of a bf16 step
+    t = ((rng.integers(0, 2 ** 16, 2000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000).view(F32)
+    t = t[np.isfinite(t) & (np.abs(t) < 3e38)]
+    sub = (rng.integers(-2 ** 20, 2 ** 20, 2000) * 2.0 ** -149).astype(F32)  # subnormals
+    for v in (x, t, sub):
+        got = eo.round_to_bf16(v)
+        want = _as_f32([ex.round_to_bfloat16(Fraction(float(a))) for a in v])
+        want = np.where(want == 0, np.copysign(F32(0), v), want).astype(F32)  # IEEE: -0 for negatives
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+        # and every result is a bfloat16: the low 16 bits are zero
+        assert np.all((got.view(np.uint32) & 0xFFFF) == 0)
+
+
+@pytest.mark.parametrize("compensate", [True, False])
+def test_bf16_state_matches_exact_rationals(compensate):
+    P, N, T = 2, 64, 10
+    st = eo.OracleState(N)
+    mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
+    for t in range(T):
+        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        o = eo.echo_call(x, st, compensate=compensate, state_bf16=True)
+        e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, state_bf16=True)
+        for key in ("S", "V", "B", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+        assert np.array_equal(st.m_fast[0], _as_f32(mf))
+        assert np.array_equal(st.m_slow[0], _as_f32(ms))
