@@ -26,9 +26,11 @@ if ROOT not in sys.path:
 METRIC = "Echo reduce GB/s (bf16-equiv payload) + % HBM peak, 1 GB msg, P=8 emulated"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
 KERNEL_SOURCES = ["error_compensated_bit_echo_amd/csrc/echo_kernels.hip",
+                  "error_compensated_bit_echo_amd/csrc/echo_gemm.hip",
                   "error_compensated_bit_echo_amd/csrc/echo_internal.h",
                   "error_compensated_bit_echo_amd/csrc/echo_div7.h",
-                  "error_compensated_bit_echo_amd/csrc/echo_quant.h"]
+                  "error_compensated_bit_echo_amd/csrc/echo_quant.h",
+                  "error_compensated_bit_echo_amd/csrc/echo_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 COPY_FLOATS = 1 << 29  # 2 GiB of fp32 for the copy kernel
 KERNEL_KEYS = {"stage1": "echo_quant_pack_k", "owner": "echo_owner_k", "decode": "echo_unpack_k"}
@@ -129,7 +131,8 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
 # ---------------------------------------------------------------------------
 # the other workloads: latency, effective bandwidth and accuracy reports
 # ---------------------------------------------------------------------------
-CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2, "variants": 2}
+CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2, "variants": 2,
+              "gemm": 0}
 CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
 
 
@@ -401,6 +404,59 @@ def sender_report(E, synth, torch, dev) -> dict:
             "rms_err_of_accumulated_output_vs_exact_by_calls": err,
             "us_per_call_graph_32_calls": lat}
 
+def gemm_report(E, torch, dev) -> dict:
+    """Stage 1 fused into the producing product (bf16 MFMA, fp32 accumulation):
+    per shape, the fused kernel against the same product written out followed
+    by the stage-1 kernel, and against torch's library product (hipBLASLt)
+    followed by the stage-1 kernel.  TFLOP/s against the MI355X dense bf16 peak."""
+    res = []
+    for P, M, K, H in ((4, 2048, 3072, 4096), (8, 128, 3072, 4096)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        A = [torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16) for _ in range(P)]
+        W = [(torch.randn(H, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16) for _ in range(P)]
+        Wt = [w.t().contiguous() for w in W]  # [K, H] for a plain (not transposed) library product
+        out = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+        st = E.echo_init_state(E.EchoConfig.make(P, M * H, "bf16"), device=dev)
+        flat = [o.view(-1) for o in out]
+
+        def fused():
+            E.echo_gemm_stage1(A, W, st)
+
+        def ours_unfused():
+            E.echo_gemm_bf16(A, W, out)
+            E.echo_stage1(flat, st)
+
+        def library_unfused():
+            for r in range(P):
+                torch.matmul(A[r], Wt[r], out=out[r])
+            E.echo_stage1(flat, st)
+
+        def product_only():
+            E.echo_gemm_bf16(A, W, out)
+
+        t = {}
+        for name, fn in (("fused", fused), ("ours_then_stage1", ours_unfused),
+                         ("library_then_stage1", library_unfused), ("ours_product_only", product_only)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            t[name] = a.elapsed_time(b) * 1e3 / reps
+        flop = 2.0 * P * M * K * H
+        res.append({"P": P, "M": M, "K": K, "H": H, "us": {k: round(v, 2) for k, v in t.items()},
+                    "TFLOPs": {k: round(flop / (v * 1e-6) / 1e12, 1) for k, v in t.items()},
+                    "bf16_peak_TFLOPs": 2500.0,
+                    "partial_bytes_not_written_or_read": 2 * 2 * P * M * H})
+    return {"config": "gemm", "shapes": res}
+
+
 def cpu_baseline(parts, n_sample: int) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
     the first ``n_sample`` elements of each of the benchmark's own partials."""
@@ -477,7 +533,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.config:
-        names = ["tiny", "prefill", "decode", "training", "tp", "groups", "variants"] if args.config == "all" \
+        names = ["tiny", "prefill", "decode", "training", "tp", "groups", "variants", "gemm"] \
+            if args.config == "all" \
             else [args.config]
         for name in names:
             print(f"# config {name}", file=sys.stderr, flush=True)
@@ -489,6 +546,8 @@ def main():
                 continue
             if name == "decode":
                 rep = decode_report(E, synth, torch, dev)
+            elif name == "gemm":
+                rep = gemm_report(E, torch, dev)
             elif name == "variants":
                 rep = sender_report(E, synth, torch, dev)
             elif name == "tp":

@@ -100,6 +100,9 @@ def load_library():
         "echo_reduce": (i32, [ctypes.POINTER(vp), vp, vp, i32, vp]),
         "echo_stage1": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
         "echo_owner": (i32, [vp, i32, vp]),
+        "echo_gemm_stage1": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int64, ctypes.c_int64, vp, vp]),
+        "echo_gemm_bf16": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]),
         "echo_decode": (i32, [vp, vp, vp]),
         "echo_reset": (i32, [vp, i32, vp]),
         "echo_destroy_state": (None, [vp]),
@@ -224,6 +227,40 @@ def echo_stage1(partials: Sequence, state: EchoState, direction: int = ECHO_FWD,
     arr = _partials_array(partials, state)
     _check(load_library().echo_stage1(arr, state.handle, int(direction),
                                       _stream_handle(stream, state.device)), "echo_stage1")
+
+
+def _bf16_matrices(mats, rows, cols, what):
+    import torch
+    for t in mats:
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (rows, cols) or not t.is_contiguous():
+            raise EchoError(ECHO_ERR_ARG, f"{what} must be contiguous bfloat16 [{rows}, {cols}]")
+    return (ctypes.c_void_p * len(mats))(*[t.data_ptr() for t in mats])
+
+
+def echo_gemm_stage1(A: Sequence, W: Sequence, state: EchoState, stream=None):
+    """Stage 1 fused into the producing product: the payload of bf16(A_r @ W_r.T)
+    for every rank (A_r [M, K], W_r [H, K] bfloat16, M*H == N)."""
+    P = state.cfg.P
+    if len(A) != P or len(W) != P:
+        raise EchoError(ECHO_ERR_ARG, f"expected {P} A and {P} W matrices")
+    M, K = A[0].shape
+    H = W[0].shape[0]
+    a = _bf16_matrices(A, M, K, "A")
+    w = _bf16_matrices(W, H, K, "W")
+    _check(load_library().echo_gemm_stage1(a, w, M, K, state.handle,
+                                           _stream_handle(stream, state.device)), "echo_gemm_stage1")
+
+
+def echo_gemm_bf16(A: Sequence, W: Sequence, out: Sequence, stream=None):
+    """out[r] = bf16(A_r @ W_r.T), the product echo_gemm_stage1 quantizes."""
+    P = len(A)
+    M, K = A[0].shape
+    H = W[0].shape[0]
+    a = _bf16_matrices(A, M, K, "A")
+    w = _bf16_matrices(W, H, K, "W")
+    o = _bf16_matrices(out, M, H, "out")
+    _check(load_library().echo_gemm_bf16(a, w, o, P, M, K, H, _stream_handle(stream, A[0].device)),
+           "echo_gemm_bf16")
 
 
 def echo_owner(state: EchoState, direction: int = ECHO_FWD, stream=None):

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libecho.so")
-SOURCES = ["echo_kernels.hip", "echo_api.hip"]
-HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h"]
+SOURCES = ["echo_kernels.hip", "echo_gemm.hip", "echo_api.hip"]
+HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h", "echo_device.h"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every multiply and add is its own IEEE operation (the

@@ -228,6 +228,74 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
   return run_stage1(partials, st, static_cast<int>(dir), static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+bool gemm_shape_ok(int64_t M, int64_t K, int64_t H) {
+  return M > 0 && K > 0 && H > 0 && M % echo::kGemmTileM == 0 && H % echo::kGemmTileN == 0 &&
+         K % echo::kGemmTileK == 0 && M / echo::kGemmTileM <= 65535 && H / echo::kGemmTileN <= INT32_MAX;
+}
+
+echo_status gemm_inputs(const void* const* A, const void* const* W, int P, echo::GemmArgs* a) {
+  if (A == nullptr || W == nullptr) return ECHO_ERR_ARG;
+  for (int r = 0; r < P; ++r)
+    if (A[r] == nullptr || W[r] == nullptr || !aligned16(A[r]) || !aligned16(W[r])) return ECHO_ERR_ARG;
+  for (int r = 0; r < echo::kMaxRanks; ++r) {
+    a->A[r] = static_cast<const uint16_t*>(A[r < P ? r : 0]);
+    a->W[r] = static_cast<const uint16_t*>(W[r < P ? r : 0]);
+  }
+  return ECHO_OK;
+}
+
+}  // namespace
+
+echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
+                             echo_state* st, echo_stream_t stream) {
+  echo_status e = check_state(st);
+  if (e != ECHO_OK) return e;
+  if (st->cfg.dtype != ECHO_BF16) return ECHO_ERR_DTYPE;
+  if (st->cfg.sender_feedback) return ECHO_ERR_ARG;
+  if (st->cfg.group != 32 || M <= 0 || st->cfg.numel % M != 0) return ECHO_ERR_SHAPE;
+  const int64_t H = st->cfg.numel / M;
+  if (!gemm_shape_ok(M, K, H)) return ECHO_ERR_SHAPE;
+  echo::GemmArgs a{};
+  if ((e = gemm_inputs(A, W, st->cfg.P, &a)) != ECHO_OK) return e;
+  a.codes = st->codes1;
+  a.scales = st->scales1;
+  a.codes_stride_words = st->codes1_stride_bytes / 4;
+  a.scales_stride = st->scales1_stride_bytes / 4;
+  a.M = M;
+  a.K = K;
+  a.H = H;
+  return echo::launch_gemm(a, st->cfg.P, true, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? ECHO_OK
+             : ECHO_ERR_HIP;
+}
+
+echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* const* out, int32_t P,
+                           int64_t M, int64_t K, int64_t H, echo_stream_t stream) {
+  if (P < 1 || P > ECHO_MAX_RANKS || !gemm_shape_ok(M, K, H)) return ECHO_ERR_SHAPE;
+  if (out == nullptr) return ECHO_ERR_ARG;
+  echo::GemmArgs a{};
+  echo_status e = gemm_inputs(A, W, P, &a);
+  if (e != ECHO_OK) return e;
+  const size_t nout = static_cast<size_t>(M) * static_cast<size_t>(H) * 2;
+  const size_t na = static_cast<size_t>(M) * static_cast<size_t>(K) * 2;
+  const size_t nw = static_cast<size_t>(H) * static_cast<size_t>(K) * 2;
+  for (int r = 0; r < P; ++r) {
+    if (out[r] == nullptr || !aligned16(out[r])) return ECHO_ERR_ARG;
+    for (int q = 0; q < P; ++q)
+      if (overlaps(out[r], nout, A[q], na) || overlaps(out[r], nout, W[q], nw) ||
+          (q != r && overlaps(out[r], nout, out[q], nout)))
+        return ECHO_ERR_ARG;
+  }
+  for (int r = 0; r < echo::kMaxRanks; ++r) a.out[r] = static_cast<uint16_t*>(out[r < P ? r : 0]);
+  a.M = M;
+  a.K = K;
+  a.H = H;
+  return echo::launch_gemm(a, P, false, static_cast<hipStream_t>(stream)) == hipSuccess ? ECHO_OK
+                                                                                      : ECHO_ERR_HIP;
+}
+
 echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;

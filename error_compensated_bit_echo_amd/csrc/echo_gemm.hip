@@ -1,0 +1,156 @@
+// The producing product with stage 1 in its epilogue (gfx950, MFMA).
+//
+// In a tensor-parallel layer each rank's partial sum is the output of a
+// row-parallel product, partial_r = A_r * W_r^T (A_r: [M, K] activations,
+// W_r: [H, K] weights, bf16, fp32 accumulation), which the rank then rounds
+// to bf16 and sends to the all-reduce.  Here the stage-1 quantization (rit.work
+// blog post "echo-4-bit-gpu-communication", «Как Echo возвращает ошибку в
+// следующие вызовы»: ranks send their segments as 4-bit integers) runs in the
+// product's epilogue: the bf16 tile goes to LDS, not to HBM, and the same
+// per-lane quantizer as the stage-1 kernel turns it into the rank's payload.
+// The payload is therefore bit-identical to stage 1 applied to the unfused
+// bf16 partial, which the same kernel writes when asked to.
+//
+// Tiling: a block computes a 128 x 128 tile of one rank's [M, H] partial with 4
+// wavefronts, each a 64 x 64 sub-tile of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.
+// K advances 64 at a time through LDS (rows padded to 72 bf16), the next K
+// slab being fetched into registers while the current one is multiplied.
+// Lane layout of the 32x32x16 bf16 product (checked on the device): lane l
+// supplies A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8, and
+// accumulator v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+#pragma clang fp contract(off)
+
+#include "echo_device.h"
+
+namespace echo {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTileM = 128, kTileN = 128, kTileK = 64;
+constexpr int kLdsK = kTileK + 8;    // bf16 per LDS row of the A and W slabs
+constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the output tile
+constexpr int kGemmThreads = 256;
+static_assert(2 * kTileM * kLdsK >= kTileM * kLdsN, "the output tile reuses the slabs' LDS");
+
+template <bool FUSED>
+__global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kTileM * kLdsK];
+  const int r = blockIdx.z;
+  const uint16_t* A = a.A[0];
+  const uint16_t* W = a.W[0];
+#pragma unroll
+  for (int i = 1; i < kMaxRanks; ++i)
+    if (r == i) {
+      A = a.A[i];
+      W = a.W[i];
+    }
+  const int64_t K = a.K, H = a.H;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kTileM;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTileN;
+  const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
+  uint16_t* As = lds;
+  uint16_t* Ws = lds + kTileM * kLdsK;
+
+  // global -> registers: 4 chunks of 8 bf16 per thread and slab; chunk i is
+  // row (t / 8) + 32 i, columns 8 (t % 8) .. +8 of the K slab
+  u32x4 ra[4], rw[4];
+  const int grow = t >> 3, gcol = (t & 7) * 8;
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(A + (m0 + grow + 32 * i) * K + k0 + gcol);
+      rw[i] = *reinterpret_cast<const u32x4*>(W + (n0 + grow + 32 * i) * K + k0 + gcol);
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  fetch(0);
+  for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
+    __syncthreads();  // the previous slab has been read
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(As + (grow + 32 * i) * kLdsK + gcol) = ra[i];
+      *reinterpret_cast<u32x4*>(Ws + (grow + 32 * i) * kLdsK + gcol) = rw[i];
+    }
+    __syncthreads();
+    if (k0 + kTileK < K) fetch(k0 + kTileK);
+#pragma unroll
+    for (int ks = 0; ks < kTileK / 16; ++ks) {
+      const int kc = 16 * ks + 8 * (lane >> 5);
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(As + (64 * wm + 32 * i + (lane & 31)) * kLdsK + kc);
+        bf[i] = *reinterpret_cast<const bf16x8*>(Ws + (64 * wn + 32 * i + (lane & 31)) * kLdsK + kc);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+
+  // the bf16 output tile, row-major in LDS
+  uint16_t* Cs = lds;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int col = 64 * wn + 32 * j + (lane & 31);
+        Cs[row * kLdsN + col] = bf16_rne(acc[i][j][v]);
+      }
+  __syncthreads();
+
+  // 2048 chunks of 8: thread t takes chunks t + 256 u; a row has 16 chunks, so
+  // the 4 lanes of a quad hold one 32-element group
+#pragma unroll
+  for (int u = 0; u < kTileM * kTileN / 8 / kGemmThreads; ++u) {
+    const int chunk = t + kGemmThreads * u;
+    const int row = chunk >> 4, cc = (chunk & 15) * 8;
+    Raw<true> raw;
+    raw.q[0] = *reinterpret_cast<const u32x4*>(Cs + row * kLdsN + cc);
+    const int64_t e = (m0 + row) * H + n0 + cc;  // element index in the rank's [M, H] partial
+    if constexpr (!FUSED) {
+      uint16_t* out = a.out[0];
+#pragma unroll
+      for (int i = 1; i < kMaxRanks; ++i)
+        if (r == i) out = a.out[i];
+      *reinterpret_cast<u32x4*>(out + e) = raw.q[0];
+    } else {
+      float v[8];
+      widen<true>(raw, v);
+      const float s = echo_div7(group_max<4>(absmax8(v)));
+      float kf[8];
+      const uint32_t w = quantize8(v, s, kf);
+      a.codes[static_cast<int64_t>(r) * a.codes_stride_words + (e >> 3)] = w;
+      if ((t & 3) == 0) a.scales[static_cast<int64_t>(r) * a.scales_stride + (e >> 5)] = s;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / kTileM),
+                  static_cast<unsigned>(P));
+  if (fused)
+    hipLaunchKernelGGL(echo_gemm_k<true>, grid, dim3(kGemmThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(echo_gemm_k<false>, grid, dim3(kGemmThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace echo

@@ -44,4 +44,21 @@ hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
                          int64_t numel, int group, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
+// The producing product partial_r = bf16(A_r * W_r^T) of every rank (A_r [M, K],
+// W_r [H, K], bf16 row-major; M % 128 == 0, H % 128 == 0, K % 64 == 0), either
+// written out (out[r], [M, H] bf16) or quantized in the epilogue into the
+// stage-1 payload (codes / scales as in Stage1Args, group 32).
+struct GemmArgs {
+  const uint16_t* A[kMaxRanks];
+  const uint16_t* W[kMaxRanks];
+  uint16_t* out[kMaxRanks];
+  uint32_t* codes;
+  float* scales;
+  int64_t codes_stride_words;
+  int64_t scales_stride;
+  int64_t M, K, H;
+};
+constexpr int kGemmTileM = 128, kGemmTileN = 128, kGemmTileK = 64;
+hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s);
+
 }  // namespace echo

@@ -127,6 +127,29 @@ echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
 echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir dir,
                         echo_stream_t stream);
 
+/* Stage 1 fused into the producing product (the step before the all-reduce in
+ * a tensor-parallel layer: each rank's partial is the output of its slice of a
+ * row-parallel product).  For every rank r the partial is
+ * bf16(A_r * W_r^T), A_r [M, K] and W_r [H, K] bfloat16 row-major (W_r's rows
+ * are output features), accumulated in fp32 on the matrix cores and rounded to
+ * nearest-even; N = M*H.  Each rank's stage-1 payload is written into the
+ * state exactly as echo_stage1 would write it from that bf16 partial, which
+ * itself never reaches memory.  Follow with echo_owner and echo_decode.
+ * A, W: host arrays of P device pointers, 16-byte aligned, read-only.
+ * Requires a bf16 state with group 32 and no sender feedback, M and H
+ * multiples of 128 (M/128 <= 65535), K a multiple of 64.  Errors: ECHO_ERR_ARG
+ * (null or misaligned pointer, sender feedback on), ECHO_ERR_SHAPE (sizes,
+ * M*H != N, group != 32), ECHO_ERR_DTYPE (state not bf16), ECHO_ERR_STATE,
+ * ECHO_ERR_HIP. */
+echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
+                             echo_state* st, echo_stream_t stream);
+
+/* The same product written out, for comparison: out[r] = bf16(A_r * W_r^T),
+ * [M, H] bfloat16 row-major, for r < P (1..16).  Same shape rules; out[r] must
+ * not overlap A or W.  Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_HIP. */
+echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* const* out, int32_t P,
+                           int64_t M, int64_t K, int64_t H, echo_stream_t stream);
+
 /* Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
  * apply the correction of direction `dir`, re-quantize into the broadcast
  * payload and update the compensator of `dir`. */

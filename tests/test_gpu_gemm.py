@@ -1,0 +1,119 @@
+"""Stage 1 fused into the producing product (MFMA bf16, fp32 accumulation).
+
+* The product itself: bf16(A_r @ W_r^T) against the exact product of the same
+  bf16 inputs (float64 on the host): within half a bf16 ulp plus the fp32
+  accumulation bound, and equal to the rounded exact product almost everywhere.
+* The fused payload: bit-identical to stage 1 of the unfused bf16 partial, by
+  the oracle and by the library's own stage-1 kernel.
+* Whole calls: fused stage 1, owner and decode against the oracle fed the
+  unfused partials, call after call.
+"""
+import numpy as np
+import pytest
+
+from oracle import echo_oracle as eo
+from parity_helpers import _compare, _fetch, _state, _torch
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 128, 64, 128), (2, 256, 512, 384), (3, 384, 1024, 256), (8, 128, 3072, 512)]
+
+
+def _inputs(P, M, K, H, seed, dev, w=None):
+    torch = _torch()
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    A = [torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16) for _ in range(P)]
+    if w is None:
+        w = [(torch.randn(H, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16) for _ in range(P)]
+    return A, w
+
+
+def _unfused(A, W):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    M, H = A[0].shape[0], W[0].shape[0]
+    out = [torch.empty(M, H, dtype=torch.bfloat16, device=A[0].device) for _ in A]
+    E.echo_gemm_bf16(A, W, out)
+    return out
+
+
+@pytest.mark.parametrize("P,M,K,H", SHAPES)
+def test_product_matches_exact_reference(cuda, P, M, K, H):
+    A, W = _inputs(P, M, K, H, 1, cuda)
+    out = _unfused(A, W)
+    for r in range(P):
+        a = A[r].float().cpu().numpy().astype(np.float64)
+        w = W[r].float().cpu().numpy().astype(np.float64)
+        exact = a @ w.T
+        mag = np.abs(a) @ np.abs(w).T
+        got = out[r].float().cpu().numpy().astype(np.float64)
+        bound = np.abs(exact) * 2.0 ** -8 + mag * K * 2.0 ** -24
+        assert np.all(np.abs(got - exact) <= bound), f"rank {r}: {np.max(np.abs(got - exact) - bound)}"
+        rounded = exact.astype(np.float32)
+        rounded_bf16 = (rounded.view(np.uint32) + 0x7FFF + ((rounded.view(np.uint32) >> 16) & 1)) >> 16
+        same = np.mean(got.astype(np.float32).view(np.uint32) >> 16 == rounded_bf16)
+        assert same > 0.97, f"rank {r}: only {same:.4f} equal to the rounded exact product"
+
+
+@pytest.mark.parametrize("P,M,K,H", SHAPES)
+def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    A, W = _inputs(P, M, K, H, 2, cuda)
+    N = M * H
+    fused = _state(P, N, "bf16")
+    E.echo_gemm_stage1(A, W, fused)
+    parts = [p.reshape(-1) for p in _unfused(A, W)]
+    ref = _state(P, N, "bf16")
+    E.echo_stage1(parts, ref)
+    vf, vr = E.echo_debug_views(fused), E.echo_debug_views(ref)
+    torch.cuda.synchronize()
+    assert torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
+    for r in range(P):
+        q, s = eo.quantize_groups(parts[r].float().cpu().numpy())
+        assert np.array_equal(vf["codes1"][r].cpu().numpy(), eo.pack_nibbles(q))
+        assert np.array_equal(vf["scales1"][r].cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+@pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024)])
+def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = M * H
+    st = _state(P, N, "bf16")
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    _, W = _inputs(P, M, K, H, 3, cuda)
+    for t in range(4):
+        A, _ = _inputs(P, M, K, H, 10 + t, cuda, w=W)
+        E.echo_gemm_stage1(A, W, st)
+        E.echo_owner(st, E.ECHO_FWD)
+        E.echo_decode(out, st)
+        host = np.stack([p.reshape(-1).float().cpu().numpy() for p in _unfused(A, W)])
+        o = eo.echo_call(host, so, eo.FWD)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
+
+
+def test_argument_errors(cuda):
+    import ctypes
+    import error_compensated_bit_echo_amd as E
+    from error_compensated_bit_echo_amd import binding as B
+    torch = _torch()
+    P, M, K, H = 2, 128, 64, 128
+    A, W = _inputs(P, M, K, H, 4, cuda)
+    lib = E.load_library()
+    arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = _state(P, M * H, "f32")
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_DTYPE
+    st = _state(P, M * H, "bf16", sender_feedback=True)
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    st = _state(P, M * H, "bf16", group=64)
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_SHAPE
+    st = _state(P, M * H, "bf16")
+    assert lib.echo_gemm_stage1(arr(A), arr(W), 64, K, st.handle, s) == B.ECHO_ERR_SHAPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, 96, st.handle, s) == B.ECHO_ERR_SHAPE
+    bad = (ctypes.c_void_p * P)(A[0].data_ptr(), A[1].data_ptr() + 2)
+    assert lib.echo_gemm_stage1(bad, arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    torch.cuda.synchronize()
