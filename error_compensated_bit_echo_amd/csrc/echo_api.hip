@@ -259,6 +259,12 @@ echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t
   if (!gemm_shape_ok(M, K, H)) return ECHO_ERR_SHAPE;
   echo::GemmArgs a{};
   if ((e = gemm_inputs(A, W, st->cfg.P, &a)) != ECHO_OK) return e;
+  // the inputs are read while the payload is written: they must not overlap the workspace
+  const size_t na = static_cast<size_t>(M) * static_cast<size_t>(K) * 2;
+  const size_t nw = static_cast<size_t>(H) * static_cast<size_t>(K) * 2;
+  for (int r = 0; r < st->cfg.P; ++r)
+    if (overlaps(A[r], na, st->ws, st->ws_bytes) || overlaps(W[r], nw, st->ws, st->ws_bytes))
+      return ECHO_ERR_ARG;
   a.codes = st->codes1;
   a.scales = st->scales1;
   a.codes_stride_words = st->codes1_stride_bytes / 4;

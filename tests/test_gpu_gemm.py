@@ -116,4 +116,8 @@ def test_argument_errors(cuda):
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, 96, st.handle, s) == B.ECHO_ERR_SHAPE
     bad = (ctypes.c_void_p * P)(A[0].data_ptr(), A[1].data_ptr() + 2)
     assert lib.echo_gemm_stage1(bad, arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    # an input inside the workspace the payload is written to (rejected before any launch)
+    inside = (ctypes.c_void_p * P)(A[0].data_ptr(), st.workspace.data_ptr())
+    assert lib.echo_gemm_stage1(inside, arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(arr(A), inside, M, K, st.handle, s) == B.ECHO_ERR_ARG
     torch.cuda.synchronize()
