@@ -254,6 +254,8 @@ def echo_gemm_stage1(A: Sequence, W: Sequence, state: EchoState, stream=None):
 def echo_gemm_bf16(A: Sequence, W: Sequence, out: Sequence, stream=None):
     """out[r] = bf16(A_r @ W_r.T), the product echo_gemm_stage1 quantizes."""
     P = len(A)
+    if P < 1 or len(W) != P or len(out) != P:
+        raise EchoError(ECHO_ERR_ARG, "A, W and out must hold the same number (>= 1) of matrices")
     M, K = A[0].shape
     H = W[0].shape[0]
     a = _bf16_matrices(A, M, K, "A")
