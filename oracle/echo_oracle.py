@@ -208,7 +208,8 @@ class OracleState:
 def echo_call(partials, state: OracleState | None, direction: int = FWD,
               compensate: bool = True, beta_fast: float = 0.5,
               beta_slow: float = 0.95, group: int = GROUP,
-              sender_feedback: bool = False, state_bf16: bool = False):
+              sender_feedback: bool = False, state_bf16: bool = False,
+              out_bf16: bool = False, own_exact: bool = False):
     """One Echo all-reduce of ``partials`` ([P, N] float32).
 
     Advances ``state`` (direction ``direction``) in place when compensating and
@@ -223,6 +224,19 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     ``state_bf16`` is another variant: the two estimates are stored in
     bfloat16, i.e. every update m <- fl(fl(beta*m) + fl(omega*r)) is rounded
     to the nearest bfloat16 before it is kept.
+
+    ``out_bf16`` (a variant): what the ranks receive is the broadcast value
+    rounded once more, to the nearest bfloat16, and the owner measures its
+    error against that delivered value, r = fl(V - bf16(B)), so the
+    compensator also returns the output rounding in later calls.  (The
+    difference is exact except when V and bf16(B) straddle a power of two.)
+
+    ``own_exact`` (a variant): the owner of a segment holds its own partial
+    and adds it as it is instead of through Q: rank j quantizes and sends
+    every segment but its own (its codes and scales there are left zero here,
+    and with sender feedback its error there is neither used nor changed), and
+    the owner's rank-order sum takes x_j (x_j + e_j with sender feedback) in
+    place of fl(q_j * s_j) on segment j.
     """
     x = np.ascontiguousarray(partials, dtype=F32)
     if x.ndim != 2:
@@ -233,6 +247,7 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     if not np.all(np.isfinite(x)):
         raise ValueError("partials must be finite")
     n_g = N // group
+    segs = owner_segments(n_g, P)
 
     # 1. stage 1 on every rank (with sender feedback: on x + e, then the new e)
     q1 = np.empty((P, N), np.int8)
@@ -246,10 +261,17 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         xs = x
     for r in range(P):
         q, s = quantize_groups(xs[r], group)
+        sent = np.ones(N, bool)
+        if own_exact:  # rank r keeps its own segment: nothing of it is quantized
+            g0, g1 = segs[r]
+            q[g0:g1] = 0
+            s[g0:g1] = 0
+            sent[g0 * group:g1 * group] = False
         q1[r] = q.reshape(-1)
         s1[r] = s
         if sender_feedback:
-            e1[r] = xs[r] - dequantize_groups(q, s, group).reshape(-1)
+            e_new = xs[r] - dequantize_groups(q, s, group).reshape(-1)
+            e1[r] = np.where(sent, e_new, e1[r])
 
     # 2.-6. each owner works on its own segment of every rank's payload
     S = np.empty(N, F32)
@@ -264,14 +286,17 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         wf, ws = F32(1) - bf, F32(1) - bs
         mf = state.m_fast[direction]
         ms = state.m_slow[direction]
-    for g0, g1 in owner_segments(n_g, P):
+    for j, (g0, g1) in enumerate(segs):
         if g1 <= g0:
             continue
         e0, e1 = g0 * group, g1 * group
         # 3. dequantize every rank's contribution and add in rank order
         acc = None
         for r in range(P):
-            d = dequantize_groups(q1[r, e0:e1], s1[r, g0:g1], group).reshape(-1)
+            if own_exact and r == j:
+                d = xs[r, e0:e1]
+            else:
+                d = dequantize_groups(q1[r, e0:e1], s1[r, g0:g1], group).reshape(-1)
             acc = d if acc is None else acc + d
         S[e0:e1] = acc
         # 4. correction from the two smoothed error estimates
@@ -288,6 +313,8 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         s2[g0:g1] = ss
         bb = dequantize_groups(qq, ss, group).reshape(-1)
         B[e0:e1] = bb
+        if out_bf16:  # the value the ranks will hold
+            bb = round_to_bf16(bb)
         # 6. error of this rounding, then the two estimates
         if compensate:
             rr = vv - bb
@@ -301,6 +328,8 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     # 7. every rank decodes the broadcast payload
     codes2 = pack_nibbles(q2)
     out = dequantize_groups(unpack_nibbles(codes2), s2, group).reshape(-1)
+    if out_bf16:
+        out = round_to_bf16(out)
     return {
         "codes1": np.stack([pack_nibbles(q1[r]) for r in range(P)]) if P else np.zeros((0, N // 2), np.uint8),
         "scales1": s1,

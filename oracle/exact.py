@@ -131,32 +131,53 @@ def dequantize(codes, scales, group=GROUP):
 
 
 def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
-              beta_slow=0.95, group=GROUP, sender_err=None, state_bf16=False):
+              beta_slow=0.95, group=GROUP, sender_err=None, state_bf16=False,
+              out_bf16=False, own_exact=False):
     """One call on exact binary32 values.
 
     ``partials`` is a list of P lists of Fractions (each a binary32 value);
     ``m_fast``/``m_slow`` are lists of Fractions, updated in place when
     compensating; ``sender_err``, if given, is the P ranks' stage-1 error
-    lists (the sender-feedback variant), updated in place.  Returns a dict of
-    lists of Fractions / ints.
+    lists (the sender-feedback variant), updated in place.  ``out_bf16``: the
+    ranks receive bf16(B) and the error is measured against it.
+    ``own_exact``: the owner of group g (g // ceil(n_groups / P)) adds its own
+    input exactly instead of through Q; its own groups are not quantized (codes
+    and scales reported as 0) and its sender error there is left alone.
+    Returns a dict of lists of Fractions / ints.
     """
     P = len(partials)
     N = len(partials[0])
-    q1, s1 = [], []
+    n_groups = N // group
+    per = (n_groups + P - 1) // P   # groups per owner, the last owner's share shorter
+
+    def owner(i):
+        return (i // group) // per
+
+    q1, s1, xin = [], [], []
     for r in range(P):
         # sender feedback (a variant): quantize x + e and keep the new error
         x = partials[r] if sender_err is None else [add(a, b) for a, b in zip(partials[r], sender_err[r])]
+        xin.append(x)
         q, s = quantize(x, group)
+        if own_exact:
+            for i in range(N):
+                if owner(i) == r:
+                    q[i] = 0
+                    s[i // group] = Fraction(0)
         q1.append(q)
         s1.append(s)
         if sender_err is not None:
             deq = dequantize(q, s, group)
-            sender_err[r][:] = [sub(a, b) for a, b in zip(x, deq)]
+            sender_err[r][:] = [e if (own_exact and owner(i) == r) else sub(a, b)
+                                for i, (a, b, e) in enumerate(zip(x, deq, sender_err[r]))]
     S = []
     for i in range(N):
         acc = None
         for r in range(P):
-            d = mul(Fraction(q1[r][i]), s1[r][i // group])
+            if own_exact and owner(i) == r:
+                d = xin[r][i]
+            else:
+                d = mul(Fraction(q1[r][i]), s1[r][i // group])
             acc = d if acc is None else add(acc, d)
         S.append(acc)
     if compensate:
@@ -167,16 +188,17 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
         V = list(S)
     q2, s2 = quantize(V, group)
     B = dequantize(q2, s2, group)
+    out = [round_to_bfloat16(b) for b in B] if out_bf16 else B
     err = [Fraction(0)] * N
     if compensate:
         bf, bs = f32(beta_fast), f32(beta_slow)
         wf, ws = sub(Fraction(1), bf), sub(Fraction(1), bs)
         for i in range(N):
-            err[i] = sub(V[i], B[i])
+            err[i] = sub(V[i], out[i])
             m_fast[i] = add(mul(bf, m_fast[i]), mul(wf, err[i]))
             m_slow[i] = add(mul(bs, m_slow[i]), mul(ws, err[i]))
             if state_bf16:  # variant: the estimates are stored in bfloat16
                 m_fast[i] = round_to_bfloat16(m_fast[i])
                 m_slow[i] = round_to_bfloat16(m_slow[i])
     return {"q1": q1, "scales1": s1, "S": S, "c": c, "V": V, "q2": q2,
-            "scales2": s2, "B": B, "r": err, "out": B}
+            "scales2": s2, "B": B, "r": err, "out": out}

@@ -51,6 +51,19 @@ MUTANTS = {
         "e1[r] = xs[r] - dequantize_groups(q, s, group).reshape(-1)",
         "e1[r] = x[r] - dequantize_groups(q, s, group).reshape(-1)"),
     "sender error added with the wrong sign": ("xs = x + e1", "xs = x - e1"),
+    "bf16 output: error measured against B, not the delivered value": (
+        "        if out_bf16:  # the value the ranks will hold\n            bb = round_to_bf16(bb)\n", ""),
+    "own partial quantized anyway": (
+        "d = xs[r, e0:e1]",
+        "d = dequantize_groups(*quantize_groups(xs[r, e0:e1], group), group).reshape(-1)"),
+    "own partial added first": (
+        "for r in range(P):\n            if own_exact and r == j:",
+        "for r in ([j] + [k for k in range(P) if k != j] if own_exact else range(P)):\n"
+        "            if own_exact and r == j:"),
+    "own segment's sender error overwritten": (
+        "e1[r] = np.where(sent, e_new, e1[r])", "e1[r] = e_new"),
+    "own segment taken from the next rank": (
+        "if own_exact and r == j:", "if own_exact and r == (j + 1) % P:"),
     "estimate biased by a tiny constant": (
         "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bf * mf[e0:e1] + wf * rr + F32(1e-30)"),
 }

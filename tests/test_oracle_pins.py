@@ -580,3 +580,141 @@ def test_bf16_state_matches_exact_rationals(compensate):
             assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
         assert np.array_equal(st.m_fast[0], _as_f32(mf))
         assert np.array_equal(st.m_slow[0], _as_f32(ms))
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 output (a variant): exact rationals, closed form of the compensator
+# with the delivered value, lossless special case
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_bf16_output_matches_exact_rationals(compensate):
+    P, N, T = 3, 64, 10
+    st = eo.OracleState(N)
+    mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
+    for t in range(T):
+        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        o = eo.echo_call(x, st, compensate=compensate, out_bf16=True)
+        e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, out_bf16=True)
+        for key in ("S", "V", "B", "r", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+        assert np.array_equal(st.m_fast[0], _as_f32(mf))
+        assert np.array_equal(st.m_slow[0], _as_f32(ms))
+
+
+def test_bf16_output_compensator_closed_form():
+    """Unrolling m_f and m_s gives, for the accumulated error of what the ranks
+    receive, D_T = sum_t (out_t - S_t) = -sum_{t<T} k_{T-1-t} r_t with
+    k_n = (0.5^n + 0.95^n) / 2, provided r is measured against the delivered
+    bfloat16 value (an error measured against B would leave the output
+    roundings, about 2^-9 relative, out of D's closed form)."""
+    P, N, T = 2, 2048, 100
+    st = eo.OracleState(N)
+    outs = []
+    for t in range(T):
+        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        outs.append(eo.echo_call(x, st, out_bf16=True))
+    assert all(np.all((o["out"].view(np.uint32) & 0xFFFF) == 0) for o in outs)
+    r = np.stack([o["r"].astype(F64) for o in outs])
+    D = np.cumsum(np.stack([o["out"].astype(F64) - o["S"].astype(F64) for o in outs]), 0)
+    bf, bs = F64(F32(0.5)), F64(F32(0.95))
+    k = 0.5 * (bf ** np.arange(T) + bs ** np.arange(T))
+    for Tq in (1, 2, 10, 50, 100):
+        pred = -np.sum(k[:Tq, None] * r[Tq - 1::-1], axis=0)
+        assert np.max(np.abs(D[Tq - 1] - pred)) < 1e-4 * np.max(np.abs(r))
+
+
+def test_bf16_output_lossless_partials():
+    """Partials on both int4 grids: without compensation the only rounding left
+    is the bfloat16 one, so out = bf16(sum) exactly."""
+    rng = np.random.default_rng(23)
+    x, exact_sum = _lossless_partials(4, 16, rng)
+    x = x * F32(1.0 + 2.0 ** -12)  # exact, and the sums are no longer bfloat16 values
+    exact_sum = exact_sum * (1.0 + 2.0 ** -12)
+    o = eo.echo_call(x, None, compensate=False, out_bf16=True)
+    want = _as_f32([ex.round_to_bfloat16(Fraction(float(v))) for v in exact_sum])
+    assert np.array_equal(o["out"], want)
+    assert not np.array_equal(o["out"].astype(F64), exact_sum)
+
+
+# ---------------------------------------------------------------------------
+# owner adds its own partial exactly (a variant): exact rationals, a hand-worked
+# value that fixes the rank order, special cases, error statistics
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate,sfb", [(True, False), (False, False), (True, True)])
+def test_own_exact_matches_exact_rationals(compensate, sfb):
+    P, N, T = 3, 160, 8   # 5 groups: owners hold 2, 2 and 1 of them
+    st = eo.OracleState(N)
+    mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
+    se = [[Fraction(0)] * N for _ in range(P)] if sfb else None
+    for t in range(T):
+        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        o = eo.echo_call(x, st, compensate=compensate, sender_feedback=sfb, own_exact=True)
+        e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate,
+                         sender_err=se, own_exact=True)
+        for r in range(P):
+            assert np.array_equal(o["q1"][r], np.array(e["q1"][r], np.int8)), (t, r)
+            assert np.array_equal(o["scales1"][r], _as_f32(e["scales1"][r]))
+            if sfb:
+                assert np.array_equal(st.sender_err[0][r], _as_f32(se[r])), (t, r)
+        for key in ("S", "V", "B", "r", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+        if compensate:
+            assert np.array_equal(st.m_fast[0], _as_f32(mf))
+
+
+def test_own_exact_rank_order_golden():
+    """P = 3, one group per owner; element 64 lies in rank 2's segment.
+    Rank 0 sends [1, 0, ...]: s = fl(1/7), code 7, fl(7 * s) = 1.
+    Rank 1 sends [3, 7, 0, ...] * 2^-25: s = 2^-25, codes 3 and 7, so 1.5 * 2^-24.
+    Rank 2 holds 2^-24 itself.
+    In rank order, 1 + 1.5 * 2^-24 rounds up to 1 + 2^-23, and adding 2^-24 is
+    then a tie that goes to the even 1 + 2^-22.  Adding the owner's value first
+    would give 1 + 2^-23 instead."""
+    x = np.zeros((3, 96), F32)
+    x[0, 64] = 1.0
+    x[1, 64], x[1, 65] = 3 * 2.0 ** -25, 7 * 2.0 ** -25
+    x[2, 64] = 2.0 ** -24
+    o = eo.echo_call(x, None, compensate=False, own_exact=True)
+    assert o["S"][64] == F32(1 + 2.0 ** -22)
+    assert o["S"][65] == F32(7 * 2.0 ** -25)
+    assert o["scales1"][1][2] == F32(2.0 ** -25)
+    assert o["scales1"][2][2] == 0 and not np.any(o["q1"][2][64:96])
+
+
+def test_own_exact_single_contributor():
+    """Only rank j non-zero: on j's own segment the sum is x_j itself, on the
+    other segments it is x_j through one stage-1 rounding."""
+    P, N = 4, 32 * 8
+    _, base = synth.host_partials(1, 0, 5, P=1, n=N)
+    segs = eo.owner_segments(N // 32, P)
+    for j in range(P):
+        x = np.zeros((P, N), F32)
+        x[j] = base[0]
+        o = eo.echo_call(x, None, compensate=False, own_exact=True)
+        q, s = eo.quantize_groups(base[0])
+        once = eo.dequantize_groups(q, s).reshape(-1)
+        for k, (g0, g1) in enumerate(segs):
+            sl = slice(g0 * 32, g1 * 32)
+            want = base[0][sl] if k == j else once[sl]
+            assert np.array_equal(o["S"][sl], want), (j, k)
+
+
+def test_own_exact_single_rank_is_one_rounding():
+    _, x = synth.host_partials(1, 0, 2, P=1, n=4096)
+    o = eo.echo_call(x, None, compensate=False, own_exact=True)
+    q, s = eo.quantize_groups(x[0])
+    assert np.array_equal(o["S"], x[0])
+    assert np.array_equal(o["out"], eo.dequantize_groups(q, s).reshape(-1))
+
+
+def test_own_exact_removes_one_rank_of_stage1_error():
+    """Stage-1 errors of independent ranks add in variance; keeping the owner's
+    share exact leaves P - 1 of the P, so the owner-sum error shrinks by about
+    sqrt((P - 1) / P)."""
+    for P in (2, 4):
+        _, x = synth.host_partials(1, 0, 9, P=P, n=1 << 14)
+        exact = eo.plain_sum(x)
+        e_all = eo.echo_call(x, None, compensate=False)["S"].astype(F64) - exact
+        e_own = eo.echo_call(x, None, compensate=False, own_exact=True)["S"].astype(F64) - exact
+        ratio = np.sqrt(np.mean(e_own ** 2) / np.mean(e_all ** 2))
+        assert abs(ratio - np.sqrt((P - 1) / P)) < 0.05, (P, ratio)
