@@ -37,25 +37,31 @@ KERNEL_KEYS = {"stage1": "echo_quant_pack_k", "owner": "echo_owner_k", "decode":
 
 
 def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool, group: int = 32,
-                      sender_feedback: bool = False, state_bf16: bool = False) -> dict:
+                      sender_feedback: bool = False, state_bf16: bool = False,
+                      out_bf16: bool = False, own_exact: bool = False) -> dict:
     """Bytes each stage must move per call (reads + writes of HBM)."""
     pl = 0.5 + 4.0 / group                     # payload bytes per element: codes + scales
-    k1 = P * N * (b_in + pl)                   # read partials; write codes + scales
+    sent = (P - 1) * N if own_exact else P * N  # rank elements that pass stage 1
+    k1 = sent * (b_in + pl)                    # read partials; write codes + scales
     if sender_feedback:
-        k1 += P * N * 8.0                      # read and write every rank's stage-1 error
-    k2 = N * (pl * P + pl)                     # read P payload segments; write broadcast payload
+        k1 += sent * 8.0                       # read and write those elements' stage-1 errors
+    if own_exact:                              # P - 1 payload segments and the owner's own partial
+        k2 = N * (pl * (P - 1) + b_in + pl)
+    else:                                      # read P payload segments; write broadcast payload
+        k2 = N * (pl * P + pl)
     if compensate:
         k2 += (8.0 if state_bf16 else 16.0) * N  # read and write m_fast, m_slow
-    k3 = N * (pl + 4.0)                        # read broadcast payload; write fp32 out
+    k3 = N * (pl + (2.0 if out_bf16 else 4.0))  # read broadcast payload; write the output
     return {"stage1": k1, "owner": k2, "decode": k3}
 
 
 def workload_tag(comp: bool, group: int = 32, sender_feedback: bool = False,
-                 state_bf16: bool = False) -> str:
+                 state_bf16: bool = False, out_bf16: bool = False, own_exact: bool = False) -> str:
     tag = f"1GiB-P8-bf16-{'comp' if comp else 'nocomp'}"
     if group != 32:
         tag += f"-g{group}"
-    return tag + ("-sfb" if sender_feedback else "") + ("-sb16" if state_bf16 else "")
+    return tag + ("-sfb" if sender_feedback else "") + ("-sb16" if state_bf16 else "") + \
+        ("-obf16" if out_bf16 else "") + ("-own" if own_exact else "")
 
 
 def kernel_source_hash() -> str:
@@ -366,28 +372,40 @@ def sender_report(E, synth, torch, dev) -> dict:
     """The variants on the prefill workload (P = 4, bf16 [2048, 4096], 72 calls,
     fresh partials per call): error of the residual stream h_T = sum of all
     outputs against the exact stream, by call count T, for compensation on/off,
-    sender feedback on/off and fp32 or bf16 state; per-call latency of each."""
+    sender feedback on/off, fp32 or bf16 state, fp32 or bf16 output and the
+    owner adding its own partial exactly or not; per-call latency of each."""
     c = synth.CONFIGS[2]
     P, N, calls = c["P"], synth.numel(2), c["calls"]
-    # (compensate, sender feedback, bf16 state)
-    combos = [(True, False, False), (False, False, False), (True, True, False), (False, True, False),
-              (True, False, True), (True, True, True)]
+    # (compensate, sender feedback, bf16 state, bf16 output, own partial exact)
+    combos = [(True, False, False, False, False), (False, False, False, False, False),
+              (True, True, False, False, False), (False, True, False, False, False),
+              (True, False, True, False, False), (True, True, True, False, False),
+              (True, False, False, True, False), (False, False, False, True, False),
+              (True, False, False, False, True), (True, True, False, False, True)]
 
     def name(k):
         return (f"comp_{'on' if k[0] else 'off'}_sfb_{'on' if k[1] else 'off'}"
-                f"_state_{'bf16' if k[2] else 'fp32'}")
+                f"_state_{'bf16' if k[2] else 'fp32'}_out_{'bf16' if k[3] else 'fp32'}"
+                + ("_own_exact" if k[4] else ""))
 
-    modes = {k: E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=k[0], sender_feedback=k[1],
-                                                   state_bf16=k[2]), device=dev) for k in combos}
-    out = torch.empty(N, dtype=torch.float32, device=dev)
+    def make(k):
+        return E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=k[0], sender_feedback=k[1],
+                                                   state_bf16=k[2], out_bf16=k[3], own_exact=k[4]),
+                                 device=dev)
+
+    def out_for(k):
+        return torch.empty(N, dtype=torch.bfloat16 if k[3] else torch.float32, device=dev)
+
+    modes = {k: make(k) for k in combos}
+    outs = {k: out_for(k) for k in combos}
     h = {k: torch.zeros(N, dtype=torch.float64, device=dev) for k in modes}
     hx = torch.zeros(N, dtype=torch.float64, device=dev)
     err = {name(k): {} for k in modes}
     for t in range(calls):
         parts = synth.device_partials(2, 0, t, device=dev)
         for k, st in modes.items():
-            E.echo_reduce(parts, out, st, E.ECHO_FWD)
-            h[k] += out.double()
+            E.echo_reduce(parts, outs[k], st, E.ECHO_FWD)
+            h[k] += outs[k].double()
         for p in parts:
             hx += p.double()
         T = t + 1
@@ -396,13 +414,12 @@ def sender_report(E, synth, torch, dev) -> dict:
                 err[name(k)][str(T)] = (h[k] - hx).pow(2).mean().sqrt().item()
     lat = {}
     for k in combos:
-        gst = E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=k[0], sender_feedback=k[1],
-                                                 state_bf16=k[2]), device=dev)
-        g, _ = _graph_us(E, torch, parts, torch.empty_like(out), gst, E.ECHO_FWD, 20)
+        g, _ = _graph_us(E, torch, parts, out_for(k), make(k), E.ECHO_FWD, 20)
         lat[name(k)] = round(_pct(g, 0.5), 2)
     return {"config": "variants", "P": P, "numel_per_rank": N, "calls": calls,
             "rms_err_of_accumulated_output_vs_exact_by_calls": err,
             "us_per_call_graph_32_calls": lat}
+
 
 def gemm_report(E, torch, dev) -> dict:
     """Stage 1 fused into the producing product (bf16 MFMA, fp32 accumulation):
@@ -457,9 +474,10 @@ def gemm_report(E, torch, dev) -> dict:
     return {"config": "gemm", "shapes": res}
 
 
-def cpu_baseline(parts, n_sample: int) -> dict:
+def cpu_baseline(parts, n_sample: int, **variant) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
-    the first ``n_sample`` elements of each of the benchmark's own partials."""
+    the first ``n_sample`` elements of each of the benchmark's own partials
+    (``variant``: the oracle's switches of the benchmarked configuration)."""
     import numpy as np
     from oracle import echo_oracle as eo
 
@@ -467,7 +485,7 @@ def cpu_baseline(parts, n_sample: int) -> dict:
     vals = np.stack([p[:n_sample].float().cpu().numpy() for p in parts])
     st = eo.OracleState(n_sample)
     t0 = time.perf_counter()
-    eo.echo_call(vals, st, eo.FWD)
+    eo.echo_call(vals, st, eo.FWD, **variant)
     dt = time.perf_counter() - t0
     del vals
     return {
@@ -476,7 +494,8 @@ def cpu_baseline(parts, n_sample: int) -> dict:
         "cores": 1,
         "kind": "oracle",
         "sample": f"one call, P={P} x the first {n_sample} elements of each rank's partial "
-                  f"({n_sample / 536870912:.4g} of the 1 GiB message), compensation on, fresh state; {dt:.2f} s; numpy "
+                  f"({n_sample / 536870912:.4g} of the 1 GiB message), "
+                  f"{', '.join(f'{k}={v}' for k, v in variant.items()) or 'compensation on'}, fresh state; {dt:.2f} s; numpy "
                   f"elementwise ops on one core ({platform.processor() or platform.machine()}, "
                   f"os.cpu_count()={os.cpu_count()})",
     }
@@ -494,6 +513,10 @@ def main():
                     help="variant: every rank feeds its stage-1 rounding error into its next call")
     ap.add_argument("--bf16-state", action="store_true",
                     help="variant: the compensator's two estimates stored in bfloat16")
+    ap.add_argument("--out-bf16", action="store_true",
+                    help="variant: bfloat16 output, the owner's error measured against it")
+    ap.add_argument("--own-exact", action="store_true",
+                    help="variant: each owner adds its own partial exactly (not quantized)")
     ap.add_argument("--cpu-sample", type=int, default=1 << 25,
                     help="elements per rank in the CPU oracle's timed sample")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle leg")
@@ -509,7 +532,7 @@ def main():
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters,
                               workload=workload_tag(not args.no_comp, args.group, args.sender_feedback,
-                                                    args.bf16_state),
+                                                    args.bf16_state, args.out_bf16, args.own_exact),
                               command=args.counter_command)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         with open(TRAFFIC_FILE, "w") as f:
@@ -564,11 +587,11 @@ def main():
     print(f"# generating {P} x {N} bf16 partials on the device", file=sys.stderr, flush=True)
     parts = synth.device_partials(cfg_id, 0, 0, device=dev)
     G = args.group
-    SFB, SB16 = args.sender_feedback, args.bf16_state
+    SFB, SB16, OBF, OWN = args.sender_feedback, args.bf16_state, args.out_bf16, args.own_exact
     cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp, group=G, sender_feedback=SFB,
-                            state_bf16=SB16)
+                            state_bf16=SB16, out_bf16=OBF, own_exact=OWN)
     st = E.echo_init_state(cfg, device=dev)
-    out = torch.empty(N, dtype=torch.float32, device=dev)
+    out = torch.empty(N, dtype=torch.bfloat16 if OBF else torch.float32, device=dev)
     torch.cuda.synchronize()
 
     # warm-up, then a fresh state for the timed calls
@@ -587,7 +610,7 @@ def main():
         e[0].record()
         E.echo_stage1(parts, st)
         e[1].record()
-        E.echo_owner(st, E.ECHO_FWD)
+        E.echo_owner(st, E.ECHO_FWD, partials=parts if OWN else None)
         e[2].record()
         E.echo_decode(out, st)
         e[3].record()
@@ -603,7 +626,7 @@ def main():
     print(f"# timed {K} calls: {ms_step:.3f} ms/step wall, {gpu_ms_step:.3f} ms/step events",
           file=sys.stderr, flush=True)
 
-    alg = algorithmic_bytes(P, N, 2, comp, G, SFB, SB16)
+    alg = algorithmic_bytes(P, N, 2, comp, G, SFB, SB16, OBF, OWN)
     total_alg = sum(alg.values())
     kernels = {}
     for k, ms in kern_ms.items():
@@ -612,7 +635,7 @@ def main():
                       "frac": round(alg[k] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     dom = max(kern_ms, key=kern_ms.get)
     achieved = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
-    workload = workload_tag(comp, G, SFB, SB16)
+    workload = workload_tag(comp, G, SFB, SB16, OBF, OWN)
     traffic = measured_traffic(dom, workload)
 
     # a plain streaming copy kernel of 2 GiB (torch's elementwise x*1, read 2 GiB,
@@ -651,9 +674,10 @@ def main():
             "workload": "1 GiB bf16 message per rank (536,870,912 elements), P=8 emulated ranks, "
                         f"group {G}, absmax/7 fp32 scales, compensation " + ("on" if comp else "off") +
                         (", sender feedback" if SFB else "") + (", bf16 state" if SB16 else "") +
+                        (", bf16 output" if OBF else "") + (", owners add their own partials exactly" if OWN else "") +
                         ", same partials every call, reset -> warm-up -> reset -> timed calls",
             "P": P, "numel_per_rank": N, "input_dtype": "bf16", "wire": "int4 codes + fp32 group scales",
-            "output_dtype": "f32", "group": G,
+            "output_dtype": "bf16" if OBF else "f32", "group": G,
         },
         "roofline": {
             "bound": "hbm",
@@ -673,7 +697,10 @@ def main():
     }
     if not args.skip_cpu:
         print(f"# CPU oracle sample: P={P} x {args.cpu_sample}", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample)
+        variant = {k: v for k, v in (("compensate", comp), ("group", G), ("sender_feedback", SFB),
+                                     ("state_bf16", SB16), ("out_bf16", OBF), ("own_exact", OWN))
+                   if v != {"compensate": True, "group": 32}.get(k, False)}
+        line["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample, **variant)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -40,17 +40,21 @@ class EchoConfig(ctypes.Structure):
         ("beta_slow", ctypes.c_float),
         ("sender_feedback", ctypes.c_int32),
         ("state_bf16", ctypes.c_int32),
+        ("out_bf16", ctypes.c_int32),
+        ("own_exact", ctypes.c_int32),
     ]
 
     @classmethod
     def make(cls, P: int, numel: int, dtype: str = "bf16", compensate: bool = True,
              beta_fast: float = 0.5, beta_slow: float = 0.95, group: int = ECHO_GROUP,
-             sender_feedback: bool = False, state_bf16: bool = False) -> "EchoConfig":
+             sender_feedback: bool = False, state_bf16: bool = False, out_bf16: bool = False,
+             own_exact: bool = False) -> "EchoConfig":
         d = {"f32": ECHO_F32, "float32": ECHO_F32, "bf16": ECHO_BF16, "bfloat16": ECHO_BF16}
         if dtype not in d:
             raise EchoError(ECHO_ERR_DTYPE, f"dtype {dtype!r}")
         return cls(P, numel, group, d[dtype], int(bool(compensate)), beta_fast, beta_slow,
-                   int(bool(sender_feedback)), int(bool(state_bf16)))
+                   int(bool(sender_feedback)), int(bool(state_bf16)), int(bool(out_bf16)),
+                   int(bool(own_exact)))
 
 
 class EchoViews(ctypes.Structure):
@@ -99,7 +103,7 @@ def load_library():
         "echo_init_state": (i32, [cfgp, vp, sz, vp, ctypes.POINTER(vp)]),
         "echo_reduce": (i32, [ctypes.POINTER(vp), vp, vp, i32, vp]),
         "echo_stage1": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
-        "echo_owner": (i32, [vp, i32, vp]),
+        "echo_owner": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
         "echo_gemm_stage1": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int64, ctypes.c_int64, vp, vp]),
         "echo_gemm_bf16": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]),
@@ -208,14 +212,16 @@ def _partials_array(partials: Sequence, state: EchoState):
 
 def _out_ptr(out, state: EchoState):
     import torch
-    if out.dtype != torch.float32 or out.numel() != state.cfg.numel or not out.is_contiguous() \
+    want = torch.bfloat16 if state.cfg.out_bf16 else torch.float32
+    if out.dtype != want or out.numel() != state.cfg.numel or not out.is_contiguous() \
             or out.device != state.device:
-        raise EchoError(ECHO_ERR_ARG, "out must be a contiguous float32 tensor of N elements on the state's device")
+        raise EchoError(ECHO_ERR_ARG, f"out must be a contiguous {want} tensor of N elements on the state's device")
     return ctypes.c_void_p(out.data_ptr())
 
 
 def echo_reduce(partials: Sequence, out, state: EchoState, direction: int = ECHO_FWD, stream=None):
-    """One Echo all-reduce of ``partials`` (P device tensors) into ``out`` (fp32)."""
+    """One Echo all-reduce of ``partials`` (P device tensors) into ``out`` (fp32, or
+    bfloat16 with the out_bf16 variant)."""
     arr = _partials_array(partials, state)
     optr = _out_ptr(out, state)
     _check(load_library().echo_reduce(arr, optr, state.handle, int(direction),
@@ -265,8 +271,10 @@ def echo_gemm_bf16(A: Sequence, W: Sequence, out: Sequence, stream=None):
            "echo_gemm_bf16")
 
 
-def echo_owner(state: EchoState, direction: int = ECHO_FWD, stream=None):
-    _check(load_library().echo_owner(state.handle, int(direction),
+def echo_owner(state: EchoState, direction: int = ECHO_FWD, stream=None, partials=None):
+    """Owner stage.  ``partials`` (the ones echo_stage1 received) are needed with own_exact."""
+    arr = _partials_array(partials, state) if partials is not None else None
+    _check(load_library().echo_owner(arr, state.handle, int(direction),
                                       _stream_handle(stream, state.device)), "echo_owner")
 
 

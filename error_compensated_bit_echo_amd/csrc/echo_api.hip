@@ -71,6 +71,8 @@ echo_status check_cfg(const echo_config* c) {
   if (!(c->beta_slow >= 0.0f && c->beta_slow <= 1.0f)) return ECHO_ERR_ARG;
   if (c->sender_feedback != 0 && c->sender_feedback != 1) return ECHO_ERR_ARG;
   if (c->state_bf16 != 0 && c->state_bf16 != 1) return ECHO_ERR_ARG;
+  if (c->out_bf16 != 0 && c->out_bf16 != 1) return ECHO_ERR_ARG;
+  if (c->own_exact != 0 && c->own_exact != 1) return ECHO_ERR_ARG;
   return ECHO_OK;
 }
 
@@ -101,9 +103,9 @@ echo_status check_partials(const void* const* partials, const echo_state* st) {
   return ECHO_OK;
 }
 
-echo_status check_out(const float* out, const echo_state* st, const void* const* partials) {
+echo_status check_out(const void* out, const echo_state* st, const void* const* partials) {
   if (out == nullptr || !aligned16(out)) return ECHO_ERR_ARG;
-  const size_t no = static_cast<size_t>(st->cfg.numel) * 4;
+  const size_t no = static_cast<size_t>(st->cfg.numel) * (st->cfg.out_bf16 ? 2 : 4);
   if (overlaps(out, no, st->ws, st->ws_bytes)) return ECHO_ERR_ARG;
   if (partials != nullptr) {
     const size_t nb = static_cast<size_t>(st->cfg.numel) * elem_bytes(st->cfg);
@@ -111,6 +113,12 @@ echo_status check_out(const float* out, const echo_state* st, const void* const*
       if (overlaps(out, no, partials[r], nb)) return ECHO_ERR_ARG;
   }
   return ECHO_OK;
+}
+
+// Chunks (8 elements) per owner segment: the ceil(n_groups / P) groups each owner takes.
+int64_t segment_chunks(const echo_config& c) {
+  const int64_t n_groups = c.numel / c.group;
+  return (n_groups + c.P - 1) / c.P * (c.group / echo::kElemsPerLane);
 }
 
 echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hipStream_t s) {
@@ -123,12 +131,14 @@ echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hip
   a.nchunk = st->cfg.numel / echo::kElemsPerLane;
   a.err = st->sender_err[dir];
   a.err_stride = st->err_floats;
+  a.own_chunks = st->cfg.own_exact ? segment_chunks(st->cfg) : 0;
   return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
 
-echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
+// partials: read only with own_exact (the owners' own shares)
+echo_status run_owner(const void* const* partials, echo_state* st, int dir, hipStream_t s) {
   echo::OwnerArgs a{};
   for (int r = 0; r < echo::kMaxRanks; ++r) {
     const int rr = r < st->cfg.P ? r : 0;  // unused slots repeat rank 0
@@ -146,15 +156,21 @@ echo_status run_owner(echo_state* st, int dir, hipStream_t s) {
   a.omega_fast = 1.0f - st->cfg.beta_fast;  // fl(1 - beta)
   a.beta_slow = st->cfg.beta_slow;
   a.omega_slow = 1.0f - st->cfg.beta_slow;
+  a.out_bf16 = st->cfg.out_bf16;
+  if (st->cfg.own_exact) {
+    a.own_bf16 = st->cfg.dtype == ECHO_BF16;
+    a.own_chunks = segment_chunks(st->cfg);
+    for (int r = 0; r < echo::kMaxRanks; ++r) a.own_src[r] = partials[r < st->cfg.P ? r : 0];
+  }
   return echo::launch_owner(a, st->cfg.P, st->cfg.compensate != 0, st->cfg.group,
-                            st->cfg.state_bf16 != 0, s) == hipSuccess
+                            st->cfg.state_bf16 != 0, st->cfg.own_exact != 0, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
 
-echo_status run_decode(float* out, const echo_state* st, hipStream_t s) {
-  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, st->cfg.group, s) ==
-                 hipSuccess
+echo_status run_decode(void* out, const echo_state* st, hipStream_t s) {
+  return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, st->cfg.group,
+                             st->cfg.out_bf16 != 0, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
@@ -253,7 +269,7 @@ echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
   if (st->cfg.dtype != ECHO_BF16) return ECHO_ERR_DTYPE;
-  if (st->cfg.sender_feedback) return ECHO_ERR_ARG;
+  if (st->cfg.sender_feedback || st->cfg.own_exact) return ECHO_ERR_ARG;
   if (st->cfg.group != 32 || M <= 0 || st->cfg.numel % M != 0) return ECHO_ERR_SHAPE;
   const int64_t H = st->cfg.numel / M;
   if (!gemm_shape_ok(M, K, H)) return ECHO_ERR_SHAPE;
@@ -302,15 +318,17 @@ echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* con
                                                                                       : ECHO_ERR_HIP;
 }
 
-echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream) {
+echo_status echo_owner(const void* const* partials, echo_state* st, echo_dir dir,
+                       echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
   if (dir != ECHO_FWD && dir != ECHO_BWD) return ECHO_ERR_ARG;
   if (st->cfg.numel == 0) return ECHO_OK;
-  return run_owner(st, static_cast<int>(dir), static_cast<hipStream_t>(stream));
+  if (st->cfg.own_exact && (e = check_partials(partials, st)) != ECHO_OK) return e;
+  return run_owner(partials, st, static_cast<int>(dir), static_cast<hipStream_t>(stream));
 }
 
-echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream) {
+echo_status echo_decode(void* out, const echo_state* st, echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
   if (st->cfg.numel == 0) return ECHO_OK;
@@ -318,7 +336,7 @@ echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream) 
   return run_decode(out, st, static_cast<hipStream_t>(stream));
 }
 
-echo_status echo_reduce(const void* const* partials, float* out, echo_state* st, echo_dir dir,
+echo_status echo_reduce(const void* const* partials, void* out, echo_state* st, echo_dir dir,
                         echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
@@ -328,7 +346,7 @@ echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
   if ((e = check_out(out, st, partials)) != ECHO_OK) return e;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if ((e = run_stage1(partials, st, static_cast<int>(dir), s)) != ECHO_OK) return e;
-  if ((e = run_owner(st, static_cast<int>(dir), s)) != ECHO_OK) return e;
+  if ((e = run_owner(partials, st, static_cast<int>(dir), s)) != ECHO_OK) return e;
   return run_decode(out, st, s);
 }
 

@@ -21,6 +21,8 @@ struct Stage1Args {
   int64_t nchunk;              // N / 8
   float* err;                  // sender feedback: rank r's stage-1 error at err + r * err_stride
   int64_t err_stride;          // floats between ranks (err == nullptr: no sender feedback)
+  int64_t own_chunks;          // own_exact: chunks per owner segment, rank r skips chunks
+                               // [r * own_chunks, (r + 1) * own_chunks); 0: nothing skipped
 };
 
 // Owner stage: sum, correct, re-quantize, update the compensator.
@@ -33,15 +35,22 @@ struct OwnerArgs {
   float* m_slow;
   int64_t nchunk;
   float beta_fast, omega_fast, beta_slow, omega_slow;
+  int32_t out_bf16;              // error measured against bf16(B), the delivered value
+  int32_t own_bf16;              // own_exact: the partials are bfloat16 (else fp32)
+  int64_t own_chunks;            // own_exact: chunks per owner segment (owner of chunk c
+                                 // is min(c / own_chunks, P - 1)); 0 when off
+  const void* own_src[kMaxRanks];  // own_exact: the rank partials
 };
 
 // group: 32, 64 or 128 elements per scale
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s);
-// state_bf16: m_fast / m_slow hold bfloat16 (the variant), else fp32
+// state_bf16: m_fast / m_slow hold bfloat16 (the variant), else fp32;
+// own_exact: a.own_src / a.own_chunks are set
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
-                        hipStream_t s);
-hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out,
-                         int64_t numel, int group, hipStream_t s);
+                        bool own_exact, hipStream_t s);
+// out: N fp32, or N bfloat16 when out_bf16
+hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out,
+                         int64_t numel, int group, bool out_bf16, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
 // The producing product partial_r = bf16(A_r * W_r^T) of every rank (A_r [M, K],

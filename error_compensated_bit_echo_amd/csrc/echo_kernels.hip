@@ -37,15 +37,20 @@ namespace {
 // grid = (ceil(nchunk / (256*U)), P); a block covers 256*U chunks of one rank,
 // chunk c0 + u*256 for lane c0.
 // ---------------------------------------------------------------------------
+// Chunks in [skip_lo, skip_hi) are neither read nor written (the rank's own
+// segment when the owner adds its partial exactly); the whole-tile path is only
+// taken by tiles that do not meet that range.
 template <bool BF16, int U, int POL, int LPG, bool SFB, bool FULL>
 __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, float* scales,
-                                            float* err, int64_t c0, int64_t nchunk) {
+                                            float* err, int64_t c0, int64_t nchunk,
+                                            int64_t skip_lo, int64_t skip_hi) {
   Raw<BF16> raw[U];
   f32x4 ev[SFB ? U : 1][2];  // sender feedback: the rank's stage-1 error of these elements
+  auto live = [&](int64_t c) { return FULL || (c < nchunk && (c < skip_lo || c >= skip_hi)); };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
-    if (FULL || c < nchunk) {
+    if (live(c)) {
       raw[u] = load_raw<BF16, (POL & kNtIn) != 0>(src, c);
       if constexpr (SFB) {
         ev[u][0] = reinterpret_cast<const f32x4*>(err)[2 * c];
@@ -69,7 +74,7 @@ __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, fl
     const float s = echo_div7(group_max<LPG>(absmax8(v)));
     float kf[8];
     const uint32_t w = quantize8(v, s, kf);
-    if (FULL || c < nchunk) {
+    if (live(c)) {
       st<(POL & kNtOut) != 0>(w, codes + c);
       if ((threadIdx.x & (LPG - 1)) == 0) scales[c >> log2i(LPG)] = s;
       if constexpr (SFB) {
@@ -94,11 +99,15 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
   float* scales = a.scales + static_cast<int64_t>(r) * a.scales_stride;
   float* err = SFB ? a.err + static_cast<int64_t>(r) * a.err_stride : nullptr;
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
+  const int64_t ce = cb + kBlock * U;
+  const int64_t skip_lo = a.own_chunks * r, skip_hi = skip_lo + a.own_chunks;
+  if (cb >= skip_lo && ce <= skip_hi) return;  // the whole tile is the rank's own segment
   const int64_t c0 = cb + threadIdx.x;
-  if (cb + kBlock * U <= a.nchunk)
-    stage1_tile<BF16, U, POL, LPG, SFB, true>(src, codes, scales, err, c0, a.nchunk);
+  if (ce <= a.nchunk && (ce <= skip_lo || cb >= skip_hi))
+    stage1_tile<BF16, U, POL, LPG, SFB, true>(src, codes, scales, err, c0, a.nchunk, 0, 0);
   else
-    stage1_tile<BF16, U, POL, LPG, SFB, false>(src, codes, scales, err, c0, a.nchunk);
+    stage1_tile<BF16, U, POL, LPG, SFB, false>(src, codes, scales, err, c0, a.nchunk, skip_lo,
+                                               skip_hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -106,19 +115,47 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
 // order, correction, stage-2 quantization, error and both estimates.
 // grid = ceil(nchunk / 256); one lane per chunk.
 // ---------------------------------------------------------------------------
-template <int P, bool COMP, int POL, int LPG, bool SB16, bool FULL>
+// OWN: the owner of the chunk adds its own partial exactly (the chunk's
+// owner is the number of segment starts r * own_chunks, r = 1..P-1, at or
+// below c); its payload slot, which stage 1 left unwritten, is not read.
+template <int P, bool COMP, int POL, int LPG, bool SB16, bool OWN, bool FULL>
 __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
   const bool ok = FULL || c < a.nchunk;
   const int64_t g = c >> log2i(LPG);
 
+  int owner = -1;
+  const void* own = a.own_src[0];
+  if constexpr (OWN) {
+    owner = 0;
+#pragma unroll
+    for (int r = 1; r < P; ++r) owner += c >= a.own_chunks * r ? 1 : 0;
+#pragma unroll
+    for (int r = 1; r < P; ++r) own = owner == r ? a.own_src[r] : own;
+  }
+
   uint32_t w[P];
   float s[P];
   f32x4 mf4[2], ms4[2];
+  u32x4 xo[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};  // OWN: the owner's raw chunk
   if (ok) {
 #pragma unroll
     for (int r = 0; r < P; ++r) {
-      w[r] = ld<(POL & kNtIn) != 0>(a.codes1[r] + c);
-      s[r] = a.scales1[r][g];
+      if (!OWN || r != owner) {
+        w[r] = ld<(POL & kNtIn) != 0>(a.codes1[r] + c);
+        s[r] = a.scales1[r][g];
+      } else {
+        w[r] = 0;
+        s[r] = 0.0f;
+      }
+    }
+    if constexpr (OWN) {
+      const u32x4* p = static_cast<const u32x4*>(own);
+      if (a.own_bf16) {
+        xo[0] = p[c];
+      } else {
+        xo[0] = p[2 * c];
+        xo[1] = p[2 * c + 1];
+      }
     }
     if constexpr (COMP) {
       constexpr bool nt = (POL & kNtStateLd) != 0;
@@ -155,6 +192,23 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
 
   float d[P][8];
   dequant_ranks<P>(w, s, d);
+  if constexpr (OWN) {
+    float x[8];
+    if (a.own_bf16) {
+      Raw<true> rb;
+      rb.q[0] = xo[0];
+      widen<true>(rb, x);
+    } else {
+      Raw<false> rf;
+      rf.q[0] = xo[0];
+      rf.q[1] = xo[1];
+      widen<false>(rf, x);
+    }
+#pragma unroll
+    for (int r = 0; r < P; ++r)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) d[r][k] = r == owner ? x[k] : d[r][k];
+  }
   float mf[8], ms[8], V[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -181,7 +235,9 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float B = kf[j] * s2;
-        const float e = V[j] - B;
+        // with a bfloat16 output the error is that of the value delivered
+        const float Bo = a.out_bf16 ? __uint_as_float(bf16_rne_carry(B) & 0xFFFF0000u) : B;
+        const float e = V[j] - Bo;
         mf[j] = a.beta_fast * mf[j] + a.omega_fast * e;
         ms[j] = a.beta_slow * ms[j] + a.omega_slow * e;
       }
@@ -201,13 +257,13 @@ __device__ __forceinline__ void owner_tile(const OwnerArgs& a, int64_t c) {
   }
 }
 
-template <int P, bool COMP, int POL, int LPG, bool SB16>
+template <int P, bool COMP, int POL, int LPG, bool SB16, bool OWN>
 __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * kBlock;
   if (cb + kBlock <= a.nchunk)
-    owner_tile<P, COMP, POL, LPG, SB16, true>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, SB16, OWN, true>(a, cb + threadIdx.x);
   else
-    owner_tile<P, COMP, POL, LPG, SB16, false>(a, cb + threadIdx.x);
+    owner_tile<P, COMP, POL, LPG, SB16, OWN, false>(a, cb + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -247,6 +303,49 @@ __device__ __forceinline__ void decode_tile(const uint32_t* codes, const float* 
   }
 }
 
+// bfloat16 output: a lane owns a whole code word (8 elements, 16 bytes of
+// output), so a wavefront store is again 1 KiB of contiguous output.
+// grid = ceil(nchunk / (256*U)), chunk c0 + u*256 for lane c0.
+template <int U, int POL, int LPG, bool FULL>
+__device__ __forceinline__ void decode_bf16_tile(const uint32_t* codes, const float* scales,
+                                                 uint16_t* out, int64_t c0, int64_t nchunk) {
+  uint32_t w[U];
+  float s[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
+    if (FULL || c < nchunk) {
+      w[u] = ld<(POL & kNtIn) != 0>(codes + c);
+      s[u] = scales[c >> log2i(LPG)];
+    } else {
+      w[u] = 0;
+      s[u] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
+    if (FULL || c < nchunk) {
+      float b[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) b[k] = static_cast<float>(nibble(w[u], k)) * s[u];
+      st<(POL & kNtOut) != 0>(pack_bf16x8(b), reinterpret_cast<u32x4*>(out) + c);
+    }
+  }
+}
+
+template <int U, int POL, int LPG>
+__global__ __launch_bounds__(kBlock) void echo_unpack_bf16_k(const uint32_t* __restrict__ codes,
+                                                              const float* __restrict__ scales,
+                                                              uint16_t* __restrict__ out,
+                                                              int64_t nchunk) {
+  const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
+  if (cb + kBlock * U <= nchunk)
+    decode_bf16_tile<U, POL, LPG, true>(codes, scales, out, cb + threadIdx.x, nchunk);
+  else
+    decode_bf16_tile<U, POL, LPG, false>(codes, scales, out, cb + threadIdx.x, nchunk);
+}
+
 template <int U, int POL, int LPG>
 __global__ __launch_bounds__(kBlock) void echo_unpack_k(const uint32_t* __restrict__ codes,
                                                          const float* __restrict__ scales,
@@ -274,25 +373,30 @@ constexpr int kOwnerPol = 0;
 constexpr int kDecodeUnroll = 2;
 constexpr int kDecodePol = kNtOut;
 
-template <int P, int LPG, int POL = kOwnerPol>
-hipError_t owner_pg(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
+template <int P, int LPG, bool OWN, int POL = kOwnerPol>
+hipError_t owner_pgo(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.nchunk + kBlock - 1) / kBlock));
   // without compensation the state is not touched, so its dtype does not matter
   if (!comp)
-    hipLaunchKernelGGL((echo_owner_k<P, false, POL, LPG, false>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, false, POL, LPG, false, OWN>), grid, dim3(kBlock), 0, s, a);
   else if (sb16)
-    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, true>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, true, OWN>), grid, dim3(kBlock), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, false>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((echo_owner_k<P, true, POL, LPG, false, OWN>), grid, dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
+template <int P, int LPG>
+hipError_t owner_pg(const OwnerArgs& a, bool comp, bool sb16, bool own, hipStream_t s) {
+  return own ? owner_pgo<P, LPG, true>(a, comp, sb16, s) : owner_pgo<P, LPG, false>(a, comp, sb16, s);
+}
+
 template <int P>
-hipError_t owner_p(const OwnerArgs& a, bool comp, int group, bool sb16, hipStream_t s) {
+hipError_t owner_p(const OwnerArgs& a, bool comp, int group, bool sb16, bool own, hipStream_t s) {
   switch (group) {
-    case 32: return owner_pg<P, 4>(a, comp, sb16, s);
-    case 64: return owner_pg<P, 8>(a, comp, sb16, s);
-    case 128: return owner_pg<P, 16>(a, comp, sb16, s);
+    case 32: return owner_pg<P, 4>(a, comp, sb16, own, s);
+    case 64: return owner_pg<P, 8>(a, comp, sb16, own, s);
+    case 128: return owner_pg<P, 16>(a, comp, sb16, own, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -315,12 +419,19 @@ hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
 }
 
 template <int U, int POL = kDecodePol, int LPG = 4>
-hipError_t decode_u(const uint32_t* codes, const float* scales, float* out, int64_t numel,
-                    hipStream_t s) {
-  const int64_t n4 = numel / 4;
-  const int64_t blocks = (n4 + kBlock * U - 1) / (kBlock * U);
-  hipLaunchKernelGGL((echo_unpack_k<U, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s,
-                     codes, scales, out, n4);
+hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64_t numel,
+                    bool out_bf16, hipStream_t s) {
+  if (out_bf16) {
+    const int64_t nchunk = numel / kElemsPerLane;
+    const int64_t blocks = (nchunk + kBlock * U - 1) / (kBlock * U);
+    hipLaunchKernelGGL((echo_unpack_bf16_k<U, POL, LPG>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, s, codes, scales, static_cast<uint16_t*>(out), nchunk);
+  } else {
+    const int64_t n4 = numel / 4;
+    const int64_t blocks = (n4 + kBlock * U - 1) / (kBlock * U);
+    hipLaunchKernelGGL((echo_unpack_k<U, POL, LPG>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
+                       0, s, codes, scales, static_cast<float*>(out), n4);
+  }
   return hipGetLastError();
 }
 
@@ -336,34 +447,34 @@ hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipSt
 }
 
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool sb16,
-                        hipStream_t s) {
+                        bool own, hipStream_t s) {
   switch (P) {
-    case 1: return owner_p<1>(a, compensate, group, sb16, s);
-    case 2: return owner_p<2>(a, compensate, group, sb16, s);
-    case 3: return owner_p<3>(a, compensate, group, sb16, s);
-    case 4: return owner_p<4>(a, compensate, group, sb16, s);
-    case 5: return owner_p<5>(a, compensate, group, sb16, s);
-    case 6: return owner_p<6>(a, compensate, group, sb16, s);
-    case 7: return owner_p<7>(a, compensate, group, sb16, s);
-    case 8: return owner_p<8>(a, compensate, group, sb16, s);
-    case 9: return owner_p<9>(a, compensate, group, sb16, s);
-    case 10: return owner_p<10>(a, compensate, group, sb16, s);
-    case 11: return owner_p<11>(a, compensate, group, sb16, s);
-    case 12: return owner_p<12>(a, compensate, group, sb16, s);
-    case 13: return owner_p<13>(a, compensate, group, sb16, s);
-    case 14: return owner_p<14>(a, compensate, group, sb16, s);
-    case 15: return owner_p<15>(a, compensate, group, sb16, s);
-    case 16: return owner_p<16>(a, compensate, group, sb16, s);
+    case 1: return owner_p<1>(a, compensate, group, sb16, own, s);
+    case 2: return owner_p<2>(a, compensate, group, sb16, own, s);
+    case 3: return owner_p<3>(a, compensate, group, sb16, own, s);
+    case 4: return owner_p<4>(a, compensate, group, sb16, own, s);
+    case 5: return owner_p<5>(a, compensate, group, sb16, own, s);
+    case 6: return owner_p<6>(a, compensate, group, sb16, own, s);
+    case 7: return owner_p<7>(a, compensate, group, sb16, own, s);
+    case 8: return owner_p<8>(a, compensate, group, sb16, own, s);
+    case 9: return owner_p<9>(a, compensate, group, sb16, own, s);
+    case 10: return owner_p<10>(a, compensate, group, sb16, own, s);
+    case 11: return owner_p<11>(a, compensate, group, sb16, own, s);
+    case 12: return owner_p<12>(a, compensate, group, sb16, own, s);
+    case 13: return owner_p<13>(a, compensate, group, sb16, own, s);
+    case 14: return owner_p<14>(a, compensate, group, sb16, own, s);
+    case 15: return owner_p<15>(a, compensate, group, sb16, own, s);
+    case 16: return owner_p<16>(a, compensate, group, sb16, own, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode(const uint32_t* codes, const float* scales, float* out, int64_t numel,
-                         int group, hipStream_t s) {
+hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out, int64_t numel,
+                         int group, bool out_bf16, hipStream_t s) {
   switch (group) {
-    case 32: return decode_u<kDecodeUnroll, kDecodePol, 4>(codes, scales, out, numel, s);
-    case 64: return decode_u<kDecodeUnroll, kDecodePol, 8>(codes, scales, out, numel, s);
-    case 128: return decode_u<kDecodeUnroll, kDecodePol, 16>(codes, scales, out, numel, s);
+    case 32: return decode_u<kDecodeUnroll, kDecodePol, 4>(codes, scales, out, numel, out_bf16, s);
+    case 64: return decode_u<kDecodeUnroll, kDecodePol, 8>(codes, scales, out, numel, out_bf16, s);
+    case 128: return decode_u<kDecodeUnroll, kDecodePol, 16>(codes, scales, out, numel, out_bf16, s);
     default: return hipErrorInvalidValue;
   }
 }

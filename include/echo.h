@@ -32,6 +32,9 @@
  *                            m <- fl(fl(beta*m) + fl((1-beta)*e)) for both;
  *   output:                  out = B (fp32; no third rounding).
  * With compensate == 0 the correction is zero and the state is not touched.
+ * Two variants change this chain: out_bf16 delivers bf16(B) and measures
+ * e = fl(V - bf16(B)); own_exact lets the owner of a segment add its own
+ * partial x_j in place of d_j (rank j quantizes every segment but its own).
  *
  * Conventions for every entry point
  *   - Device pointers point to the memory of the device that was current when
@@ -86,6 +89,15 @@ typedef struct {
                       /* fl(q*s), per rank and direction); 0 = off (default)       */
   int32_t state_bf16; /* 1 = variant: m_fast / m_slow stored in bfloat16 (each   */
                       /* fp32 update rounded to nearest, ties to even); 0 = fp32  */
+  int32_t out_bf16;   /* 1 = variant: the output is bfloat16, bf16(B) rounded to  */
+                      /* nearest even, and the owner's error is measured against */
+                      /* it, e = fl(V - bf16(B)), so later calls compensate the  */
+                      /* output rounding too; 0 = fp32 output B (default)         */
+  int32_t own_exact;  /* 1 = variant: the owner of segment j adds its own partial */
+                      /* x_j as it is (x_j + e_j with sender feedback) in rank    */
+                      /* order instead of fl(q_j*s_j); rank j neither quantizes  */
+                      /* nor sends segment j (its stage-1 codes, scales and error */
+                      /* there are left untouched); 0 = off (default)             */
 } echo_config;
 
 typedef struct echo_state echo_state; /* opaque host handle */
@@ -113,11 +125,11 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
 /* One whole all-reduce: echo_stage1, then echo_owner on direction `dir`,
  * then echo_decode.  partials: host array of P device pointers, each to N
  * contiguous elements of cfg.dtype, 16-byte aligned, read-only for the call.
- * out: device pointer to N fp32, 16-byte aligned, overlapping neither the
- * partials nor the workspace; it receives the reduced tensor every rank would
- * hold.  The state of `dir` advances in place.  Deterministic: identical
- * inputs and state give bit-identical results. */
-echo_status echo_reduce(const void* const* partials, float* out, echo_state* st,
+ * out: device pointer to N fp32 (N bfloat16 with out_bf16), 16-byte aligned,
+ * overlapping neither the partials nor the workspace; it receives the reduced
+ * tensor every rank would hold.  The state of `dir` advances in place.
+ * Deterministic: identical inputs and state give bit-identical results. */
+echo_status echo_reduce(const void* const* partials, void* out, echo_state* st,
                         echo_dir dir, echo_stream_t stream);
 
 /* Stage 1 on every rank: quantize each rank's partial to int4 codes and fp32
@@ -136,10 +148,11 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
  * state exactly as echo_stage1 would write it from that bf16 partial, which
  * itself never reaches memory.  Follow with echo_owner and echo_decode.
  * A, W: host arrays of P device pointers, 16-byte aligned, read-only.
- * Requires a bf16 state with group 32 and no sender feedback, M and H
- * multiples of 128 (M/128 <= 65535), K a multiple of 64.  Errors: ECHO_ERR_ARG
- * (null or misaligned pointer, A or W overlapping the workspace, sender
- * feedback on), ECHO_ERR_SHAPE (sizes,
+ * Requires a bf16 state with group 32, no sender feedback and no own_exact
+ * (the owner would need the partial itself), M and H multiples of 128
+ * (M/128 <= 65535), K a multiple of 64.  Errors: ECHO_ERR_ARG (null or
+ * misaligned pointer, A or W overlapping the workspace, sender feedback or
+ * own_exact on), ECHO_ERR_SHAPE (sizes,
  * M*H != N, group != 32), ECHO_ERR_DTYPE (state not bf16), ECHO_ERR_STATE,
  * ECHO_ERR_HIP. */
 echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
@@ -153,11 +166,16 @@ echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* con
 
 /* Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
  * apply the correction of direction `dir`, re-quantize into the broadcast
- * payload and update the compensator of `dir`. */
-echo_status echo_owner(echo_state* st, echo_dir dir, echo_stream_t stream);
+ * payload and update the compensator of `dir`.  partials: with own_exact, the
+ * same P device pointers the preceding echo_stage1 received (the owners read
+ * their own shares from them; ECHO_ERR_ARG if NULL); otherwise ignored and
+ * may be NULL. */
+echo_status echo_owner(const void* const* partials, echo_state* st, echo_dir dir,
+                       echo_stream_t stream);
 
-/* Every rank's decode of the broadcast payload into `out` (N fp32). */
-echo_status echo_decode(float* out, const echo_state* st, echo_stream_t stream);
+/* Every rank's decode of the broadcast payload into `out` (N fp32, or N
+ * bfloat16 with out_bf16; 16-byte aligned, not in the workspace). */
+echo_status echo_decode(void* out, const echo_state* st, echo_stream_t stream);
 
 /* Zero the compensator (and, with sender_feedback, the ranks' stage-1 errors)
  * of the directions in dir_mask (1 = fwd, 2 = bwd, 3 = both), e.g. at the

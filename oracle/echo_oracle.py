@@ -209,7 +209,7 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
               compensate: bool = True, beta_fast: float = 0.5,
               beta_slow: float = 0.95, group: int = GROUP,
               sender_feedback: bool = False, state_bf16: bool = False,
-              out_bf16: bool = False, own_exact: bool = False):
+              out_bf16: bool = False, own_exact: bool = False, segments=None):
     """One Echo all-reduce of ``partials`` ([P, N] float32).
 
     Advances ``state`` (direction ``direction``) in place when compensating and
@@ -237,6 +237,11 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     and with sender feedback its error there is neither used nor changed), and
     the owner's rank-order sum takes x_j (x_j + e_j with sender feedback) in
     place of fl(q_j * s_j) on segment j.
+
+    ``segments``: the group ranges [g0, g1) owned by ranks 0..P-1; by default
+    the ceil split of this message (owner_segments).  Only own_exact depends
+    on it: a group-aligned window of a longer message passes that message's
+    split restricted to the window.
     """
     x = np.ascontiguousarray(partials, dtype=F32)
     if x.ndim != 2:
@@ -247,7 +252,9 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     if not np.all(np.isfinite(x)):
         raise ValueError("partials must be finite")
     n_g = N // group
-    segs = owner_segments(n_g, P)
+    segs = owner_segments(n_g, P) if segments is None else [tuple(sg) for sg in segments]
+    if len(segs) != P:
+        raise ValueError("one segment per rank")
 
     # 1. stage 1 on every rank (with sender feedback: on x + e, then the new e)
     q1 = np.empty((P, N), np.int8)
@@ -344,6 +351,7 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         "B": B,
         "r": err,
         "out": out,
+        "segments": segs,
     }
 
 

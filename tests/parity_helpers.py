@@ -28,11 +28,12 @@ def _upload(raw, dtype, device):
 
 
 def _state(P, N, dtype, compensate=True, beta=(0.5, 0.95), device="cuda:0", poison=True, group=32,
-           sender_feedback=False, state_bf16=False):
+           sender_feedback=False, state_bf16=False, out_bf16=False, own_exact=False):
     torch = _torch()
     import error_compensated_bit_echo_amd as E
     cfg = E.EchoConfig.make(P, N, dtype, compensate, beta[0], beta[1], group=group,
-                            sender_feedback=sender_feedback, state_bf16=state_bf16)
+                            sender_feedback=sender_feedback, state_bf16=state_bf16,
+                            out_bf16=out_bf16, own_exact=own_exact)
     ws = torch.full((max(E.echo_workspace_bytes(cfg), 1),), 0xFF if poison else 0,
                     dtype=torch.uint8, device=device)
     return E.echo_init_state(cfg, ws)
@@ -54,13 +55,28 @@ def _fetch(state, out, direction, lo=0, hi=None):
         "scales2": v["scales2"][g0:g1].cpu().numpy(),
         "m_fast": v["m_fast"][lo:hi].float().cpu().numpy(),  # bf16 state widens exactly
         "m_slow": v["m_slow"][lo:hi].float().cpu().numpy(),
-        "out": out[lo:hi].cpu().numpy(),
+        "out": out[lo:hi].float().cpu().numpy(),  # a bf16 output widens exactly
         "sender_err": None if v["sender_err"] is None else v["sender_err"][:, lo:hi].cpu().numpy(),
     }
 
 
-def _compare(g, o, st_oracle, direction, compensate, where=""):
-    """Assert the parity bar; returns the number of float elements not bit-equal."""
+def _out_tensor(state, device="cuda:0"):
+    torch = _torch()
+    dt = torch.bfloat16 if state.cfg.out_bf16 else torch.float32
+    return torch.empty(state.numel, dtype=dt, device=device)
+
+
+def _compare(g, o, st_oracle, direction, compensate, where="", own_exact=False):
+    """Assert the parity bar; returns the number of float elements not bit-equal.
+    With own_exact, a rank's stage-1 payload over its own segment is never
+    written (the owner adds its partial itself) and is left out."""
+    if own_exact:
+        g = dict(g)
+        g["codes1"], g["scales1"] = g["codes1"].copy(), g["scales1"].copy()
+        G = o["q2"].size // max(o["scales2"].size, 1)
+        for r, (g0, g1) in enumerate(o["segments"]):
+            g["codes1"][r, g0 * G // 2:g1 * G // 2] = o["codes1"][r, g0 * G // 2:g1 * G // 2]
+            g["scales1"][r, g0:g1] = o["scales1"][r, g0:g1]
     assert np.array_equal(g["codes1"], o["codes1"]), f"stage-1 codes differ {where}"
     assert np.array_equal(g["scales1"].view(np.uint32), o["scales1"].view(np.uint32)), \
         f"stage-1 scales differ {where}"

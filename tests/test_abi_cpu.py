@@ -39,9 +39,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_config_struct_layout():
-    # int32 P; (pad) int64 numel; int32 group; enum dtype; int32 compensate; float; float
-    assert ctypes.sizeof(B.EchoConfig) == 48
+    # int32 P; (pad) int64 numel; int32 group; enum dtype; int32 compensate; float; float;
+    # int32 sender_feedback, state_bf16, out_bf16, own_exact; (pad to 8)
+    assert ctypes.sizeof(B.EchoConfig) == 56
     assert B.EchoConfig.state_bf16.offset == 40
+    assert B.EchoConfig.out_bf16.offset == 44
+    assert B.EchoConfig.own_exact.offset == 48
     assert B.EchoConfig.numel.offset == 8
     assert B.EchoConfig.beta_slow.offset == 32
     assert ctypes.sizeof(B.EchoViews) == 80
@@ -66,6 +69,9 @@ def test_workspace_bytes_formula():
         # bf16 state: four compensator vectors of 2N bytes instead of 4N
         cfg = B.EchoConfig.make(P, N, dt, group=G, state_bf16=True)
         assert _ws(cfg) == want - 4 * al(4 * N) + 4 * al(2 * N)
+        # the bf16-output and own-partial variants need no workspace of their own
+        cfg = B.EchoConfig.make(P, N, dt, group=G, out_bf16=True, own_exact=True)
+        assert _ws(cfg) == want
     assert _ws(B.EchoConfig.make(4, 0)) == 0
 
 
@@ -77,7 +83,7 @@ def test_workspace_bytes_formula():
     ("dtype", 7, B.ECHO_ERR_DTYPE), ("compensate", 2, B.ECHO_ERR_ARG),
     ("beta_fast", -0.5, B.ECHO_ERR_ARG), ("beta_slow", float("nan"), B.ECHO_ERR_ARG),
     ("beta_slow", 1.5, B.ECHO_ERR_ARG), ("sender_feedback", 2, B.ECHO_ERR_ARG),
-    ("state_bf16", 3, B.ECHO_ERR_ARG),
+    ("state_bf16", 3, B.ECHO_ERR_ARG), ("out_bf16", 2, B.ECHO_ERR_ARG), ("own_exact", -1, B.ECHO_ERR_ARG),
 ])
 def test_init_rejects_bad_config_without_touching_the_gpu(field, value, status):
     lib = B.load_library()
@@ -102,7 +108,7 @@ def test_init_rejects_missing_or_small_workspace():
 
 def test_calls_on_a_null_state_are_rejected():
     lib = B.load_library()
-    assert lib.echo_owner(None, 0, None) == B.ECHO_ERR_STATE
+    assert lib.echo_owner(None, None, 0, None) == B.ECHO_ERR_STATE
     assert lib.echo_reset(None, 3, None) == B.ECHO_ERR_STATE
     assert lib.echo_decode(None, None, None) == B.ECHO_ERR_STATE
     assert lib.echo_stage1(None, None, 0, None) == B.ECHO_ERR_STATE

@@ -109,6 +109,8 @@ def test_argument_errors(cuda):
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_DTYPE
     st = _state(P, M * H, "bf16", sender_feedback=True)
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    st = _state(P, M * H, "bf16", own_exact=True)  # the owner would need the partial itself
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
     st = _state(P, M * H, "bf16", group=64)
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_SHAPE
     st = _state(P, M * H, "bf16")

@@ -10,7 +10,7 @@ import pytest
 
 from oracle import echo_oracle as eo
 from error_compensated_bit_echo_amd import synth
-from parity_helpers import F32, _compare, _fetch, _state, _torch, _upload
+from parity_helpers import F32, _compare, _fetch, _out_tensor, _state, _torch, _upload
 
 pytestmark = pytest.mark.gpu
 
@@ -272,7 +272,7 @@ def test_argument_errors_launch_nothing(cuda):
     bad = (ctypes.c_void_p * P)(parts[0].data_ptr(), parts[1].data_ptr() + 2)
     assert lib.echo_reduce(bad, ctypes.c_void_p(out.data_ptr()), st.handle, 0, s) == B.ECHO_ERR_ARG
     assert lib.echo_reduce(arr, ctypes.c_void_p(out.data_ptr()), st.handle, 2, s) == B.ECHO_ERR_ARG
-    assert lib.echo_owner(st.handle, 5, s) == B.ECHO_ERR_ARG
+    assert lib.echo_owner(None, st.handle, 5, s) == B.ECHO_ERR_ARG
     assert lib.echo_reset(st.handle, 0, s) == B.ECHO_ERR_ARG
     assert lib.echo_reset(st.handle, 4, s) == B.ECHO_ERR_ARG
     # binding-level checks: dtype and count
@@ -309,8 +309,16 @@ def _windows(N, n_win, width, seed):
     return sorted(starts)
 
 
+def _window_segments(N, P, group, w, width):
+    """The whole message's owner split, restricted to the window [w, w + width)."""
+    lo, hi = w // group, (w + width) // group
+    return [(min(max(a, lo), hi) - lo, min(max(b, lo), hi) - lo)
+            for a, b in eo.owner_segments(N // group, P)]
+
+
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
-                  P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False):
+                  P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
+                  out_bf16=False, own_exact=False):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
     value distribution and dtype)."""
@@ -320,9 +328,13 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     P = c["P"] if P is None else P
     N = synth.numel(cfg_id) if N is None else N
     st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback,
-                state_bf16=state_bf16)
-    out = torch.empty(N, dtype=torch.float32, device=cuda)
+                state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact)
+    out = _out_tensor(st, cuda)
     wins = _windows(N, n_win, width, cfg_id)
+    if own_exact:  # add a window on every segment boundary
+        per = eo.owner_segments(N // 32, P)
+        wins = sorted(set(wins) | {max(0, min(N - width, g0 * 32 - width // 2)) // 32 * 32
+                                   for g0, _ in per[1:]})
     so = {w: eo.OracleState(width) for w in wins}
     parts = None
     for t in range(calls):
@@ -334,10 +346,11 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
             for w in wins:
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
                 o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
-                                 state_bf16=state_bf16)
+                                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact,
+                                 segments=_window_segments(N, P, 32, w, width) if own_exact else None)
                 g = _fetch(st, out, d, w, w + width)
                 assert _compare(g, o, so[w], d, compensate,
-                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}") == 0
+                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}", own_exact) == 0
         print(f"cfg{cfg_id} P={P} N={N}: call {t} ok", flush=True)
 
 
@@ -484,3 +497,172 @@ def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
 
 def test_bf16_state_full_size(cuda):
     _windowed_run(cuda, 2, 6, (0,), state_bf16=True)
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 output (a variant): out = bf16(B), the error measured against it
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_bf16_output_tiny_config_every_call(cuda, compensate):
+    import error_compensated_bit_echo_amd as E
+    c = synth.CONFIGS[1]
+    P, N = c["P"], synth.numel(1)
+    st = _state(P, N, "f32", compensate, out_bf16=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    for t in range(c["calls"]):
+        raw, vals = synth.host_partials(1, 0, t)
+        E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, out_bf16=True)
+        assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}") == 0
+
+
+@pytest.mark.parametrize("P,dtype,group,sfb,sb16", [(1, "bf16", 32, False, False), (3, "f32", 32, False, False),
+                                                    (8, "bf16", 32, False, False), (16, "bf16", 64, True, False),
+                                                    (4, "f32", 128, False, True), (8, "bf16", 32, True, True)])
+def test_bf16_output_multi_tile_both_directions(cuda, P, dtype, group, sfb, sb16):
+    import error_compensated_bit_echo_amd as E
+    N = 2048 * 5 + group * 3
+    st = _state(P, N, dtype, group=group, sender_feedback=sfb, state_bf16=sb16, out_bf16=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    rng = np.random.default_rng(P * 10 + group)
+    for t in range(5):
+        for d in (0, 1):
+            if (t + d) % 2:
+                vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+                raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
+            else:
+                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+            E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, group=group, sender_feedback=sfb, state_bf16=sb16, out_bf16=True)
+            assert _compare(_fetch(st, out, d), o, so, d, True,
+                            f"G={group} P={P} sfb={sfb} sb16={sb16} call {t} dir {d}") == 0
+
+
+def test_bf16_output_full_size(cuda):
+    _windowed_run(cuda, 2, 6, (0,), out_bf16=True)
+
+
+# ---------------------------------------------------------------------------
+# the owner adds its own partial exactly (a variant)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("compensate", [True, False])
+def test_own_exact_tiny_config_every_call(cuda, compensate):
+    import error_compensated_bit_echo_amd as E
+    c = synth.CONFIGS[1]
+    P, N = c["P"], synth.numel(1)
+    st = _state(P, N, "f32", compensate, own_exact=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    for t in range(c["calls"]):
+        raw, vals = synth.host_partials(1, 0, t)
+        E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
+        o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, own_exact=True)
+        assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}", own_exact=True) == 0
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_own_exact_multi_tile_ragged(cuda, P, dtype):
+    """Segment boundaries that fall inside tiles, a ragged tail, both directions."""
+    import error_compensated_bit_echo_amd as E
+    N = 32 * (64 * 3 + 37) * 8 + 32 * 5
+    st = _state(P, N, dtype, own_exact=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    for t in range(3):
+        for d in (0, 1):
+            raw, vals = synth.host_partials(2, d, t, P=P, n=N, dtype=dtype)
+            E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, own_exact=True)
+            assert _compare(_fetch(st, out, d), o, so, d, True, f"P={P} {dtype} call {t} dir {d}",
+                            own_exact=True) == 0
+
+
+@pytest.mark.parametrize("P,dtype,group,sfb,comp,sb16,obf", [
+    (4, "bf16", 64, False, True, False, False), (3, "f32", 128, False, True, False, False),
+    (8, "bf16", 32, True, True, False, False), (16, "f32", 64, True, False, False, False),
+    (5, "bf16", 32, False, False, False, True), (8, "bf16", 32, True, True, True, True)])
+def test_own_exact_with_other_variants(cuda, P, dtype, group, sfb, comp, sb16, obf):
+    import error_compensated_bit_echo_amd as E
+    N = 2048 * 5 + group * 3
+    st = _state(P, N, dtype, comp, group=group, sender_feedback=sfb, state_bf16=sb16, out_bf16=obf,
+                own_exact=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    rng = np.random.default_rng(P * 7 + group)
+    for t in range(5):
+        for d in (0, 1):
+            if (t + d) % 2:
+                vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
+                raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
+            else:
+                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+            E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, compensate=comp, group=group, sender_feedback=sfb,
+                             state_bf16=sb16, out_bf16=obf, own_exact=True)
+            assert _compare(_fetch(st, out, d), o, so, d, comp,
+                            f"G={group} P={P} sfb={sfb} comp={comp} call {t} dir {d}", own_exact=True) == 0
+
+
+@pytest.mark.parametrize("P,N", [(8, 96), (16, 32 * 20), (3, 32), (4, 32 * 5)])
+def test_own_exact_fewer_groups_than_owners(cuda, P, N):
+    """Owners with empty segments (ceil split): ranks past the last group skip nothing."""
+    import error_compensated_bit_echo_amd as E
+    st = _state(P, N, "bf16", own_exact=True)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    for t in range(3):
+        raw, vals = synth.host_partials(2, 0, t, P=P, n=N)
+        E.echo_reduce(_upload(raw, "bf16", cuda), out, st, 0)
+        o = eo.echo_call(vals, so, 0, own_exact=True)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"P={P} N={N} call {t}", own_exact=True) == 0
+
+
+def test_own_exact_stage_entry_points_and_graph(cuda):
+    """Stage by stage (the owner given the partials) equals echo_reduce; a captured
+    graph replays like eager calls; the owner stage needs the partials."""
+    import ctypes
+    import error_compensated_bit_echo_amd as E
+    from error_compensated_bit_echo_amd import binding as B
+    torch = _torch()
+    P, N = 8, 64 * 4096 + 32 * 3
+    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    parts = _upload(raw, "bf16", cuda)
+    kw = dict(own_exact=True, out_bf16=True)
+    s1, s2, sg = _state(P, N, "bf16", **kw), _state(P, N, "bf16", **kw), _state(P, N, "bf16", **kw)
+    o1, o2, og = _out_tensor(s1, cuda), _out_tensor(s2, cuda), _out_tensor(sg, cuda)
+    for d in (0, 1, 1, 0):
+        E.echo_reduce(parts, o1, s1, d)
+        E.echo_stage1(parts, s2, d)
+        E.echo_owner(s2, d, partials=parts)
+        E.echo_decode(o2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for d in (0, 1):
+        assert torch.equal(E.echo_debug_views(s1, d)["m_slow"], E.echo_debug_views(s2, d)["m_slow"])
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert E.load_library().echo_owner(None, s2.handle, 0, s) == B.ECHO_ERR_ARG
+    # graph capture
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.echo_reduce(parts, og, sg, E.ECHO_FWD)
+    torch.cuda.synchronize()
+    E.echo_reset(sg, 3)
+    E.echo_reset(s1, 3)
+    for k in range(3):
+        E.echo_reduce(parts, o1, s1, E.ECHO_FWD)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, og), f"replay {k}"
+        _ = (o1.float() * 2).sum().item()
+
+
+def test_own_exact_full_size(cuda):
+    _windowed_run(cuda, 2, 6, (0,), own_exact=True)
+
+
+def test_own_exact_headline_size(cuda):
+    """1 GiB bf16 per rank, P = 8, the same partials every call."""
+    _windowed_run(cuda, 5, 4, (0,), same_partials=True, n_win=6, width=1 << 14, own_exact=True)

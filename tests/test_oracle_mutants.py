@@ -37,8 +37,8 @@ MUTANTS = {
         "quot = v[nz].astype(F64) / s[nz].astype(F64)[:, None]",
         "quot = (v[nz] / s[nz][:, None]).astype(F64)"),
     "ranks summed in reverse order": (
-        "for r in range(P):\n            d = dequantize_groups",
-        "for r in reversed(range(P)):\n            d = dequantize_groups"),
+        "for r in range(P):\n            if own_exact and r == j:",
+        "for r in reversed(range(P)):\n            if own_exact and r == j:"),
     "nibbles in the other order": (
         "return (u[0::2] | (u[1::2] << np.uint8(4))).astype(np.uint8)",
         "return (u[1::2] | (u[0::2] << np.uint8(4))).astype(np.uint8)"),
@@ -48,8 +48,8 @@ MUTANTS = {
         "s = a / F32(QMAX)  # binary32 division, round to nearest even",
         "s = np.maximum(a / F32(QMAX), F32(1e-30))"),
     "sender error from the partial, not from x + e": (
-        "e1[r] = xs[r] - dequantize_groups(q, s, group).reshape(-1)",
-        "e1[r] = x[r] - dequantize_groups(q, s, group).reshape(-1)"),
+        "e_new = xs[r] - dequantize_groups(q, s, group).reshape(-1)",
+        "e_new = x[r] - dequantize_groups(q, s, group).reshape(-1)"),
     "sender error added with the wrong sign": ("xs = x + e1", "xs = x - e1"),
     "bf16 output: error measured against B, not the delivered value": (
         "        if out_bf16:  # the value the ranks will hold\n            bb = round_to_bf16(bb)\n", ""),

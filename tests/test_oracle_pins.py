@@ -718,3 +718,20 @@ def test_own_exact_removes_one_rank_of_stage1_error():
         e_own = eo.echo_call(x, None, compensate=False, own_exact=True)["S"].astype(F64) - exact
         ratio = np.sqrt(np.mean(e_own ** 2) / np.mean(e_all ** 2))
         assert abs(ratio - np.sqrt((P - 1) / P)) < 0.05, (P, ratio)
+
+
+def test_own_exact_window_with_the_message_split_equals_whole_message():
+    """Groups are independent once the owner of each group is fixed: a window
+    given the whole message's owner split reproduces the whole call there."""
+    P, N, G = 3, 32 * 40, 32
+    _, x = synth.host_partials(1, 0, 4, P=P, n=N)
+    whole = eo.echo_call(x, eo.OracleState(N), own_exact=True)
+    segs = eo.owner_segments(N // G, P)
+    for g_lo, g_hi in ((0, 40), (5, 19), (13, 14), (12, 33)):
+        win = [(min(max(a, g_lo), g_hi) - g_lo, min(max(b, g_lo), g_hi) - g_lo) for a, b in segs]
+        o = eo.echo_call(x[:, g_lo * G:g_hi * G], eo.OracleState((g_hi - g_lo) * G), own_exact=True,
+                         segments=win)
+        for key in ("S", "V", "out", "q2", "scales2"):
+            lo, hi = (g_lo, g_hi) if key == "scales2" else (g_lo * G, g_hi * G)
+            assert np.array_equal(o[key], whole[key][lo:hi]), (g_lo, g_hi, key)
+        assert np.array_equal(o["q1"], whole["q1"][:, g_lo * G:g_hi * G])
