@@ -27,6 +27,7 @@ METRIC = "Echo reduce GB/s (bf16-equiv payload) + % HBM peak, 1 GB msg, P=8 emul
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published
 # sources of the three kernels whose HBM traffic the counter runs measure
 KERNEL_SOURCES = ["error_compensated_bit_echo_amd/csrc/echo_kernels.hip",
+                  "error_compensated_bit_echo_amd/csrc/echo_owner.h",
                   "error_compensated_bit_echo_amd/csrc/echo_internal.h",
                   "error_compensated_bit_echo_amd/csrc/echo_div7.h",
                   "error_compensated_bit_echo_amd/csrc/echo_quant.h",

@@ -9,14 +9,16 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libecho.so")
-SOURCES = ["echo_kernels.hip", "echo_gemm.hip", "echo_api.hip"]
-HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h", "echo_device.h"]
+SOURCES = ["echo_kernels.hip", "echo_owner_p1_4.hip", "echo_owner_p5_8.hip", "echo_owner_p9_12.hip",
+           "echo_owner_p13_16.hip", "echo_gemm.hip", "echo_api.hip"]
+HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h", "echo_device.h", "echo_owner.h"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: every multiply and add is its own IEEE operation (the
@@ -24,7 +26,7 @@ ARCH = "gfx950"
 # -packed-fp32-ops off: no v_pk_*_f32 instructions are emitted.
 # Denormals are kept (HIP's default; no fast-math, no flush-to-zero).
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
@@ -38,20 +40,37 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libecho)")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every HIP source into ``libecho.so``; returns its path."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+
+
+def build_library(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source (in parallel, one object each) and link
+    ``libecho.so``; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    cc = hipcc()
+    tmpdir = tempfile.mkdtemp(prefix="echo_build_")
+    tmp = LIB + f".tmp{os.getpid()}"
+    try:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        cmds = [[cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        # the host pass does not know the gfx feature flag; that warning is expected
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+    finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    # the host pass does not know the gfx feature flag; that warning is expected
-    os.replace(tmp, LIB)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -48,6 +48,15 @@ hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipSt
 // own_exact: a.own_src / a.own_chunks are set
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
                         bool own_exact, hipStream_t s);
+// the owner launches by rank count, one compilation unit each (echo_owner_p*.hip)
+hipError_t launch_owner_p1_4(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p5_8(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p9_12(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                              bool own_exact, hipStream_t s);
+hipError_t launch_owner_p13_16(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                               bool own_exact, hipStream_t s);
 // out: N fp32, or N bfloat16 when out_bf16
 hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out,
                          int64_t numel, int group, bool out_bf16, hipStream_t s);
