@@ -116,7 +116,10 @@ def device_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | Non
             x.mul_(std)
         if c["outlier_p"] > 0.0:
             mask = torch.rand(n, generator=g, device=device) < c["outlier_p"]
-            x[mask] *= c["outlier_mult"]
+            # in slices: torch's masked indexing mis-sizes its buffers past 2^32 elements
+            for lo in range(0, n, 1 << 30):
+                xs, ms = x[lo:lo + (1 << 30)], mask[lo:lo + (1 << 30)]
+                xs[ms] *= c["outlier_mult"]
             del mask
         out.append(x if c["dtype"] == "f32" else x.to(torch.bfloat16))
         del x

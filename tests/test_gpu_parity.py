@@ -318,10 +318,10 @@ def _window_segments(N, P, group, w, width):
 
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
                   P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
-                  out_bf16=False, own_exact=False):
+                  out_bf16=False, own_exact=False, extra_windows=()):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
-    value distribution and dtype)."""
+    value distribution and dtype); extra_windows adds group-aligned window starts."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     c = synth.CONFIGS[cfg_id]
@@ -330,7 +330,7 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback,
                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact)
     out = _out_tensor(st, cuda)
-    wins = _windows(N, n_win, width, cfg_id)
+    wins = sorted(set(_windows(N, n_win, width, cfg_id)) | set(extra_windows))
     if own_exact:  # add a window on every segment boundary
         per = eo.owner_segments(N // 32, P)
         wins = sorted(set(wins) | {max(0, min(N - width, g0 * 32 - width // 2)) // 32 * 32
@@ -666,3 +666,13 @@ def test_own_exact_full_size(cuda):
 def test_own_exact_headline_size(cuda):
     """1 GiB bf16 per rank, P = 8, the same partials every call."""
     _windowed_run(cuda, 5, 4, (0,), same_partials=True, n_win=6, width=1 << 14, own_exact=True)
+
+
+def test_element_indices_beyond_2_32(cuda):
+    """N = 2^32 + 96 elements per rank (P = 2; bf16 state and output and the owners'
+    own shares keep the footprint near 65 GB): element, chunk and scale indices
+    pass 2^32, 2^29 and 2^27, byte offsets pass 2^33.  Windows at both ends (the
+    last one spans element 2^32), on the owner boundary and just below 2^32."""
+    N, width = (1 << 32) + 96, 1 << 13
+    _windowed_run(cuda, 5, 2, (0,), P=2, N=N, n_win=4, width=width, state_bf16=True,
+                  out_bf16=True, own_exact=True, extra_windows=((1 << 32) - 2 * width,))
