@@ -676,3 +676,34 @@ def test_element_indices_beyond_2_32(cuda):
     N, width = (1 << 32) + 96, 1 << 13
     _windowed_run(cuda, 5, 2, (0,), P=2, N=N, n_win=4, width=width, state_bf16=True,
                   out_bf16=True, own_exact=True, extra_windows=((1 << 32) - 2 * width,))
+
+
+def test_independent_states_on_two_streams(cuda):
+    """Two states with different configurations, driven on two streams at once,
+    give exactly what each gives alone: the library keeps no state of its own."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P1, N1, P2, N2 = 8, 32 * 4096 * 3, 3, 64 * 1024 + 192
+    raw1, _ = synth.host_partials(3, 0, 0, P=P1, n=N1)
+    raw2, _ = synth.host_partials(2, 1, 0, P=P2, n=N2, dtype="f32")
+    p1, p2 = _upload(raw1, "bf16", cuda), _upload(raw2, "f32", cuda)
+    cfg = [dict(P=P1, N=N1, dtype="bf16", kw=dict(own_exact=True)),
+           dict(P=P2, N=N2, dtype="f32", kw=dict(state_bf16=True, out_bf16=True, group=64))]
+
+    def run(streams):
+        sts = [_state(c["P"], c["N"], c["dtype"], **c["kw"]) for c in cfg]
+        outs = [_out_tensor(st, cuda) for st in sts]
+        torch.cuda.synchronize()
+        for t in range(4):
+            for i, (st, parts) in enumerate(zip(sts, (p1, p2))):
+                s = streams[i]
+                with torch.cuda.stream(s):
+                    E.echo_reduce(parts, outs[i], st, t % 2, stream=s)
+        torch.cuda.synchronize()
+        return [o.clone() for o in outs], [E.echo_debug_views(st, 0)["m_slow"].clone() for st in sts]
+
+    cur = torch.cuda.current_stream()
+    alone = run([cur, cur])
+    both = run([torch.cuda.Stream(), torch.cuda.Stream()])
+    for a, b in zip(alone[0] + alone[1], both[0] + both[1]):
+        assert torch.equal(a, b)
