@@ -330,9 +330,10 @@ def decode_report(E, synth, torch, dev) -> dict:
 def tp_report(torch, dev) -> dict:
     """Echo inside a tensor-parallel MLP stack (8 layers, P = 4, 2048 tokens,
     hidden 4096, ffn 16384): one training step (forward + backward, 8 Echo calls
-    per direction) with Echo, Echo without compensation and exact all-reduces;
-    errors of the loss and the gradients against the exact step, step time and
-    the time of the Echo calls inside it."""
+    per direction) with Echo, Echo without compensation and exact all-reduces
+    (fp32 products), and with Echo and the row-parallel products in bfloat16 on
+    libecho's kernel, written out or with stage 1 fused into them; errors of the
+    loss and the gradients against the exact fp32 step, and step times."""
     from error_compensated_bit_echo_amd import tp
 
     T, H, F, P, L = 2048, 4096, 16384, 4, 8
@@ -353,11 +354,26 @@ def tp_report(torch, dev) -> dict:
         torch.cuda.synchronize()
         ms[mode] = a.elapsed_time(b)
 
+    # the row-parallel product in bfloat16 on libecho's kernel, written out then
+    # reduced, or with stage 1 in its epilogue (bit-identical results)
+    for prod in ("bf16", "bf16_fused"):
+        m2 = tp.TPMLPStack(L, H, F, P, seed=21, device=dev, product=prod)
+        group = tp.EchoGroup(P, T * H, mode="echo", device=dev)
+        tp.train_step(m2, group, x0, target)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        res["echo_" + prod] = tp.train_step(m2, group, x0, target)
+        b.record()
+        torch.cuda.synchronize()
+        ms["echo_" + prod] = a.elapsed_time(b)
+        del m2
+
     def rel(x, y):
         return float((x - y).float().norm() / y.float().norm())
 
     errs = {}
-    for mode in ("echo", "echo_off"):
+    for mode in ("echo", "echo_off", "echo_bf16", "echo_bf16_fused"):
         loss, dx, dw = res[mode]
         errs[mode] = {"loss_rel_err": abs(float(loss - res["exact"][0])) / float(res["exact"][0]),
                       "dx0_rel_err": rel(dx, res["exact"][1]),

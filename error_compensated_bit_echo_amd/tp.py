@@ -19,6 +19,12 @@ by all the block's calls of one pass and reset at the start of each step.
 The P ranks are P tensors on one GPU; every reduction runs in libecho's
 kernels through the C ABI.  A ``mode`` of "exact" replaces both collectives by
 a plain sum (the bf16 wire values added in fp32), for comparison.
+
+The row-parallel product and ``g`` can also run as one step in bfloat16
+(``product="bf16_fused"``): libecho's MFMA product writes each rank's stage-1
+payload straight from its output tile, then the owner and decode stages
+finish the all-reduce; ``"bf16"`` runs the same product written out followed
+by a whole Echo call, which gives bit-identical results.
 """
 from __future__ import annotations
 
@@ -52,6 +58,29 @@ class EchoGroup:
             B.echo_reset(self.state, 3)
         self.log.clear()
 
+    def product_allreduce(self, A, W, fused: bool):
+        """Forward all-reduce of bf16(A_r @ W_r^T) (A_r [T, K], W_r [H, K] bf16)
+        on the forward state: fused, stage 1 runs in the product's epilogue;
+        otherwise the product is written out and reduced by a whole call."""
+        import torch
+
+        if self.mode == "exact":
+            raise ValueError("the bf16 product path needs an Echo state")
+        T, H = A[0].shape[0], W[0].shape[0]
+        out = torch.empty(self.numel, dtype=torch.float32, device=self.device)
+        if fused:
+            B.echo_gemm_stage1(A, W, self.state)
+            B.echo_owner(self.state, B.ECHO_FWD)
+            B.echo_decode(out, self.state)
+        else:
+            parts = [torch.empty(T, H, dtype=torch.bfloat16, device=self.device) for _ in range(self.P)]
+            B.echo_gemm_bf16(A, W, parts)
+            B.echo_reduce([p.view(-1) for p in parts], out, self.state, B.ECHO_FWD)
+        if self.record:
+            self.log.append((B.ECHO_FWD, ("product", [a.detach().clone() for a in A],
+                                          [w.detach().clone() for w in W]), out.detach().clone()))
+        return out
+
     def allreduce(self, partials, direction: int):
         """Sum of the P bf16 partials ([..] contiguous, numel each) as fp32."""
         import torch
@@ -71,6 +100,33 @@ class EchoGroup:
 
 def _fns():
     import torch
+
+    class RowParallelEcho(torch.autograd.Function):
+        """g(h_r @ W2_r) with the products in bfloat16 on libecho's matrix-core
+        kernel: forward gives sum_r bf16(bf16(h_r) @ bf16(W2_r)) through Echo
+        (fused: stage 1 in the product's epilogue); backward is the fp32
+        gradient of sum_r h_r @ W2_r (the rounding passed straight through)."""
+
+        @staticmethod
+        def forward(ctx, group: "EchoGroup", shape, fused: bool, *hw):
+            P = group.P
+            hs, ws = hw[:P], hw[P:]
+            A = [h.to(torch.bfloat16).contiguous() for h in hs]   # [T, F/P]
+            W = [w.t().to(torch.bfloat16).contiguous() for w in ws]  # [H, F/P]: output features by K
+            out = group.product_allreduce(A, W, fused)
+            ctx.save_for_backward(*hs, *ws)
+            ctx.P = P
+            return out.view(shape)
+
+        @staticmethod
+        def backward(ctx, grad):
+            P = ctx.P
+            saved = ctx.saved_tensors
+            hs, ws = saved[:P], saved[P:]
+            g = grad.contiguous()
+            dh = [g @ w.t().contiguous() for w in ws]
+            dw = [h.t().contiguous() @ g for h in hs]
+            return (None, None, None) + tuple(dh) + tuple(dw)
 
     class ReduceForward(torch.autograd.Function):
         """g: forward all-reduce of the P partial outputs; backward identity per rank."""
@@ -100,10 +156,18 @@ def _fns():
             out = ctx.group.allreduce(parts, B.ECHO_BWD)
             return None, out.view(ctx.shape).to(ctx.dtype)
 
-    return ReduceForward, ReduceBackward
+    return ReduceForward, ReduceBackward, RowParallelEcho
 
 
 _FNS = None
+
+
+def row_parallel_echo(group: "EchoGroup", hs, ws, shape, fused: bool):
+    """g(sum_r h_r @ W2_r) with bf16 products on libecho's kernel (see RowParallelEcho)."""
+    global _FNS
+    if _FNS is None:
+        _FNS = _fns()
+    return _FNS[2].apply(group, shape, fused, *hs, *ws)
 
 
 def reduce_forward(group: EchoGroup, partials, shape):
@@ -126,15 +190,21 @@ class TPMLPStack:
     """L pre-norm MLP blocks, each split over P ranks: W1 column-parallel
     ([H, F] in P slices of F/P columns), W2 row-parallel ([F, H] in P slices of
     F/P rows); x <- x + g(sum_r gelu(f(a)_r @ W1_r) @ W2_r), a = rmsnorm(x).
-    Weights are fp32 and seeded; the products are taken in fp32 and each
-    rank's partial output is rounded to bf16 (the wire dtype)."""
+    Weights are fp32 and seeded.  product "f32": the products are taken in fp32
+    and each rank's partial output is rounded to bf16 (the wire dtype);
+    "bf16" / "bf16_fused": the row-parallel product runs in bfloat16 on
+    libecho's kernel (written out, or with stage 1 in its epilogue; T and H
+    multiples of 128, F/P of 64)."""
 
-    def __init__(self, layers: int, hidden: int, ffn: int, P: int, seed: int = 0, device=None):
+    def __init__(self, layers: int, hidden: int, ffn: int, P: int, seed: int = 0, device=None,
+                 product: str = "f32"):
         import torch
 
         if ffn % P:
             raise ValueError("ffn must be divisible by P")
-        self.L, self.H, self.F, self.P = layers, hidden, ffn, P
+        if product not in ("f32", "bf16", "bf16_fused"):
+            raise ValueError(f"product {product!r}")
+        self.L, self.H, self.F, self.P, self.product = layers, hidden, ffn, P, product
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
@@ -156,9 +226,13 @@ class TPMLPStack:
         for l in range(self.L):
             a = x * torch.rsqrt(x.pow(2).mean(dim=-1, keepdim=True) + 1e-6)
             xs = replicate(group, a)
-            partials = [(torch.nn.functional.gelu(xs[r] @ self.w1[l][r]) @ self.w2[l][r]).to(torch.bfloat16)
-                        for r in range(self.P)]
-            x = x + reduce_forward(group, [p.reshape(-1) for p in partials], x.shape)
+            hs = [torch.nn.functional.gelu(xs[r] @ self.w1[l][r]) for r in range(self.P)]
+            if self.product == "f32":
+                partials = [(hs[r] @ self.w2[l][r]).to(torch.bfloat16) for r in range(self.P)]
+                y = reduce_forward(group, [p.reshape(-1) for p in partials], x.shape)
+            else:
+                y = row_parallel_echo(group, hs, self.w2[l], x.shape, self.product == "bf16_fused")
+            x = x + y
         return x
 
 

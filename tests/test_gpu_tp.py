@@ -64,3 +64,40 @@ def test_tp_step_errors_against_exact_allreduce(cuda):
         print(f"{mode}: loss rel err {e_loss:.2e}, dL/dx0 rel err {e_dx:.3e}, worst dL/dW rel err {e_dw:.3e}",
               flush=True)
         assert e_loss < 0.05 and e_dx < 0.5 and e_dw < 0.5
+
+
+def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda):
+    """Row-parallel products in bfloat16 on libecho's kernel: with stage 1 in the
+    product's epilogue the whole training step (loss, input and weight
+    gradients) is bit-identical to the product written out and reduced by
+    echo_reduce, and every reduction matches the oracle run on the partials the
+    written-out product gives (teacher-forced, one oracle state per direction)."""
+    import torch
+    import error_compensated_bit_echo_amd as E
+    from error_compensated_bit_echo_amd import tp
+    res = {}
+    for prod in ("bf16_fused", "bf16"):
+        model = tp.TPMLPStack(L, H, F, P, seed=11, device=cuda, product=prod)
+        g = torch.Generator(device=cuda)
+        g.manual_seed(12)
+        x0 = torch.randn(T, H, generator=g, device=cuda)
+        target = torch.randn(T, H, generator=g, device=cuda)
+        group = tp.EchoGroup(P, T * H, mode="echo", device=cuda, record=(prod == "bf16_fused"))
+        res[prod] = (tp.train_step(model, group, x0, target), group)
+    (lf, dxf, dwf), gf = res["bf16_fused"]
+    (lu, dxu, dwu), _ = res["bf16"]
+    assert torch.equal(lf, lu) and torch.equal(dxf, dxu)
+    assert all(torch.equal(a, b) for a, b in zip(dwf, dwu))
+
+    st = eo.OracleState(T * H)
+    assert [d for d, _, _ in gf.log] == [0] * L + [1] * L
+    for k, (d, parts, out) in enumerate(gf.log):
+        if d == 0:
+            tag, A, W = parts
+            assert tag == "product"
+            written = [torch.empty(T, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
+            E.echo_gemm_bf16(A, W, written)
+            parts = written
+        host = np.stack([p.reshape(-1).float().cpu().numpy() for p in parts])
+        o = eo.echo_call(host, st, d)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), o["out"].view(np.uint32)), f"call {k} dir {d}"
