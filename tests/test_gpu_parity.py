@@ -100,8 +100,13 @@ def _special_values(P, N, rng):
     return g.reshape(P, N)
 
 
+EDGE_VARIANTS = [{}, {"own_exact": True, "out_bf16": True},
+                 {"state_bf16": True, "sender_feedback": True, "group": 64}]
+
+
+@pytest.mark.parametrize("variant", range(len(EDGE_VARIANTS)))
 @pytest.mark.parametrize("case", ["ties", "special", "one_group", "fewer_groups_than_ranks"])
-def test_edge_cases(cuda, case):
+def test_edge_cases(cuda, case, variant):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     rng = np.random.default_rng(5)
@@ -113,14 +118,18 @@ def test_edge_cases(cuda, case):
         P, N, gen = 2, 32, lambda P, N, r: r.standard_normal((P, N)).astype(F32)
     else:
         P, N, gen = 16, 32 * 5, lambda P, N, r: r.standard_normal((P, N)).astype(F32)
-    st = _state(P, N, "f32")
+    kw = EDGE_VARIANTS[variant]
+    if N % kw.get("group", 32):
+        N = 2 * N if case == "one_group" else N + 32  # whole groups of 64
+    st = _state(P, N, "f32", **kw)
     so = eo.OracleState(N)
-    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    out = _out_tensor(st, cuda)
     for t in range(6):
         x = gen(P, N, rng)
         E.echo_reduce(_upload(x, "f32", cuda), out, st, E.ECHO_FWD)
-        o = eo.echo_call(x, so, eo.FWD)
-        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
+        o = eo.echo_call(x, so, eo.FWD, **kw)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} {kw} call {t}",
+                        own_exact=kw.get("own_exact", False)) == 0
 
 
 def test_empty_message_is_a_no_op(cuda):
