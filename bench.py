@@ -497,10 +497,27 @@ def gemm_report(E, torch, dev) -> dict:
     return {"config": "gemm", "shapes": res}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(parts, n_sample: int, **variant) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
     the first ``n_sample`` elements of each of the benchmark's own partials
-    (``variant``: the oracle's switches of the benchmarked configuration)."""
+    (``variant``: the oracle's switches of the benchmarked configuration).
+    Then the same oracle run by a pool of threads, one call each over
+    independent group-aligned windows of twice that sample (numpy releases the
+    interpreter lock inside its array loops; windows are exact because groups
+    and compensator elements are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     from oracle import echo_oracle as eo
 
@@ -511,16 +528,36 @@ def cpu_baseline(parts, n_sample: int, **variant) -> dict:
     eo.echo_call(vals, st, eo.FWD, **variant)
     dt = time.perf_counter() - t0
     del vals
+
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    nthr = max(1, min(16, ncpu))
+    win = (2 * n_sample) // nthr // 128 * 128
+    wins = [np.stack([p[i * win:(i + 1) * win].float().cpu().numpy() for p in parts]) for i in range(nthr)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=nthr) as ex:
+        list(ex.map(lambda w: eo.echo_call(w, eo.OracleState(win), eo.FWD, **variant), wins))
+    dt_par = time.perf_counter() - t0
+    del wins
+    what = ', '.join(f'{k}={v}' for k, v in variant.items()) or 'compensation on'
     return {
         "value": round(P * 2 * n_sample / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"one call, P={P} x the first {n_sample} elements of each rank's partial "
-                  f"({n_sample / 536870912:.4g} of the 1 GiB message), "
-                  f"{', '.join(f'{k}={v}' for k, v in variant.items()) or 'compensation on'}, fresh state; {dt:.2f} s; numpy "
-                  f"elementwise ops on one core ({platform.processor() or platform.machine()}, "
-                  f"os.cpu_count()={os.cpu_count()})",
+                  f"({n_sample / 536870912:.4g} of the 1 GiB message), {what}, fresh state; {dt:.2f} s; numpy "
+                  f"elementwise ops on one core ({_cpu_model()}, os.cpu_count()={os.cpu_count()}, "
+                  f"affinity {ncpu})",
+        "threads": {
+            "value": round(P * 2 * win * nthr / dt_par / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthr,
+            "sample": f"{nthr} threads, one oracle call each on a window of {win} elements per rank "
+                      f"(the first {win * nthr} elements), {what}; {dt_par:.2f} s",
+        },
     }
 
 
