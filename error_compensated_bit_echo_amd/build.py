@@ -74,6 +74,24 @@ def build_library(verbose: bool = False, jobs: int = 0) -> str:
     return LIB
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "echo_c_client.c")
+C_CLIENT = os.path.join(ROOT, "tests", "c_client", "echo_c_client")
+
+
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain C test client of the C ABI (gcc, strict C11) against
+    the built libecho.so and the HIP runtime; returns its path."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", "-isystem", os.path.join(rocm, "include"),
+           C_CLIENT_SRC, f"-L{PKG}", "-lecho", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../error_compensated_bit_echo_amd",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_CLIENT]
+    _run(cmd, verbose)
+    return C_CLIENT
+
+
 if __name__ == "__main__":
     path = build_library(verbose="-v" in sys.argv)
     print(path)
+    print(build_c_client(verbose="-v" in sys.argv))

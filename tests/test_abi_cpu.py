@@ -137,3 +137,35 @@ def test_product_entry_point_rejects_bad_shapes_without_touching_the_gpu():
     misaligned = (ctypes.c_void_p * 2)(4096 + 2, 8192)
     assert lib.echo_gemm_bf16(misaligned, fake, outs, 2, 128, 64, 128, None) == B.ECHO_ERR_ARG
     assert lib.echo_gemm_stage1(fake, fake, 128, 64, None, None) == B.ECHO_ERR_STATE
+
+
+def test_header_is_strict_c_and_matches_the_binding_layout(tmp_path):
+    """include/echo.h compiles as strict C99 and C11 (gcc -pedantic -Werror) and its
+    structs have the sizes and offsets the Python binding assumes."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    src = tmp_path / "h.c"
+    src.write_text("""
+#include <stddef.h>
+#include "echo.h"
+_Static_assert(sizeof(echo_config) == %d, "echo_config size");
+_Static_assert(offsetof(echo_config, numel) == %d, "numel");
+_Static_assert(offsetof(echo_config, sender_feedback) == %d, "sender_feedback");
+_Static_assert(offsetof(echo_config, state_bf16) == %d, "state_bf16");
+_Static_assert(offsetof(echo_config, out_bf16) == %d, "out_bf16");
+_Static_assert(offsetof(echo_config, own_exact) == %d, "own_exact");
+_Static_assert(sizeof(echo_views) == %d, "echo_views size");
+_Static_assert(offsetof(echo_views, sender_err_stride) == %d, "sender_err_stride");
+int main(void) { return 0; }
+""" % (ctypes.sizeof(B.EchoConfig), B.EchoConfig.numel.offset, B.EchoConfig.sender_feedback.offset,
+       B.EchoConfig.state_bf16.offset, B.EchoConfig.out_bf16.offset, B.EchoConfig.own_exact.offset,
+       ctypes.sizeof(B.EchoViews), B.EchoViews.sender_err_stride.offset))
+    subprocess.run([gcc, "-std=c11", "-pedantic", "-Wall", "-Wextra", "-Werror", f"-I{inc}", "-fsyntax-only",
+                    str(src)], check=True, capture_output=True)
+    c99 = tmp_path / "h99.c"
+    c99.write_text('#include "echo.h"\nint main(void) { return 0; }\n')
+    subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", f"-I{inc}", "-fsyntax-only",
+                    str(c99)], check=True, capture_output=True)
