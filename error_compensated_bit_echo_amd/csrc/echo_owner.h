@@ -190,9 +190,12 @@ __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
     owner_tile<P, COMP, POL, LPG, SB16, OWN, U, false>(a, cb + threadIdx.x);
 }
 
-// Cache policy of the owner's accesses, chosen by measurement: plain loads and
-// stores (non-temporal compensator loads made the kernel 14 % slower).
-constexpr int kOwnerPol = 0;
+// Cache policy of the owner's accesses, chosen by measuring the whole call
+// (stage 1, owner, decode back to back, 1 GiB at P = 8): non-temporal loads of
+// the stage-1 codes and non-temporal stores of the broadcast codes and of the
+// estimates, plain loads of the estimates (non-temporal ones made the kernel
+// 14 % slower).  Against plain accesses the owner takes 2.12 instead of 2.19 ms.
+constexpr int kOwnerPol = kNtIn | kNtOut | kNtStateSt;
 
 // Chunks per lane, chosen by measurement (1 GiB messages at P = 2, 4 and 8,
 // 512 MiB at P = 16): two is within 1 % of the best everywhere and up to 5 %
