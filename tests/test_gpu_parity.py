@@ -310,11 +310,11 @@ def test_wire_bytes_match_the_oracle(cuda):
 # sampled group-aligned windows (the numerics are independent per group and the
 # state per element, so a window of the oracle equals that window of the tensor)
 # ---------------------------------------------------------------------------
-def _windows(N, n_win, width, seed):
+def _windows(N, n_win, width, seed, align=32):
     rng = np.random.default_rng(seed)
-    starts = {0, N - width}
+    starts = {0, (N - width) // align * align}
     while len(starts) < n_win:
-        starts.add(int(rng.integers(0, (N - width) // 32)) * 32)
+        starts.add(int(rng.integers(0, (N - width) // align)) * align)
     return sorted(starts)
 
 
@@ -327,7 +327,7 @@ def _window_segments(N, P, group, w, width):
 
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
                   P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
-                  out_bf16=False, own_exact=False, extra_windows=()):
+                  out_bf16=False, own_exact=False, extra_windows=(), group=32):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
     value distribution and dtype); extra_windows adds group-aligned window starts."""
@@ -337,12 +337,12 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     P = c["P"] if P is None else P
     N = synth.numel(cfg_id) if N is None else N
     st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback,
-                state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact)
+                state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group)
     out = _out_tensor(st, cuda)
-    wins = sorted(set(_windows(N, n_win, width, cfg_id)) | set(extra_windows))
+    wins = sorted(set(_windows(N, n_win, width, cfg_id, align=group)) | set(extra_windows))
     if own_exact:  # add a window on every segment boundary
-        per = eo.owner_segments(N // 32, P)
-        wins = sorted(set(wins) | {max(0, min(N - width, g0 * 32 - width // 2)) // 32 * 32
+        per = eo.owner_segments(N // group, P)
+        wins = sorted(set(wins) | {max(0, min(N - width, g0 * group - width // 2)) // group * group
                                    for g0, _ in per[1:]})
     so = {w: eo.OracleState(width) for w in wins}
     parts = None
@@ -355,8 +355,8 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
             for w in wins:
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
                 o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
-                                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact,
-                                 segments=_window_segments(N, P, 32, w, width) if own_exact else None)
+                                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group,
+                                 segments=_window_segments(N, P, group, w, width) if own_exact else None)
                 g = _fetch(st, out, d, w, w + width)
                 assert _compare(g, o, so[w], d, compensate,
                                 f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}", own_exact) == 0
@@ -383,6 +383,13 @@ def test_largest_rank_count_large_message(cuda):
 def test_fp32_partials_of_2GiB(cuda):
     """fp32 partials of 2^29 elements (2 GiB each, so byte offsets pass 2^31)."""
     _windowed_run(cuda, 1, 3, (0,), P=2, N=1 << 29, n_win=8, width=1 << 14)
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_larger_groups_full_size(cuda, group):
+    """The group-size variants at the prefill size, where every kernel takes its
+    two-chunks-per-lane launch (small messages take one)."""
+    _windowed_run(cuda, 2, 4, (0,), group=group)
 
 
 def test_full_size_without_compensation(cuda):
