@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libecho.so")
-SOURCES = ["echo_kernels.hip", "echo_owner_p1_4.hip", "echo_owner_p5_8.hip", "echo_owner_p9_12.hip",
-           "echo_owner_p13_16.hip", "echo_gemm.hip", "echo_api.hip"]
+SOURCES = ["echo_kernels.hip"] + [f"echo_owner_p{lo}_{lo + 1}.hip" for lo in range(1, 17, 2)] + \
+    ["echo_gemm.hip", "echo_api.hip"]
 HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h", "echo_device.h", "echo_owner.h"]
 ARCH = "gfx950"
 
@@ -60,7 +60,7 @@ def build_library(verbose: bool = False, jobs: int = 0) -> str:
         objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
         cmds = [[cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, s), "-o", o]
                 for s, o in zip(SOURCES, objs)]
-        jobs = jobs or min(len(cmds), os.cpu_count() or 1, 8)
+        jobs = jobs or min(len(cmds), os.cpu_count() or 1, 16)
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()

@@ -24,6 +24,7 @@ struct echo_state {
   int64_t err_floats;           // floats per sender-error vector (padded)
   float* sender_err[2];         // sender feedback: rank r of direction d at
                                 // sender_err[d] + r * err_floats; nullptr when off
+  bool streaming;               // the cache policy of the calls (echo::streaming_call)
 };
 
 namespace {
@@ -132,7 +133,8 @@ echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hip
   a.err = st->sender_err[dir];
   a.err_stride = st->err_floats;
   a.own_chunks = st->cfg.own_exact ? segment_chunks(st->cfg) : 0;
-  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, s) == hipSuccess
+  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, st->streaming, s) ==
+                 hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
@@ -157,6 +159,7 @@ echo_status run_owner(const void* const* partials, echo_state* st, int dir, hipS
   a.beta_slow = st->cfg.beta_slow;
   a.omega_slow = 1.0f - st->cfg.beta_slow;
   a.out_bf16 = st->cfg.out_bf16;
+  a.streaming = st->streaming ? 1 : 0;
   if (st->cfg.own_exact) {
     a.own_bf16 = st->cfg.dtype == ECHO_BF16;
     a.own_chunks = segment_chunks(st->cfg);
@@ -170,7 +173,7 @@ echo_status run_owner(const void* const* partials, echo_state* st, int dir, hipS
 
 echo_status run_decode(void* out, const echo_state* st, hipStream_t s) {
   return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, st->cfg.group,
-                             st->cfg.out_bf16 != 0, s) == hipSuccess
+                             st->cfg.out_bf16 != 0, st->streaming, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
@@ -199,6 +202,7 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
   if (st == nullptr) return ECHO_ERR_ARG;
   st->cfg = *cfg;
   st->device = dev;
+  st->streaming = echo::streaming_call(cfg->P, cfg->numel, cfg->dtype == ECHO_BF16);
   st->ws = static_cast<char*>(workspace);
   st->ws_bytes = ws_bytes;
   if (cfg->numel > 0) {

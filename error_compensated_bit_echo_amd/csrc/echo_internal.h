@@ -40,26 +40,41 @@ struct OwnerArgs {
   int64_t own_chunks;            // own_exact: chunks per owner segment (owner of chunk c
                                  // is min(c / own_chunks, P - 1)); 0 when off
   const void* own_src[kMaxRanks];  // own_exact: the rank partials
+  int32_t streaming;             // 1: the streaming cache policy (non-temporal codes and
+                                 // estimate stores); 0: every access plain
 };
 
+// streaming: a call whose data does not stay in the last-level cache between the
+// stages (launch_stage1, launch_decode and OwnerArgs::streaming pick the cache
+// policy from it)
+bool streaming_call(int P, int64_t numel, bool bf16_input);
 // group: 32, 64 or 128 elements per scale
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s);
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, bool streaming,
+                         hipStream_t s);
 // state_bf16: m_fast / m_slow hold bfloat16 (the variant), else fp32;
 // own_exact: a.own_src / a.own_chunks are set
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
                         bool own_exact, hipStream_t s);
-// the owner launches by rank count, one compilation unit each (echo_owner_p*.hip)
-hipError_t launch_owner_p1_4(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+// the owner launches by rank count, two per compilation unit (echo_owner_p*.hip)
+hipError_t launch_owner_p1_2(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
                              bool own_exact, hipStream_t s);
-hipError_t launch_owner_p5_8(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+hipError_t launch_owner_p3_4(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
                              bool own_exact, hipStream_t s);
-hipError_t launch_owner_p9_12(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
-                              bool own_exact, hipStream_t s);
-hipError_t launch_owner_p13_16(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
-                               bool own_exact, hipStream_t s);
+hipError_t launch_owner_p5_6(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p7_8(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p9_10(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p11_12(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p13_14(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
+hipError_t launch_owner_p15_16(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
+                             bool own_exact, hipStream_t s);
 // out: N fp32, or N bfloat16 when out_bf16
 hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out,
-                         int64_t numel, int group, bool out_bf16, hipStream_t s);
+                         int64_t numel, int group, bool out_bf16, bool streaming, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
 // The producing product partial_r = bf16(A_r * W_r^T) of every rank (A_r [M, K],

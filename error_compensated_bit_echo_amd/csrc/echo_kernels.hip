@@ -214,13 +214,18 @@ __global__ __launch_bounds__(kBlock) void echo_zero_k(float* __restrict__ p, int
 }
 
 // Tuning of the launches (unroll and cache policy), chosen by measurement of
-// the whole call (the kernels back to back, as a call runs them).  The decode
-// stores plainly: right after the owner, its non-temporal stores took 0.44 ms
-// against 0.39 (alone, the two are within 2 %).
+// the whole call (the kernels back to back, as a call runs them).  Two cache
+// policies: streaming calls read the partials and write the stage-1 payload
+// non-temporally and the decode stores plainly (right after a streaming owner,
+// non-temporal decode stores took 0.44 ms against 0.39 at 1 GiB, P = 8); calls
+// whose data stays in the last-level cache between the stages run stage 1 and
+// the owner plain, so that the owner finds the payload in the cache, and the
+// decode stores non-temporally.
 constexpr int kStage1Unroll = 2;
 constexpr int kStage1Pol = kNtIn | kNtOut;
 constexpr int kDecodeUnroll = 2;
-constexpr int kDecodePol = 0;
+constexpr int kDecodePolStreaming = 0;
+constexpr int kDecodePolCached = kNtOut;
 
 template <int U, int POL = kStage1Pol, int LPG = 4, bool SFB = false>
 hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
@@ -236,18 +241,23 @@ hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
 // Small messages take one chunk per lane: when two per lane would launch fewer
 // than 1024 blocks over all ranks (four per CU), one per lane is faster (at
 // P = 8, 2^18 elements: 2.9 us against 3.5).
-template <int LPG>
-hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
+template <int LPG, int POL>
+hipError_t stage1_gp(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock * kStage1Unroll - 1) / (kBlock * kStage1Unroll) * P;
   if (blocks < 1024) {
-    if (a.err != nullptr) return stage1_u<1, kStage1Pol, LPG, true>(a, P, bf16, s);
-    return stage1_u<1, kStage1Pol, LPG, false>(a, P, bf16, s);
+    if (a.err != nullptr) return stage1_u<1, POL, LPG, true>(a, P, bf16, s);
+    return stage1_u<1, POL, LPG, false>(a, P, bf16, s);
   }
-  if (a.err != nullptr) return stage1_u<kStage1Unroll, kStage1Pol, LPG, true>(a, P, bf16, s);
-  return stage1_u<kStage1Unroll, kStage1Pol, LPG, false>(a, P, bf16, s);
+  if (a.err != nullptr) return stage1_u<kStage1Unroll, POL, LPG, true>(a, P, bf16, s);
+  return stage1_u<kStage1Unroll, POL, LPG, false>(a, P, bf16, s);
 }
 
-template <int U, int POL = kDecodePol, int LPG = 4>
+template <int LPG>
+hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, bool streaming, hipStream_t s) {
+  return streaming ? stage1_gp<LPG, kStage1Pol>(a, P, bf16, s) : stage1_gp<LPG, 0>(a, P, bf16, s);
+}
+
+template <int U, int POL, int LPG>
 hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64_t numel,
                     bool out_bf16, hipStream_t s) {
   if (out_bf16) {
@@ -266,41 +276,65 @@ hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64
 
 }  // namespace
 
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, hipStream_t s) {
+// A call whose bytes (stage 1 + owner + decode, group 32) lie between 96 MB and
+// 640 MB keeps the stage-1 payload in the 256 MB last-level cache until the
+// owner reads it if stage 1 and the owner access memory plainly: measured
+// 10-14 % faster there (P = 4 and 8, 100 to 550 MB per call), equal below, and
+// 2-5 % slower above, where streaming wins.
+bool streaming_call(int P, int64_t numel, bool bf16_input) {
+  const double bytes = static_cast<double>(numel) * (P * ((bf16_input ? 2.0 : 4.0) + 0.625) + 21.25);
+  return !(bytes >= 96e6 && bytes <= 640e6);
+}
+
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, bool streaming,
+                         hipStream_t s) {
   switch (group) {
-    case 32: return stage1_g<4>(a, P, bf16, s);
-    case 64: return stage1_g<8>(a, P, bf16, s);
-    case 128: return stage1_g<16>(a, P, bf16, s);
+    case 32: return stage1_g<4>(a, P, bf16, streaming, s);
+    case 64: return stage1_g<8>(a, P, bf16, streaming, s);
+    case 128: return stage1_g<16>(a, P, bf16, streaming, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool sb16,
                         bool own, hipStream_t s) {
-  if (P >= 1 && P <= 4) return launch_owner_p1_4(a, P, compensate, group, sb16, own, s);
-  if (P >= 5 && P <= 8) return launch_owner_p5_8(a, P, compensate, group, sb16, own, s);
-  if (P >= 9 && P <= 12) return launch_owner_p9_12(a, P, compensate, group, sb16, own, s);
-  if (P >= 13 && P <= 16) return launch_owner_p13_16(a, P, compensate, group, sb16, own, s);
-  return hipErrorInvalidValue;
-}
-
-// Below 2^20 elements the decode takes one unit per lane (more blocks, fewer
-// idle CUs); above, two.
-template <int U>
-hipError_t decode_g(const uint32_t* codes, const float* scales, void* out, int64_t numel, int group,
-                    bool out_bf16, hipStream_t s) {
-  switch (group) {
-    case 32: return decode_u<U, kDecodePol, 4>(codes, scales, out, numel, out_bf16, s);
-    case 64: return decode_u<U, kDecodePol, 8>(codes, scales, out, numel, out_bf16, s);
-    case 128: return decode_u<U, kDecodePol, 16>(codes, scales, out, numel, out_bf16, s);
+  switch ((P + 1) / 2) {
+    case 1: return launch_owner_p1_2(a, P, compensate, group, sb16, own, s);
+    case 2: return launch_owner_p3_4(a, P, compensate, group, sb16, own, s);
+    case 3: return launch_owner_p5_6(a, P, compensate, group, sb16, own, s);
+    case 4: return launch_owner_p7_8(a, P, compensate, group, sb16, own, s);
+    case 5: return launch_owner_p9_10(a, P, compensate, group, sb16, own, s);
+    case 6: return launch_owner_p11_12(a, P, compensate, group, sb16, own, s);
+    case 7: return launch_owner_p13_14(a, P, compensate, group, sb16, own, s);
+    case 8: return launch_owner_p15_16(a, P, compensate, group, sb16, own, s);
     default: return hipErrorInvalidValue;
   }
 }
 
+// Below 2^20 elements the decode takes one unit per lane (more blocks, fewer
+// idle CUs); above, two.
+template <int U, int POL>
+hipError_t decode_g(const uint32_t* codes, const float* scales, void* out, int64_t numel, int group,
+                    bool out_bf16, hipStream_t s) {
+  switch (group) {
+    case 32: return decode_u<U, POL, 4>(codes, scales, out, numel, out_bf16, s);
+    case 64: return decode_u<U, POL, 8>(codes, scales, out, numel, out_bf16, s);
+    case 128: return decode_u<U, POL, 16>(codes, scales, out, numel, out_bf16, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int POL>
+hipError_t decode_p(const uint32_t* codes, const float* scales, void* out, int64_t numel, int group,
+                    bool out_bf16, hipStream_t s) {
+  if (numel < (int64_t(1) << 20)) return decode_g<1, POL>(codes, scales, out, numel, group, out_bf16, s);
+  return decode_g<kDecodeUnroll, POL>(codes, scales, out, numel, group, out_bf16, s);
+}
+
 hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out, int64_t numel,
-                         int group, bool out_bf16, hipStream_t s) {
-  if (numel < (int64_t(1) << 20)) return decode_g<1>(codes, scales, out, numel, group, out_bf16, s);
-  return decode_g<kDecodeUnroll>(codes, scales, out, numel, group, out_bf16, s);
+                         int group, bool out_bf16, bool streaming, hipStream_t s) {
+  if (streaming) return decode_p<kDecodePolStreaming>(codes, scales, out, numel, group, out_bf16, s);
+  return decode_p<kDecodePolCached>(codes, scales, out, numel, group, out_bf16, s);
 }
 
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s) {

@@ -190,12 +190,17 @@ __global__ __launch_bounds__(kBlock) void echo_owner_k(const OwnerArgs a) {
     owner_tile<P, COMP, POL, LPG, SB16, OWN, U, false>(a, cb + threadIdx.x);
 }
 
-// Cache policy of the owner's accesses, chosen by measuring the whole call
-// (stage 1, owner, decode back to back, 1 GiB at P = 8): non-temporal loads of
-// the stage-1 codes and non-temporal stores of the broadcast codes and of the
-// estimates, plain loads of the estimates (non-temporal ones made the kernel
-// 14 % slower).  Against plain accesses the owner takes 2.12 instead of 2.19 ms.
-constexpr int kOwnerPol = kNtIn | kNtOut | kNtStateSt;
+// Cache policy of the owner's accesses in streaming calls (OwnerArgs::streaming),
+// chosen by measuring the whole call (stage 1, owner, decode back to back, 1 GiB
+// at P = 8): non-temporal loads of the stage-1 codes and non-temporal stores of
+// the broadcast codes and of the estimates, plain loads of the estimates
+// (non-temporal ones made the kernel 14 % slower).  Against plain accesses the
+// owner takes 2.12 instead of 2.19 ms.  Calls whose data mostly stays in the
+// last-level cache run every access plain.  The policy is a template parameter:
+// a run-time switch between two loads that differ only in their cache hint is
+// merged by the compiler into one plain load.
+constexpr int kOwnerPolStreaming = kNtIn | kNtOut | kNtStateSt;
+constexpr int kOwnerPolCached = 0;
 
 // Chunks per lane, chosen by measurement (1 GiB messages at P = 2, 4 and 8,
 // 512 MiB at P = 16): two is within 1 % of the best everywhere and up to 5 %
@@ -208,7 +213,7 @@ template <int P, bool OWN>
 constexpr int owner_unroll() { return OWN && P > 8 ? 1 : 2; }
 constexpr int64_t kOwnerSmallChunks = int64_t(1) << 18;
 
-template <int P, int LPG, bool OWN, int U, int POL = kOwnerPol>
+template <int P, int LPG, bool OWN, int U, int POL>
 hipError_t owner_pgou(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.nchunk + kBlock * U - 1) / (kBlock * U)));
   // without compensation the state is not touched, so its dtype does not matter
@@ -221,11 +226,17 @@ hipError_t owner_pgou(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int P, int LPG, bool OWN, int POL>
+hipError_t owner_pgop(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
+  constexpr int U = owner_unroll<P, OWN>();
+  if (U == 1 || a.nchunk < kOwnerSmallChunks) return owner_pgou<P, LPG, OWN, 1, POL>(a, comp, sb16, s);
+  return owner_pgou<P, LPG, OWN, U, POL>(a, comp, sb16, s);
+}
+
 template <int P, int LPG, bool OWN>
 hipError_t owner_pgo(const OwnerArgs& a, bool comp, bool sb16, hipStream_t s) {
-  constexpr int U = owner_unroll<P, OWN>();
-  if (U == 1 || a.nchunk < kOwnerSmallChunks) return owner_pgou<P, LPG, OWN, 1>(a, comp, sb16, s);
-  return owner_pgou<P, LPG, OWN, U>(a, comp, sb16, s);
+  if (a.streaming) return owner_pgop<P, LPG, OWN, kOwnerPolStreaming>(a, comp, sb16, s);
+  return owner_pgop<P, LPG, OWN, kOwnerPolCached>(a, comp, sb16, s);
 }
 
 template <int P, int LPG>

@@ -1,14 +1,12 @@
-// Owner-stage launches for 1 to 4 ranks (one of four units, so that the
+// Owner-stage launches for 3 and 4 ranks (one of eight units, so that the
 // instantiations compile in parallel).
 #include "echo_owner.h"
 
 namespace echo {
 
-hipError_t launch_owner_p1_4(const OwnerArgs& a, int P, bool compensate, int group, bool sb16,
+hipError_t launch_owner_p3_4(const OwnerArgs& a, int P, bool compensate, int group, bool sb16,
                           bool own, hipStream_t s) {
   switch (P) {
-    case 1: return owner_p<1>(a, compensate, group, sb16, own, s);
-    case 2: return owner_p<2>(a, compensate, group, sb16, own, s);
     case 3: return owner_p<3>(a, compensate, group, sb16, own, s);
     case 4: return owner_p<4>(a, compensate, group, sb16, own, s);
     default: return hipErrorInvalidValue;
