@@ -235,13 +235,17 @@ def stream_report(name, E, synth, torch, dev, group: int = 32) -> dict:
     graph, _ = _graph_us(E, torch, parts, gout, gst, dirs[-1], 20)
     pl = 0.5 + 4.0 / group
     alg = N * (P * (b_in + pl) + pl * (P + 2) + 4 + 16)
+    ws_bytes = N * (P * b_in + (P + 1) * pl + 8 + 4)
     med = _pct(graph, 0.5)
     return {
         "config": name if group == 32 else f"{name}-g{group}", "group": group,
         "P": P, "numel_per_rank": N, "input_dtype": dtype,
         "payload_bytes_per_element": pl,
         "calls": c["calls"] * len(dirs), "alg_bytes_per_call": int(alg),
-        "cache_resident": bool(alg + P * N * b_in < CACHE_BYTES),
+        # distinct bytes a call touches: partials, the P + 1 payloads, one direction's
+        # two fp32 estimates, the fp32 output
+        "working_set_bytes": int(ws_bytes),
+        "cache_resident": bool(ws_bytes <= CACHE_BYTES),
         "us_per_call": {"eager_events_median": round(_pct(eager, 0.5), 2),
                         "eager_events_p90": round(_pct(eager, 0.9), 2),
                         "eager_wall_back_to_back": round(wall, 2),
