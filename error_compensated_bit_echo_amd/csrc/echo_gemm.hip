@@ -13,13 +13,15 @@
 //
 // Tiling: a block computes a 128 x 128 tile of one rank's [M, H] partial with 4
 // wavefronts, each a 64 x 64 sub-tile of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.
-// K advances 64 at a time through two LDS slabs (rows padded to 72 bf16, which
-// keeps the 16-byte fragment reads free of bank conflicts): while the matrix
-// cores work on one slab, the next is fetched from global memory into
-// registers and then stored into the other slab, so each K step needs one
-// barrier.  (Measured at P = 4, M = 2048, K = 3072, H = 4096: 9 % faster than
-// one slab with two barriers; 256 x 128 tiles, at one wavefront per SIMD, and
-// 128 x 64 tiles were slower.)
+// K advances 64 at a time through two LDS slabs: while the matrix cores work on
+// one slab, the next one streams from global memory straight into the other
+// (global_load_lds_dwordx4: each wavefront instruction fills 1 KiB of LDS, eight
+// 128-byte rows, with no register staging), so each K step needs one barrier.
+// The slabs are unpadded; within a row the 16-byte chunk c of row r sits in slot
+// c ^ ((r / 2) % 8), which spreads the 32 rows a fragment read touches over all
+// LDS banks.  (Measured at P = 4, M = 2048, K = 3072, H = 4096: 11 % faster than
+// staging through registers into padded rows; 256 x 128 tiles, at one wavefront
+// per SIMD, and 128 x 64 tiles were slower.)
 // Lane layout of the 32x32x16 bf16 product (checked on the device): lane l
 // supplies A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8, and
 // accumulator v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
@@ -34,15 +36,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileM = 128, kTileN = 128, kTileK = 64;
-constexpr int kLdsK = kTileK + 8;    // bf16 per LDS row of the A and W slabs
-constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the output tile
+constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the output tile (padded)
 constexpr int kGemmThreads = 256;
-constexpr int kSlab = (kTileM + kTileN) * kLdsK;  // bf16 of one A + W slab
+constexpr int kSlabA = kTileM * kTileK;            // bf16 of one A slab (16 KiB)
+constexpr int kSlab = (kTileM + kTileN) * kTileK;  // bf16 of one A + W slab
 static_assert(2 * kSlab >= kTileM * kLdsN, "the output tile reuses the slabs' LDS");
+// a slab row is 128 bytes; each wavefront loads 4 blocks of 8 rows of A and of W
+static_assert(kTileK == 64 && kTileN == kTileM && kTileM == 4 * 8 * (kGemmThreads / 64),
+              "the slab loads assume 128 x 64 slabs filled by four wavefronts");
+
+// Element offset of (row, 16-byte chunk c) in a swizzled slab of 64-element rows.
+__device__ __forceinline__ int slab_at(int row, int c) { return row * kTileK + 8 * (c ^ ((row >> 1) & 7)); }
 
 template <bool FUSED>
 __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kSlab];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kSlab];
   const int r = blockIdx.z;
   const uint16_t* A = a.A[0];
   const uint16_t* W = a.W[0];
@@ -57,15 +65,20 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTileN;
   const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
 
-  // global -> registers: 4 chunks of 8 bf16 per thread and slab; chunk i is
-  // row (t / 8) + 32 i, columns 8 (t % 8) .. +8 of the K slab
-  u32x4 ra[4], rw[4];
-  const int grow = t >> 3, gcol = (t & 7) * 8;
-  auto fetch = [&](int64_t k0) {
+  // global -> LDS slab `buf`: wavefront w fills the 1 KiB blocks 4w .. 4w+3 of the
+  // A slab and of the W slab; in block i lane l writes slot l, i.e. row 8i + l/8,
+  // slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row
+  const int wave = t >> 6;
+  auto issue = [&](int buf, int64_t k0) {
+    uint16_t* As = lds + buf * kSlab;
+    uint16_t* Ws = As + kSlabA;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(A + (m0 + grow + 32 * i) * K + k0 + gcol);
-      rw[i] = *reinterpret_cast<const u32x4*>(W + (n0 + grow + 32 * i) * K + k0 + gcol);
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * wave + j;
+      const int row = 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      __builtin_amdgcn_global_load_lds(A + (m0 + row) * K + k0 + 8 * c, As + 512 * i, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(W + (n0 + row) * K + k0 + 8 * c, Ws + 512 * i, 16, 0, 0);
     }
   };
   f32x16 acc[2][2];
@@ -76,33 +89,24 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // the fetched slab -> LDS slab `buf` (A rows, then W rows)
-  auto stash = [&](int buf) {
-    uint16_t* As = lds + buf * kSlab;
-    uint16_t* Ws = As + kTileM * kLdsK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(As + (grow + 32 * i) * kLdsK + gcol) = ra[i];
-      *reinterpret_cast<u32x4*>(Ws + (grow + 32 * i) * kLdsK + gcol) = rw[i];
-    }
-  };
-  fetch(0);
-  stash(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
   for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
     const bool more = k0 + kTileK < K;
-    if (more) fetch(k0 + kTileK);  // in flight during the products below
+    // the other slab was last read before the previous barrier, so it is free
+    if (more) issue(cur ^ 1, k0 + kTileK);  // in flight during the products below
     const uint16_t* As = lds + cur * kSlab;
-    const uint16_t* Ws = As + kTileM * kLdsK;
+    const uint16_t* Ws = As + kSlabA;
 #pragma unroll
     for (int ks = 0; ks < kTileK / 16; ++ks) {
-      const int kc = 16 * ks + 8 * (lane >> 5);
+      const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
       bf16x8 af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (64 * wm + 32 * i + (lane & 31)) * kLdsK + kc);
-        bf[i] = *reinterpret_cast<const bf16x8*>(Ws + (64 * wn + 32 * i + (lane & 31)) * kLdsK + kc);
+        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at(64 * wm + 32 * i + (lane & 31), c));
+        bf[i] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(64 * wn + 32 * i + (lane & 31), c));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -110,8 +114,7 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    // the other slab was last read before the previous barrier, so it is free
-    if (more) stash(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the other slab have landed
     __syncthreads();
     cur ^= 1;
   }
