@@ -337,7 +337,8 @@ def tp_report(torch, dev) -> dict:
     per direction) with Echo, Echo without compensation and exact all-reduces
     (fp32 products), and with Echo and the row-parallel products in bfloat16 on
     libecho's kernel, written out or with stage 1 fused into them; errors of the
-    loss and the gradients against the exact fp32 step, and step times."""
+    loss and the gradients against the exact fp32 step, and step times (median
+    of three steps after a warm-up step)."""
     from error_compensated_bit_echo_amd import tp
 
     T, H, F, P, L = 2048, 4096, 16384, 4, 8
@@ -347,30 +348,29 @@ def tp_report(torch, dev) -> dict:
     x0 = torch.randn(T, H, generator=g, device=dev)
     target = torch.randn(T, H, generator=g, device=dev)
     res, ms = {}, {}
+
+    def timed(m, group):
+        """One warm-up step, then the median of three timed steps."""
+        tp.train_step(m, group, x0, target)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            out = tp.train_step(m, group, x0, target)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return out, sorted(times)[1]
+
     for mode in ("exact", "echo", "echo_off"):
-        group = tp.EchoGroup(P, T * H, mode=mode, device=dev)
-        tp.train_step(model, group, x0, target)  # warm-up
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        res[mode] = tp.train_step(model, group, x0, target)
-        b.record()
-        torch.cuda.synchronize()
-        ms[mode] = a.elapsed_time(b)
+        res[mode], ms[mode] = timed(model, tp.EchoGroup(P, T * H, mode=mode, device=dev))
 
     # the row-parallel product in bfloat16 on libecho's kernel, written out then
     # reduced, or with stage 1 in its epilogue (bit-identical results)
     for prod in ("bf16", "bf16_fused"):
         m2 = tp.TPMLPStack(L, H, F, P, seed=21, device=dev, product=prod)
-        group = tp.EchoGroup(P, T * H, mode="echo", device=dev)
-        tp.train_step(m2, group, x0, target)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        res["echo_" + prod] = tp.train_step(m2, group, x0, target)
-        b.record()
-        torch.cuda.synchronize()
-        ms["echo_" + prod] = a.elapsed_time(b)
+        res["echo_" + prod], ms["echo_" + prod] = timed(m2, tp.EchoGroup(P, T * H, mode="echo", device=dev))
         del m2
 
     def rel(x, y):
