@@ -375,6 +375,39 @@ def test_headline_config_full_size(cuda):
     _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=8, width=1 << 15)
 
 
+def test_headline_config_every_group_of_the_first_two_calls(cuda):
+    """1 GiB bf16 per rank, P = 8, the same partials every call: after each of the
+    first two calls every group of the message is checked (both payloads, the
+    output and both estimates), the oracle running on 16 threads over
+    independent windows of 2^23 elements, each with its own state."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    cfg_id = 5
+    c = synth.CONFIGS[cfg_id]
+    P, N = c["P"], synth.numel(cfg_id)
+    W = 1 << 23
+    st = _state(P, N, c["dtype"], poison=False)
+    out = _out_tensor(st, cuda)
+    parts = synth.device_partials(cfg_id, 0, 0, device=cuda)
+    so = {w: eo.OracleState(W) for w in range(0, N, W)}
+
+    def check(w, t):
+        host = np.stack([p[w:w + W].float().cpu().numpy() for p in parts])
+        o = eo.echo_call(host, so[w], 0)
+        g = _fetch(st, out, 0, w, w + W)
+        return _compare(g, o, so[w], 0, True, f"call {t} window {w}")
+
+    for t in range(2):
+        E.echo_reduce(parts, out, st, E.ECHO_FWD)
+        torch.cuda.synchronize()
+        with ThreadPoolExecutor(max_workers=16) as ex:
+            inexact = sum(ex.map(lambda w: check(w, t), sorted(so)))
+        assert inexact == 0
+        print(f"call {t}: all {N // 32} groups ok", flush=True)
+
+
 def test_largest_rank_count_large_message(cuda):
     """P = 16 (the most ranks the library takes), 2^27 bf16 elements per rank."""
     _windowed_run(cuda, 5, 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
