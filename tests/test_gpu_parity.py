@@ -408,6 +408,53 @@ def test_headline_config_every_group_of_the_first_two_calls(cuda):
         print(f"call {t}: all {N // 32} groups ok", flush=True)
 
 
+def _full_run(cuda, cfg_id, calls, directions, W=1 << 21, **variant):
+    """The configuration's first calls at full size, every group checked after each
+    call: the oracle runs on 16 threads over the windows of W elements that tile
+    the message, each with its own state (given the whole message's owner split
+    when the owners keep their own shares)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.CONFIGS[cfg_id]
+    P, N = c["P"], synth.numel(cfg_id)
+    assert N % W == 0
+    st = _state(P, N, c["dtype"], poison=False, **variant)
+    out = _out_tensor(st, cuda)
+    so = {w: eo.OracleState(W) for w in range(0, N, W)}
+    own = variant.get("own_exact", False)
+    group = variant.get("group", 32)
+    for t in range(calls):
+        for d in directions:
+            parts = synth.device_partials(cfg_id, d, t, device=cuda)
+            E.echo_reduce(parts, out, st, d)
+            torch.cuda.synchronize()
+
+            def check(w):
+                host = np.stack([p[w:w + W].float().cpu().numpy() for p in parts])
+                o = eo.echo_call(host, so[w], d, segments=_window_segments(N, P, group, w, W) if own else None,
+                                 **variant)
+                return _compare(_fetch(st, out, d, w, w + W), o, so[w], d, True,
+                                f"cfg{cfg_id} call {t} dir {d} window {w}", own)
+
+            with ThreadPoolExecutor(max_workers=16) as ex:
+                assert sum(ex.map(check, sorted(so))) == 0
+            print(f"cfg{cfg_id} call {t} dir {d}: all {N // group} groups ok", flush=True)
+
+
+def test_prefill_config_every_group(cuda):
+    _full_run(cuda, 2, 3, (0,))
+
+
+def test_training_config_every_group_interleaved(cuda):
+    _full_run(cuda, 4, 2, (0, 1))
+
+
+def test_prefill_config_every_group_with_variants(cuda):
+    _full_run(cuda, 2, 3, (0,), own_exact=True, out_bf16=True, state_bf16=True)
+
+
 def test_largest_rank_count_large_message(cuda):
     """P = 16 (the most ranks the library takes), 2^27 bf16 elements per rank."""
     _windowed_run(cuda, 5, 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
