@@ -35,21 +35,25 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTileM = 128, kTileN = 128, kTileK = 64;
+constexpr int kTileN = 128, kTileK = 64;
 constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the output tile (padded)
 constexpr int kGemmThreads = 256;
-constexpr int kSlabA = kTileM * kTileK;            // bf16 of one A slab (16 KiB)
-constexpr int kSlab = (kTileM + kTileN) * kTileK;  // bf16 of one A + W slab
-static_assert(2 * kSlab >= kTileM * kLdsN, "the output tile reuses the slabs' LDS");
-// a slab row is 128 bytes; each wavefront loads 4 blocks of 8 rows of A and of W
-static_assert(kTileK == 64 && kTileN == kTileM && kTileM == 4 * 8 * (kGemmThreads / 64),
-              "the slab loads assume 128 x 64 slabs filled by four wavefronts");
+// a slab row is 128 bytes; each wavefront loads BM/32 blocks of 8 rows of A and 4 of W
+static_assert(kTileK == 64 && kTileN == 4 * 8 * (kGemmThreads / 64),
+              "the slab loads assume 64-element rows and four wavefronts");
 
 // Element offset of (row, 16-byte chunk c) in a swizzled slab of 64-element rows.
 __device__ __forceinline__ int slab_at(int row, int c) { return row * kTileK + 8 * (c ^ ((row >> 1) & 7)); }
 
-template <bool FUSED>
+// BM: rows of the block tile, 128 (2 x 2 MFMA tiles per wavefront) or 64 (1 x 2,
+// for short products that would otherwise leave CUs without a second block).
+template <int BM, bool FUSED>
 __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
+  static_assert(BM == 128 || BM == 64, "block tile of 128 or 64 rows");
+  constexpr int MI = BM / 64;                      // 32-row MFMA tiles per wavefront
+  constexpr int kSlabA = BM * kTileK;              // bf16 of one A slab
+  constexpr int kSlab = (BM + kTileN) * kTileK;    // bf16 of one A + W slab
+  static_assert(2 * kSlab >= BM * kLdsN, "the output tile reuses the slabs' LDS");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kSlab];
   const int r = blockIdx.z;
   const uint16_t* A = a.A[0];
@@ -61,29 +65,36 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
       W = a.W[i];
     }
   const int64_t K = a.K, H = a.H;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kTileM;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTileN;
   const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
 
-  // global -> LDS slab `buf`: wavefront w fills the 1 KiB blocks 4w .. 4w+3 of the
-  // A slab and of the W slab; in block i lane l writes slot l, i.e. row 8i + l/8,
-  // slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row
+  // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks (BM/32) w ... of the
+  // A slab and 4w .. 4w+3 of the W slab; in block i lane l writes slot l, i.e. row
+  // 8i + l/8, slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row
   const int wave = t >> 6;
   auto issue = [&](int buf, int64_t k0) {
     uint16_t* As = lds + buf * kSlab;
     uint16_t* Ws = As + kSlabA;
+    const int sub = (lane & 7);
+#pragma unroll
+    for (int j = 0; j < BM / 32; ++j) {
+      const int i = (BM / 32) * wave + j;
+      const int row = 8 * i + (lane >> 3);
+      __builtin_amdgcn_global_load_lds(A + (m0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), As + 512 * i,
+                                       16, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = 4 * wave + j;
       const int row = 8 * i + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      __builtin_amdgcn_global_load_lds(A + (m0 + row) * K + k0 + 8 * c, As + 512 * i, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(W + (n0 + row) * K + k0 + 8 * c, Ws + 512 * i, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(W + (n0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), Ws + 512 * i,
+                                       16, 0, 0);
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -102,14 +113,15 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kTileK / 16; ++ks) {
       const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
-      bf16x8 af[2], bf[2];
+      bf16x8 af[MI], bf[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at(64 * wm + 32 * i + (lane & 31), c));
-        bf[i] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(64 * wn + 32 * i + (lane & 31), c));
-      }
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at((BM / 2) * wm + 32 * i + (lane & 31), c));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(64 * wn + 32 * j + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -122,21 +134,21 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
   // the bf16 output tile, row-major in LDS
   uint16_t* Cs = lds;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int row = (BM / 2) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int col = 64 * wn + 32 * j + (lane & 31);
         Cs[row * kLdsN + col] = bf16_rne(acc[i][j][v]);
       }
   __syncthreads();
 
-  // 2048 chunks of 8: thread t takes chunks t + 256 u; a row has 16 chunks, so
-  // the 4 lanes of a quad hold one 32-element group
+  // BM * 16 chunks of 8: thread t takes chunks t + 256 u; a row has 16 chunks,
+  // so the 4 lanes of a quad hold one 32-element group
 #pragma unroll
-  for (int u = 0; u < kTileM * kTileN / 8 / kGemmThreads; ++u) {
+  for (int u = 0; u < BM * kTileN / 8 / kGemmThreads; ++u) {
     const int chunk = t + kGemmThreads * u;
     const int row = chunk >> 4, cc = (chunk & 15) * 8;
     Raw<true> raw;
@@ -162,14 +174,27 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / kTileM),
+namespace {
+
+template <int BM>
+hipError_t gemm_bm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
   if (fused)
-    hipLaunchKernelGGL(echo_gemm_k<true>, grid, dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, true>), grid, dim3(kGemmThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(echo_gemm_k<false>, grid, dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, false>), grid, dim3(kGemmThreads), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// 128-row tiles unless that grid would give the 256 CUs fewer than two blocks
+// each; then 64-row tiles.
+hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+  const int64_t blocks128 = (a.M / kGemmTileM) * (a.H / kTileN) * P;
+  if (blocks128 < 512) return gemm_bm<64>(a, P, fused, s);
+  return gemm_bm<128>(a, P, fused, s);
 }
 
 }  // namespace echo
