@@ -64,6 +64,24 @@ MUTANTS = {
         "e1[r] = np.where(sent, e_new, e1[r])", "e1[r] = e_new"),
     "own segment taken from the next rank": (
         "if own_exact and r == j:", "if own_exact and r == (j + 1) % P:"),
+    "bf16 rounding ties away from zero": (
+        "np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)",
+        "np.ldexp(np.sign(m) * np.floor(np.abs(np.ldexp(m, 8)) + 0.5), e - 8)"),
+    "bf16 subnormal step 2^-134": (
+        "np.rint(x * 2.0 ** 133) * 2.0 ** -133", "np.rint(x * 2.0 ** 134) * 2.0 ** -134"),
+    "reset keeps the sender errors": (
+        "                    self.sender_err[d][:] = 0\n", "                    pass\n"),
+    "absmax without the absolute value": (
+        "a = np.max(np.abs(v), axis=1)", "a = np.max(v, axis=1)"),
+    "dequantization ignores the group size": (
+        "codes = np.asarray(codes, dtype=np.int8).reshape(-1, group)",
+        "codes = np.asarray(codes, dtype=np.int8).reshape(-1, 32)"),
+    "nibble mask drops the sign bit": (
+        "u = c.view(np.uint8) & np.uint8(0x0F)", "u = c.view(np.uint8) & np.uint8(0x07)"),
+    "low nibble not sign-extended": (
+        "out[0::2] = ((lo ^ 8) - 8).astype(np.int8)", "out[0::2] = lo.astype(np.int8)"),
+    "bf16 output not rounded": (
+        "        out = round_to_bf16(out)\n", "        pass\n"),
     "estimate biased by a tiny constant": (
         "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bf * mf[e0:e1] + wf * rr + F32(1e-30)"),
 }

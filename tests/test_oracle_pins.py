@@ -735,3 +735,22 @@ def test_own_exact_window_with_the_message_split_equals_whole_message():
             lo, hi = (g_lo, g_hi) if key == "scales2" else (g_lo * G, g_hi * G)
             assert np.array_equal(o[key], whole[key][lo:hi]), (g_lo, g_hi, key)
         assert np.array_equal(o["q1"], whole["q1"][:, g_lo * G:g_hi * G])
+
+
+def test_reset_clears_the_sender_errors_too():
+    """With sender feedback, a reset makes the next call equal a fresh state's:
+    output, both estimates and every rank's stage-1 error."""
+    P, N = 3, 32 * 20
+    st = eo.OracleState(N)
+    for t in range(3):
+        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        eo.echo_call(x, st, sender_feedback=True)
+    assert np.any(st.sender_err[0] != 0)
+    st.reset(1)
+    fresh = eo.OracleState(N)
+    _, x = synth.host_partials(1, 0, 7, P=P, n=N)
+    a = eo.echo_call(x, st, sender_feedback=True)
+    b = eo.echo_call(x, fresh, sender_feedback=True)
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(st.sender_err[0], fresh.sender_err[0])
+    assert np.array_equal(st.m_slow[0], fresh.m_slow[0])
