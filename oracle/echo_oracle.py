@@ -221,8 +221,9 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
     the last difference exact.  The stage-1 errors then telescope, so the
     accumulated end-to-end error stays bounded too.
 
-    ``state_bf16`` is another variant: the two estimates are stored in
-    bfloat16, i.e. every update m <- fl(fl(beta*m) + fl(omega*r)) is rounded
+    ``state_bf16`` is another variant: the carried state is stored in
+    bfloat16, i.e. every update m <- fl(fl(beta*m) + fl(omega*r)) of the two
+    estimates, and with sender feedback every new stage-1 error e, is rounded
     to the nearest bfloat16 before it is kept.
 
     ``out_bf16`` (a variant): what the ranks receive is the broadcast value
@@ -278,6 +279,8 @@ def echo_call(partials, state: OracleState | None, direction: int = FWD,
         s1[r] = s
         if sender_feedback:
             e_new = xs[r] - dequantize_groups(q, s, group).reshape(-1)
+            if state_bf16:
+                e_new = round_to_bf16(e_new)
             e1[r] = np.where(sent, e_new, e1[r])
 
     # 2.-6. each owner works on its own segment of every rank's payload

@@ -138,7 +138,8 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
     ``partials`` is a list of P lists of Fractions (each a binary32 value);
     ``m_fast``/``m_slow`` are lists of Fractions, updated in place when
     compensating; ``sender_err``, if given, is the P ranks' stage-1 error
-    lists (the sender-feedback variant), updated in place.  ``out_bf16``: the
+    lists (the sender-feedback variant), updated in place (rounded to bfloat16
+    with ``state_bf16``).  ``out_bf16``: the
     ranks receive bf16(B) and the error is measured against it.
     ``own_exact``: the owner of group g (g // ceil(n_groups / P)) adds its own
     input exactly instead of through Q; its own groups are not quantized (codes
@@ -168,8 +169,11 @@ def echo_call(partials, m_fast, m_slow, compensate=True, beta_fast=0.5,
         s1.append(s)
         if sender_err is not None:
             deq = dequantize(q, s, group)
-            sender_err[r][:] = [e if (own_exact and owner(i) == r) else sub(a, b)
-                                for i, (a, b, e) in enumerate(zip(x, deq, sender_err[r]))]
+            new = [sub(a, b) for a, b in zip(x, deq)]
+            if state_bf16:  # variant: the carried state, sender errors included, in bfloat16
+                new = [round_to_bfloat16(e) for e in new]
+            sender_err[r][:] = [e if (own_exact and owner(i) == r) else n
+                                for i, (n, e) in enumerate(zip(new, sender_err[r]))]
     S = []
     for i in range(N):
         acc = None

@@ -82,6 +82,8 @@ MUTANTS = {
         "out[0::2] = ((lo ^ 8) - 8).astype(np.int8)", "out[0::2] = lo.astype(np.int8)"),
     "bf16 output not rounded": (
         "        out = round_to_bf16(out)\n", "        pass\n"),
+    "bf16 state keeps the sender errors in fp32": (
+        "            if state_bf16:\n                e_new = round_to_bf16(e_new)\n", ""),
     "estimate biased by a tiny constant": (
         "mf[e0:e1] = bf * mf[e0:e1] + wf * rr", "mf[e0:e1] = bf * mf[e0:e1] + wf * rr + F32(1e-30)"),
 }

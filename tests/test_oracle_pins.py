@@ -754,3 +754,44 @@ def test_reset_clears_the_sender_errors_too():
     assert np.array_equal(a["out"], b["out"])
     assert np.array_equal(st.sender_err[0], fresh.sender_err[0])
     assert np.array_equal(st.m_slow[0], fresh.m_slow[0])
+
+
+@pytest.mark.parametrize("own", [False, True])
+def test_bf16_state_with_sender_feedback_matches_exact_rationals(own):
+    """With bf16 state the ranks' stage-1 errors are kept in bfloat16 too."""
+    P, N, T = 3, 96, 8
+    st = eo.OracleState(N)
+    mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
+    se = [[Fraction(0)] * N for _ in range(P)]
+    for t in range(T):
+        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        o = eo.echo_call(x, st, sender_feedback=True, state_bf16=True, own_exact=own)
+        e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, sender_err=se, state_bf16=True,
+                         own_exact=own)
+        for r in range(P):
+            assert np.array_equal(st.sender_err[0][r], _as_f32(se[r])), (t, r)
+            assert np.all((st.sender_err[0][r].view(np.uint32) & 0xFFFF) == 0)
+        for key in ("S", "V", "B", "out"):
+            assert np.array_equal(o[key], _as_f32(e[key])), (t, key)
+
+
+def test_bf16_sender_errors_still_bound_the_end_to_end_error():
+    """Rounding the carried stage-1 errors to bfloat16 perturbs the telescoping
+    sum by far less than the stage-1 step: the accumulated end-to-end error
+    still stays flat, close to the fp32-state run."""
+    P, N = 2, 2048
+
+    def run(T, sb16):
+        st = eo.OracleState(N)
+        acc = np.zeros(N, F64)
+        rms = []
+        for t in range(T):
+            _, x = synth.host_partials(1, 0, t, P=P, n=N)
+            o = eo.echo_call(x, st, sender_feedback=True, state_bf16=sb16)
+            acc += o["out"].astype(F64) - eo.plain_sum(x)
+            rms.append(np.sqrt(np.mean(acc ** 2)))
+        return np.array(rms)
+
+    b16, f32 = run(256, True), run(256, False)
+    assert b16[-16:].mean() < 1.3 * b16[:16].mean()
+    assert abs(b16[-1] - f32[-1]) < 0.1 * f32[-1]
