@@ -44,8 +44,8 @@ def algorithmic_bytes(P: int, N: int, b_in: int, compensate: bool, group: int = 
     pl = 0.5 + 4.0 / group                     # payload bytes per element: codes + scales
     sent = (P - 1) * N if own_exact else P * N  # rank elements that pass stage 1
     k1 = sent * (b_in + pl)                    # read partials; write codes + scales
-    if sender_feedback:
-        k1 += sent * 8.0                       # read and write those elements' stage-1 errors
+    if sender_feedback:                        # read and write those elements' stage-1 errors
+        k1 += sent * (4.0 if state_bf16 else 8.0)  # (bfloat16 with the bf16 state)
     if own_exact:                              # P - 1 payload segments and the owner's own partial
         k2 = N * (pl * (P - 1) + b_in + pl)
     else:                                      # read P payload segments; write broadcast payload

@@ -335,7 +335,8 @@ def echo_debug_views(state: EchoState, direction: int = ECHO_FWD) -> dict:
         "m_fast": sl(v.m_fast, sb * N).view(sdt),
         "m_slow": sl(v.m_slow, sb * N).view(sdt),
         # sender feedback: [P, N] stage-1 errors of the ranks for ``direction``
+        # (bfloat16 with the state_bf16 variant)
         "sender_err": None if not v.sender_err else
-        sl(v.sender_err, P * v.sender_err_stride).view(torch.float32)
-        .view(P, v.sender_err_stride // 4)[:, :N],
+        sl(v.sender_err, P * v.sender_err_stride).view(sdt)
+        .view(P, v.sender_err_stride // sb)[:, :N],
     }

@@ -21,9 +21,9 @@ struct echo_state {
   float* m_slow[2];
   float* state_base;            // both directions, contiguous, then the sender errors
   int64_t vec_words;            // 4-byte words per compensator vector (fp32 or bf16, padded)
-  int64_t err_floats;           // floats per sender-error vector (padded)
+  int64_t err_words;            // 4-byte words per sender-error vector (fp32 or bf16, padded)
   float* sender_err[2];         // sender feedback: rank r of direction d at
-                                // sender_err[d] + r * err_floats; nullptr when off
+                                // sender_err[d] + r * err_words; nullptr when off
   bool streaming;               // the cache policy of the calls (echo::streaming_call)
 };
 
@@ -37,7 +37,7 @@ struct Layout {
   size_t codes1_stride, scales1_stride;  // bytes per rank
   size_t off_codes1, off_scales1, off_codes2, off_scales2, off_state, off_sender;
   size_t vec_bytes;                      // one compensator vector (fp32 or bf16), aligned
-  size_t err_bytes;                      // one rank's fp32 sender-error vector, aligned
+  size_t err_bytes;                      // one rank's sender-error vector (fp32 or bf16), aligned
   size_t total;                          // without the base-alignment slack
 };
 
@@ -54,7 +54,7 @@ Layout make_layout(const echo_config& c) {
   L.off_scales2 = L.off_codes2 + align_up(N / 2);
   L.off_state = L.off_scales2 + align_up(scale_bytes);
   L.vec_bytes = align_up((c.state_bf16 ? 2 : 4) * N);
-  L.err_bytes = align_up(4 * N);
+  L.err_bytes = align_up((c.state_bf16 ? 2 : 4) * N);  // bf16 state: all carried state in bf16
   L.off_sender = L.off_state + 4 * L.vec_bytes;
   // sender feedback: every rank's stage-1 error, per direction, after the state
   L.total = L.off_sender + (c.sender_feedback ? 2 * P * L.err_bytes : 0);
@@ -131,7 +131,8 @@ echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hip
   a.scales_stride = st->scales1_stride_bytes / 4;
   a.nchunk = st->cfg.numel / echo::kElemsPerLane;
   a.err = st->sender_err[dir];
-  a.err_stride = st->err_floats;
+  a.err_stride = st->err_words;
+  a.err_bf16 = st->cfg.state_bf16;
   a.own_chunks = st->cfg.own_exact ? segment_chunks(st->cfg) : 0;
   return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, st->streaming, s) ==
                  hipSuccess
@@ -220,15 +221,15 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
     }
     st->state_base = reinterpret_cast<float*>(base + L.off_state);
     st->vec_words = static_cast<int64_t>(L.vec_bytes / 4);
-    st->err_floats = static_cast<int64_t>(L.err_bytes / 4);
-    const int64_t sender_floats = cfg->sender_feedback ? 2 * cfg->P * st->err_floats : 0;
+    st->err_words = static_cast<int64_t>(L.err_bytes / 4);
+    const int64_t sender_words = cfg->sender_feedback ? 2 * cfg->P * st->err_words : 0;
     for (int d = 0; d < 2; ++d)
       st->sender_err[d] = cfg->sender_feedback
-                              ? reinterpret_cast<float*>(base + L.off_sender) + d * cfg->P * st->err_floats
+                              ? reinterpret_cast<float*>(base + L.off_sender) + d * cfg->P * st->err_words
                               : nullptr;
     // the compensator vectors and the sender errors are contiguous: one fill
     // (zero bits are +0 in fp32 and in bf16)
-    if (echo::launch_zero(st->state_base, 4 * st->vec_words + sender_floats,
+    if (echo::launch_zero(st->state_base, 4 * st->vec_words + sender_words,
                           static_cast<hipStream_t>(stream)) != hipSuccess) {
       delete st;
       return ECHO_ERR_HIP;
@@ -365,7 +366,7 @@ echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream) {
     // m_fast[d] and m_slow[d] are adjacent: one fill covers both
     if (echo::launch_zero(st->m_fast[d], 2 * st->vec_words, s) != hipSuccess) return ECHO_ERR_HIP;
     if (st->sender_err[d] != nullptr &&
-        echo::launch_zero(st->sender_err[d], st->cfg.P * st->err_floats, s) != hipSuccess)
+        echo::launch_zero(st->sender_err[d], st->cfg.P * st->err_words, s) != hipSuccess)
       return ECHO_ERR_HIP;
   }
   return ECHO_OK;
@@ -411,7 +412,7 @@ echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out
   out->m_fast = st->m_fast[dir];
   out->m_slow = st->m_slow[dir];
   out->sender_err = st->sender_err[dir];
-  out->sender_err_stride = st->sender_err[dir] != nullptr ? static_cast<size_t>(4 * st->err_floats) : 0;
+  out->sender_err_stride = st->sender_err[dir] != nullptr ? static_cast<size_t>(4 * st->err_words) : 0;
   return ECHO_OK;
 }
 

@@ -20,7 +20,8 @@ struct Stage1Args {
   int64_t scales_stride;       // floats between ranks
   int64_t nchunk;              // N / 8
   float* err;                  // sender feedback: rank r's stage-1 error at err + r * err_stride
-  int64_t err_stride;          // floats between ranks (err == nullptr: no sender feedback)
+  int64_t err_stride;          // 4-byte words between ranks (err == nullptr: no sender feedback)
+  int32_t err_bf16;            // the errors are kept as bfloat16 bits (with the bf16 state), else fp32
   int64_t own_chunks;          // own_exact: chunks per owner segment, rank r skips chunks
                                // [r * own_chunks, (r + 1) * own_chunks); 0: nothing skipped
 };

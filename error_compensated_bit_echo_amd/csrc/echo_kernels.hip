@@ -43,26 +43,29 @@ namespace {
 // Chunks in [skip_lo, skip_hi) are neither read nor written (the rank's own
 // segment when the owner adds its partial exactly); the whole-tile path is only
 // taken by tiles that do not meet that range.
-template <bool BF16, int U, int POL, int LPG, bool SFB, bool FULL>
+// SFB (sender feedback): 0 off; 1 the rank's stage-1 errors are fp32 (32 B per
+// chunk); 2 they are bfloat16 (16 B per chunk), each new error rounded to
+// nearest even before it is kept.
+template <bool BF16, int U, int POL, int LPG, int SFB, bool FULL>
 __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, float* scales,
                                             float* err, int64_t c0, int64_t nchunk,
                                             int64_t skip_lo, int64_t skip_hi) {
   Raw<BF16> raw[U];
-  f32x4 ev[SFB ? U : 1][2];  // sender feedback: the rank's stage-1 error of these elements
+  Raw<SFB == 2> ev[SFB ? U : 1];  // sender feedback: the rank's stage-1 error of these elements
   auto live = [&](int64_t c) { return FULL || (c < nchunk && (c < skip_lo || c >= skip_hi)); };
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
     if (live(c)) {
       raw[u] = load_raw<BF16, (POL & kNtIn) != 0>(src, c);
-      if constexpr (SFB) {
-        ev[u][0] = reinterpret_cast<const f32x4*>(err)[2 * c];
-        ev[u][1] = reinterpret_cast<const f32x4*>(err)[2 * c + 1];
-      }
+      if constexpr (SFB != 0) ev[u] = load_raw<SFB == 2, false>(err, c);
     } else {
 #pragma unroll
       for (int i = 0; i < (BF16 ? 1 : 2); ++i) raw[u].q[i] = u32x4{0u, 0u, 0u, 0u};
-      if constexpr (SFB) ev[u][0] = ev[u][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (SFB != 0) {
+#pragma unroll
+        for (int i = 0; i < (SFB == 2 ? 1 : 2); ++i) ev[u].q[i] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 #pragma unroll
@@ -70,9 +73,11 @@ __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, fl
     const int64_t c = c0 + static_cast<int64_t>(u) * kBlock;
     float v[8];
     widen<BF16>(raw[u], v);
-    if constexpr (SFB) {
+    if constexpr (SFB != 0) {
+      float e[8];
+      widen<SFB == 2>(ev[u], e);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = v[j] + ev[u][j >> 2][j & 3];  // x' = fl(x + e)
+      for (int j = 0; j < 8; ++j) v[j] = v[j] + e[j];  // x' = fl(x + e)
     }
     const float s = echo_div7(group_max<LPG>(absmax8(v)));
     float kf[8];
@@ -80,18 +85,22 @@ __device__ __forceinline__ void stage1_tile(const void* src, uint32_t* codes, fl
     if (live(c)) {
       st<(POL & kNtOut) != 0>(w, codes + c);
       if ((threadIdx.x & (LPG - 1)) == 0) scales[c >> log2i(LPG)] = s;
-      if constexpr (SFB) {
+      if constexpr (SFB != 0) {
         float e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) e[j] = v[j] - kf[j] * s;  // e = x' - fl(q*s), exact
-        reinterpret_cast<f32x4*>(err)[2 * c] = f32x4{e[0], e[1], e[2], e[3]};
-        reinterpret_cast<f32x4*>(err)[2 * c + 1] = f32x4{e[4], e[5], e[6], e[7]};
+        if constexpr (SFB == 2) {
+          reinterpret_cast<u32x4*>(err)[c] = pack_bf16x8(e);
+        } else {
+          reinterpret_cast<f32x4*>(err)[2 * c] = f32x4{e[0], e[1], e[2], e[3]};
+          reinterpret_cast<f32x4*>(err)[2 * c + 1] = f32x4{e[4], e[5], e[6], e[7]};
+        }
       }
     }
   }
 }
 
-template <bool BF16, int U, int POL, int LPG, bool SFB>
+template <bool BF16, int U, int POL, int LPG, int SFB>
 __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) {
   const int r = blockIdx.y;
   const void* src = a.src[0];
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(kBlock) void echo_quant_pack_k(const Stage1Args a) 
     if (r == i) src = a.src[i];
   uint32_t* codes = a.codes + static_cast<int64_t>(r) * a.codes_stride_words;
   float* scales = a.scales + static_cast<int64_t>(r) * a.scales_stride;
-  float* err = SFB ? a.err + static_cast<int64_t>(r) * a.err_stride : nullptr;
+  float* err = SFB != 0 ? a.err + static_cast<int64_t>(r) * a.err_stride : nullptr;
   const int64_t cb = static_cast<int64_t>(blockIdx.x) * (kBlock * U);
   const int64_t ce = cb + kBlock * U;
   const int64_t skip_lo = a.own_chunks * r, skip_hi = skip_lo + a.own_chunks;
@@ -227,7 +236,7 @@ constexpr int kDecodeUnroll = 2;
 constexpr int kDecodePolStreaming = 0;
 constexpr int kDecodePolCached = kNtOut;
 
-template <int U, int POL = kStage1Pol, int LPG = 4, bool SFB = false>
+template <int U, int POL = kStage1Pol, int LPG = 4, int SFB = 0>
 hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock * U - 1) / (kBlock * U);
   const dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(P));
@@ -244,12 +253,15 @@ hipError_t stage1_u(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
 template <int LPG, int POL>
 hipError_t stage1_gp(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
   const int64_t blocks = (a.nchunk + kBlock * kStage1Unroll - 1) / (kBlock * kStage1Unroll) * P;
+  const int sfb = a.err == nullptr ? 0 : (a.err_bf16 ? 2 : 1);
   if (blocks < 1024) {
-    if (a.err != nullptr) return stage1_u<1, POL, LPG, true>(a, P, bf16, s);
-    return stage1_u<1, POL, LPG, false>(a, P, bf16, s);
+    if (sfb == 2) return stage1_u<1, POL, LPG, 2>(a, P, bf16, s);
+    if (sfb == 1) return stage1_u<1, POL, LPG, 1>(a, P, bf16, s);
+    return stage1_u<1, POL, LPG, 0>(a, P, bf16, s);
   }
-  if (a.err != nullptr) return stage1_u<kStage1Unroll, POL, LPG, true>(a, P, bf16, s);
-  return stage1_u<kStage1Unroll, POL, LPG, false>(a, P, bf16, s);
+  if (sfb == 2) return stage1_u<kStage1Unroll, POL, LPG, 2>(a, P, bf16, s);
+  if (sfb == 1) return stage1_u<kStage1Unroll, POL, LPG, 1>(a, P, bf16, s);
+  return stage1_u<kStage1Unroll, POL, LPG, 0>(a, P, bf16, s);
 }
 
 template <int LPG>

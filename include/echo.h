@@ -87,8 +87,9 @@ typedef struct {
   int32_t sender_feedback; /* 1 = variant: every rank also feeds its own stage-1 */
                       /* rounding error into its next call (x' = x + e, e <- x' - */
                       /* fl(q*s), per rank and direction); 0 = off (default)       */
-  int32_t state_bf16; /* 1 = variant: m_fast / m_slow stored in bfloat16 (each   */
-                      /* fp32 update rounded to nearest, ties to even); 0 = fp32  */
+  int32_t state_bf16; /* 1 = variant: m_fast / m_slow (and, with sender_feedback, */
+                      /* the ranks' stage-1 errors) stored in bfloat16, each fp32 */
+                      /* update rounded to nearest, ties to even; 0 = fp32        */
   int32_t out_bf16;   /* 1 = variant: the output is bfloat16, bf16(B) rounded to  */
                       /* nearest even, and the owner's error is measured against */
                       /* it, e = fl(V - bf16(B)), so later calls compensate the  */
@@ -109,7 +110,7 @@ typedef void* echo_stream_t; /* a hipStream_t */
  * compensator vectors of both directions (2 x 2 x 4N B, or 2 x 2 x 2N B with
  * state_bf16) and, with
  * sender_feedback, every rank's stage-1 error for both directions
- * (2 x P x 4N B), plus alignment slack.  Returns 0 for an invalid configuration and for N == 0. */
+ * (2 x P x 4N B, or 2 x P x 2N B with state_bf16), plus alignment slack.  Returns 0 for an invalid configuration and for N == 0. */
 size_t echo_workspace_bytes(const echo_config* cfg);
 
 /* Create a state over a caller-owned device workspace of `ws_bytes` bytes
@@ -204,8 +205,9 @@ typedef struct {
   const float* bcast_scales;   /* N/group fp32                                             */
   void* m_fast;                /* N fp32 (N bf16 with state_bf16), compensator of the dir  */
   void* m_slow;                /* N fp32 (N bf16 with state_bf16)                          */
-  float* sender_err;           /* rank r: (char*)sender_err + r*sender_err_stride, N fp32, */
-  size_t sender_err_stride;    /* the requested direction; NULL without sender_feedback   */
+  void* sender_err;            /* rank r: (char*)sender_err + r*sender_err_stride, N fp32 */
+                               /* (N bf16 with state_bf16), the requested direction;     */
+  size_t sender_err_stride;    /* NULL without sender_feedback                            */
 } echo_views;
 
 echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out);

@@ -56,7 +56,7 @@ def _fetch(state, out, direction, lo=0, hi=None):
         "m_fast": v["m_fast"][lo:hi].float().cpu().numpy(),  # bf16 state widens exactly
         "m_slow": v["m_slow"][lo:hi].float().cpu().numpy(),
         "out": out[lo:hi].float().cpu().numpy(),  # a bf16 output widens exactly
-        "sender_err": None if v["sender_err"] is None else v["sender_err"][:, lo:hi].cpu().numpy(),
+        "sender_err": None if v["sender_err"] is None else v["sender_err"][:, lo:hi].float().cpu().numpy(),
     }
 
 
