@@ -591,8 +591,10 @@ def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
                             f"G={group} P={P} sfb={sfb} call {t} dir {d}") == 0
 
 
-def test_bf16_state_full_size(cuda):
-    _windowed_run(cuda, 2, 6, (0,), state_bf16=True)
+@pytest.mark.parametrize("sfb", [False, True])
+def test_bf16_state_full_size(cuda, sfb):
+    """Prefill size; with sender feedback the ranks' stage-1 errors are bf16 too."""
+    _windowed_run(cuda, 2, 6, (0,), state_bf16=True, sender_feedback=sfb)
 
 
 # ---------------------------------------------------------------------------
