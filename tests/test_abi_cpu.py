@@ -69,6 +69,9 @@ def test_workspace_bytes_formula():
         # bf16 state: four compensator vectors of 2N bytes instead of 4N
         cfg = B.EchoConfig.make(P, N, dt, group=G, state_bf16=True)
         assert _ws(cfg) == want - 4 * al(4 * N) + 4 * al(2 * N)
+        # both: the ranks' stage-1 errors are carried state too, kept in bf16
+        cfg = B.EchoConfig.make(P, N, dt, group=G, state_bf16=True, sender_feedback=True)
+        assert _ws(cfg) == want - 4 * al(4 * N) + 4 * al(2 * N) + 2 * P * al(2 * N)
         # the bf16-output and own-partial variants need no workspace of their own
         cfg = B.EchoConfig.make(P, N, dt, group=G, out_bf16=True, own_exact=True)
         assert _ws(cfg) == want
