@@ -327,10 +327,11 @@ def _window_segments(N, P, group, w, width):
 
 def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
                   P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
-                  out_bf16=False, own_exact=False, extra_windows=(), group=32):
+                  out_bf16=False, own_exact=False, extra_windows=(), group=32, threads=1):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
-    value distribution and dtype); extra_windows adds group-aligned window starts."""
+    value distribution and dtype); extra_windows adds group-aligned window starts;
+    threads > 1 runs the oracle on the windows in parallel (each has its own state)."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     c = synth.CONFIGS[cfg_id]
@@ -352,14 +353,23 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
                 parts = None
                 parts = synth.device_partials(cfg_id, d, t, P=P, n=N, device=cuda)
             E.echo_reduce(parts, out, st, d)
-            for w in wins:
+            torch.cuda.synchronize()
+
+            def check(w):
                 host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
                 o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
                                  state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group,
                                  segments=_window_segments(N, P, group, w, width) if own_exact else None)
                 g = _fetch(st, out, d, w, w + width)
-                assert _compare(g, o, so[w], d, compensate,
-                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}", own_exact) == 0
+                return _compare(g, o, so[w], d, compensate,
+                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}", own_exact)
+
+            if threads > 1:
+                from concurrent.futures import ThreadPoolExecutor
+                with ThreadPoolExecutor(max_workers=threads) as ex:
+                    assert sum(ex.map(check, wins)) == 0
+            else:
+                assert sum(check(w) for w in wins) == 0
         print(f"cfg{cfg_id} P={P} N={N}: call {t} ok", flush=True)
 
 
@@ -372,7 +382,10 @@ def test_training_config_full_size_interleaved(cuda):
 
 
 def test_headline_config_full_size(cuda):
-    _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=8, width=1 << 15)
+    """All 10 calls of the 1 GiB P = 8 message, 16 group-aligned windows of 2^20
+    elements (the first, the last and 14 random ones) checked after every call."""
+    _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=16, width=1 << 20,
+                  threads=16)
 
 
 def test_headline_config_every_group_of_the_first_two_calls(cuda):
