@@ -513,14 +513,54 @@ def _cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(parts, n_sample: int, **variant) -> dict:
+def gpu_first_call_window(E, torch, parts, st, out, n: int) -> dict:
+    """Reset the state, run one call and copy back what it left in the first n
+    elements: both payloads, the output and the forward estimates (fresh state,
+    so the oracle can replay exactly this call on the same window)."""
+    E.echo_reset(st, 3)
+    E.echo_reduce(parts, out, st, E.ECHO_FWD)
+    v = E.echo_debug_views(st, E.ECHO_FWD)
+    torch.cuda.synchronize()
+    G = st.cfg.group
+    return {"codes1": v["codes1"][:, :n // 2].cpu().numpy(), "scales1": v["scales1"][:, :n // G].cpu().numpy(),
+            "codes2": v["codes2"][:n // 2].cpu().numpy(), "scales2": v["scales2"][:n // G].cpu().numpy(),
+            "out": out[:n].float().cpu().numpy(), "m_fast": v["m_fast"][:n].float().cpu().numpy(),
+            "m_slow": v["m_slow"][:n].float().cpu().numpy()}
+
+
+def _parity_check(g: dict, o: dict, st, compensate: bool) -> dict:
+    """The GPU's first call on the sample window against the oracle's: codes and
+    scales of both stages bit-exact; out and the estimates within 1e-5 of the
+    group's broadcast scale (also counted where not bit-identical)."""
+    import numpy as np
+    exact = all(np.array_equal(g[k].view(np.uint8), np.ascontiguousarray(o[k]).view(np.uint8))
+                for k in ("codes1", "scales1", "codes2", "scales2"))
+    s2 = np.repeat(o["scales2"].astype(np.float64), g["out"].size // max(o["scales2"].size, 1))
+    pairs = [("out", o["out"])]
+    if compensate:
+        pairs += [("m_fast", st.m_fast[0]), ("m_slow", st.m_slow[0])]
+    worst, differ = 0.0, 0
+    for k, want in pairs:
+        d = np.abs(g[k].astype(np.float64) - want.astype(np.float64))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            rel = np.where(s2 > 0, d / s2, np.where(d > 0, np.inf, 0.0))
+        worst = max(worst, float(rel.max()) if rel.size else 0.0)
+        differ += int(np.count_nonzero(g[k] != want))
+    return {"elements_per_rank": int(g["out"].size), "codes_and_scales_bit_exact": bool(exact),
+            "max_err_over_group_scale": worst, "floats_not_bit_identical": differ,
+            "pass": bool(exact and worst <= 1e-5)}
+
+
+def cpu_baseline(parts, n_sample: int, gpu_window=None, **variant) -> dict:
     """The CPU oracle, as it stands, timed on one call over a bounded sample:
     the first ``n_sample`` elements of each of the benchmark's own partials
     (``variant``: the oracle's switches of the benchmarked configuration).
     Then the same oracle run by a pool of threads, one call each over
     independent group-aligned windows of twice that sample (numpy releases the
     interpreter lock inside its array loops; windows are exact because groups
-    and compensator elements are independent)."""
+    and compensator elements are independent).  ``gpu_window``: what the
+    GPU's first call from a fresh state left in the same sample window, checked
+    against the timed oracle call."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -530,9 +570,13 @@ def cpu_baseline(parts, n_sample: int, **variant) -> dict:
     vals = np.stack([p[:n_sample].float().cpu().numpy() for p in parts])
     st = eo.OracleState(n_sample)
     t0 = time.perf_counter()
-    eo.echo_call(vals, st, eo.FWD, **variant)
+    o = eo.echo_call(vals, st, eo.FWD, **variant)
     dt = time.perf_counter() - t0
     del vals
+    parity = None
+    if gpu_window is not None:
+        parity = _parity_check(gpu_window, o, st, variant.get("compensate", True))
+    del o
 
     try:
         ncpu = len(os.sched_getaffinity(0))
@@ -563,6 +607,7 @@ def cpu_baseline(parts, n_sample: int, **variant) -> dict:
             "sample": f"{nthr} threads, one oracle call each on a window of {win} elements per rank "
                       f"(the first {win * nthr} elements), {what}; {dt_par:.2f} s",
         },
+        "parity_check": parity,
     }
 
 
@@ -769,7 +814,9 @@ def main():
         variant = {k: v for k, v in (("compensate", comp), ("group", G), ("sender_feedback", SFB),
                                      ("state_bf16", SB16), ("out_bf16", OBF), ("own_exact", OWN))
                    if v != {"compensate": True, "group": 32}.get(k, False)}
-        line["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample, **variant)
+        # the owners' own shares need the whole message's owner split, which a window lacks
+        gw = None if OWN else gpu_first_call_window(E, torch, parts, st, out, args.cpu_sample)
+        line["cpu_baseline"] = cpu_baseline(parts, args.cpu_sample, gpu_window=gw, **variant)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
