@@ -6,8 +6,8 @@
 // to bf16 and sends to the all-reduce.  Here the stage-1 quantization (rit.work
 // blog post "echo-4-bit-gpu-communication", «Как Echo возвращает ошибку в
 // следующие вызовы»: ranks send their segments as 4-bit integers) runs in the
-// product's epilogue: the bf16 tile goes to LDS, not to HBM, and the same
-// per-lane quantizer as the stage-1 kernel turns it into the rank's payload.
+// product's epilogue: the bf16 partial never leaves the registers, and the
+// same quantizer as the stage-1 kernel turns it into the rank's payload.
 // The payload is therefore bit-identical to stage 1 applied to the unfused
 // bf16 partial, which the same kernel writes when asked to.
 //
@@ -36,7 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 128, kTileK = 64;
-constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the output tile (padded)
+constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the written-out tile (padded)
 constexpr int kGemmThreads = 256;
 // a slab row is 128 bytes; each wavefront loads BM/32 blocks of 8 rows of A and 4 of W
 static_assert(kTileK == 64 && kTileN == 4 * 8 * (kGemmThreads / 64),
@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
   constexpr int MI = BM / 64;                      // 32-row MFMA tiles per wavefront
   constexpr int kSlabA = BM * kTileK;              // bf16 of one A slab
   constexpr int kSlab = (BM + kTileN) * kTileK;    // bf16 of one A + W slab
-  static_assert(2 * kSlab >= BM * kLdsN, "the output tile reuses the slabs' LDS");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kSlab];
+  static_assert(2 * kSlab >= BM * kLdsN, "the written-out tile reuses the slabs' LDS");
   const int r = blockIdx.z;
   const uint16_t* A = a.A[0];
   const uint16_t* W = a.W[0];
@@ -124,50 +124,80 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);  // C^T tile
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the other slab have landed
     __syncthreads();
     cur ^= 1;
   }
 
-  // the bf16 output tile, row-major in LDS
-  uint16_t* Cs = lds;
+  // Epilogue straight from the accumulators (no LDS round trip).  The product
+  // is computed transposed, C^T = W * A^T, so lane l of tile (i, j) holds
+  // output row m = (BM/2) wm + 32 i + l % 32 and the 16 columns
+  // h = 64 wn + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4: a group of 32 columns of
+  // one row lives in lanes l and l ^ 32 (16 values each), and each run of 4
+  // consecutive columns in one lane.
+  const int half = lane >> 5;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int64_t m = m0 + (BM / 2) * wm + 32 * i + (lane & 31);
+      const int64_t e = m * H + n0 + 64 * wn + 32 * j;  // first element of the row's group
+      float v[16];  // the bf16-rounded partial, widened
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = (BM / 2) * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = 64 * wn + 32 * j + (lane & 31);
-        Cs[row * kLdsN + col] = bf16_rne(acc[i][j][v]);
+      for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(static_cast<uint32_t>(bf16_rne(acc[i][j][k])) << 16);
+      if constexpr (!FUSED) {
+        // into the row-major LDS tile, 4 columns (8 bytes) per store; written out below
+        const int row = (BM / 2) * wm + 32 * i + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // columns 8q + 4 half .. + 3
+          const uint32_t lo = (__float_as_uint(v[4 * q + 1]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q]) >> 16);
+          const uint32_t hi = (__float_as_uint(v[4 * q + 3]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q + 2]) >> 16);
+          *reinterpret_cast<uint2*>(lds + row * kLdsN + 64 * wn + 32 * j + 8 * q + 4 * half) = make_uint2(lo, hi);
+        }
+      } else {
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) amax = fmaxf(amax, __builtin_fabsf(v[k]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float s = echo_div7(amax);
+        float v0[8], v1[8], kf[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          v0[k] = v[k];
+          v1[k] = v[8 + k];
+        }
+        // w0: columns 4 half + {0..3} (low half-word) and 8 + 4 half + {0..3} (high);
+        // w1: the same plus 16
+        const uint32_t w0 = quantize8(v0, s, kf);
+        const uint32_t w1 = quantize8(v1, s, kf);
+        // code word q of the group holds columns 8q .. 8q + 7, its low half-word from
+        // the lower lane; the lower lane writes words 0 and 1, the upper 2 and 3
+        const uint32_t got = __shfl_xor(half ? w0 : w1, 32);
+        uint2 words;
+        if (half == 0)
+          words = make_uint2((w0 & 0xFFFFu) | (got << 16), (w0 >> 16) | (got & 0xFFFF0000u));
+        else
+          words = make_uint2((got & 0xFFFFu) | (w1 << 16), (got >> 16) | (w1 & 0xFFFF0000u));
+        uint32_t* codes = a.codes + static_cast<int64_t>(r) * a.codes_stride_words;
+        *reinterpret_cast<uint2*>(codes + (e >> 3) + 2 * half) = words;
+        if (half == 0) a.scales[static_cast<int64_t>(r) * a.scales_stride + (e >> 5)] = s;
       }
-  __syncthreads();
-
-  // BM * 16 chunks of 8: thread t takes chunks t + 256 u; a row has 16 chunks,
-  // so the 4 lanes of a quad hold one 32-element group
+    }
+  if constexpr (!FUSED) {
+    // the bf16 tile from LDS to the rank's partial: 16 lanes per 256-byte row
+    __syncthreads();
+    uint16_t* out = a.out[0];
 #pragma unroll
-  for (int u = 0; u < BM * kTileN / 8 / kGemmThreads; ++u) {
-    const int chunk = t + kGemmThreads * u;
-    const int row = chunk >> 4, cc = (chunk & 15) * 8;
-    Raw<true> raw;
-    raw.q[0] = *reinterpret_cast<const u32x4*>(Cs + row * kLdsN + cc);
-    const int64_t e = (m0 + row) * H + n0 + cc;  // element index in the rank's [M, H] partial
-    if constexpr (!FUSED) {
-      uint16_t* out = a.out[0];
+    for (int q = 1; q < kMaxRanks; ++q)
+      if (r == q) out = a.out[q];
 #pragma unroll
-      for (int i = 1; i < kMaxRanks; ++i)
-        if (r == i) out = a.out[i];
-      *reinterpret_cast<u32x4*>(out + e) = raw.q[0];
-    } else {
-      float v[8];
-      widen<true>(raw, v);
-      const float s = echo_div7(group_max<4>(absmax8(v)));
-      float kf[8];
-      const uint32_t w = quantize8(v, s, kf);
-      a.codes[static_cast<int64_t>(r) * a.codes_stride_words + (e >> 3)] = w;
-      if ((t & 3) == 0) a.scales[static_cast<int64_t>(r) * a.scales_stride + (e >> 5)] = s;
+    for (int u = 0; u < BM * kTileN / 8 / kGemmThreads; ++u) {
+      const int chunk = t + kGemmThreads * u;
+      const int row = chunk >> 4, cc = (chunk & 15) * 8;
+      *reinterpret_cast<u32x4*>(out + (m0 + row) * H + n0 + cc) =
+          *reinterpret_cast<const u32x4*>(lds + row * kLdsN + cc);
     }
   }
 }
