@@ -22,7 +22,7 @@ a plain sum (the bf16 wire values added in fp32), for comparison.
 
 The row-parallel product and ``g`` can also run as one step in bfloat16
 (``product="bf16_fused"``): libecho's MFMA product writes each rank's stage-1
-payload straight from its output tile, then the owner and decode stages
+payload straight from its accumulators, then the owner and decode stages
 finish the all-reduce; ``"bf16"`` runs the same product written out followed
 by a whole Echo call, which gives bit-identical results.
 """
