@@ -622,7 +622,8 @@ def main():
     ap.add_argument("--sender-feedback", action="store_true",
                     help="variant: every rank feeds its stage-1 rounding error into its next call")
     ap.add_argument("--bf16-state", action="store_true",
-                    help="variant: the compensator's two estimates stored in bfloat16")
+                    help="variant: the carried state (both estimates and, with sender feedback, the "
+                         "ranks' stage-1 errors) stored in bfloat16")
     ap.add_argument("--out-bf16", action="store_true",
                     help="variant: bfloat16 output, the owner's error measured against it")
     ap.add_argument("--own-exact", action="store_true",
