@@ -24,7 +24,7 @@ struct echo_state {
   int64_t err_words;            // 4-byte words per sender-error vector (fp32 or bf16, padded)
   float* sender_err[2];         // sender feedback: rank r of direction d at
                                 // sender_err[d] + r * err_words; nullptr when off
-  bool streaming;               // the cache policy of the calls (echo::streaming_call)
+  echo::CallPolicy policy;      // the cache policy of the calls (echo::call_policy)
 };
 
 namespace {
@@ -134,7 +134,7 @@ echo_status run_stage1(const void* const* partials, echo_state* st, int dir, hip
   a.err_stride = st->err_words;
   a.err_bf16 = st->cfg.state_bf16;
   a.own_chunks = st->cfg.own_exact ? segment_chunks(st->cfg) : 0;
-  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, st->streaming, s) ==
+  return echo::launch_stage1(a, st->cfg.P, st->cfg.dtype == ECHO_BF16, st->cfg.group, st->policy, s) ==
                  hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
@@ -160,7 +160,7 @@ echo_status run_owner(const void* const* partials, echo_state* st, int dir, hipS
   a.beta_slow = st->cfg.beta_slow;
   a.omega_slow = 1.0f - st->cfg.beta_slow;
   a.out_bf16 = st->cfg.out_bf16;
-  a.streaming = st->streaming ? 1 : 0;
+  a.streaming = st->policy == echo::kCallStreaming ? 1 : 0;
   if (st->cfg.own_exact) {
     a.own_bf16 = st->cfg.dtype == ECHO_BF16;
     a.own_chunks = segment_chunks(st->cfg);
@@ -174,7 +174,7 @@ echo_status run_owner(const void* const* partials, echo_state* st, int dir, hipS
 
 echo_status run_decode(void* out, const echo_state* st, hipStream_t s) {
   return echo::launch_decode(st->codes2, st->scales2, out, st->cfg.numel, st->cfg.group,
-                             st->cfg.out_bf16 != 0, st->streaming, s) == hipSuccess
+                             st->cfg.out_bf16 != 0, st->policy == echo::kCallStreaming, s) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;
 }
@@ -203,7 +203,7 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
   if (st == nullptr) return ECHO_ERR_ARG;
   st->cfg = *cfg;
   st->device = dev;
-  st->streaming = echo::streaming_call(cfg->P, cfg->numel, cfg->dtype == ECHO_BF16);
+  st->policy = echo::call_policy(cfg->P, cfg->numel, cfg->dtype == ECHO_BF16);
   st->ws = static_cast<char*>(workspace);
   st->ws_bytes = ws_bytes;
   if (cfg->numel > 0) {

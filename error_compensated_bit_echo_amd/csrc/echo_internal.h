@@ -45,12 +45,15 @@ struct OwnerArgs {
                                  // estimate stores); 0: every access plain
 };
 
-// streaming: a call whose data does not stay in the last-level cache between the
-// stages (launch_stage1, launch_decode and OwnerArgs::streaming pick the cache
-// policy from it)
-bool streaming_call(int P, int64_t numel, bool bf16_input);
+// Cache policy of a call, from the bytes it touches: streaming (its data does not
+// stay in the last-level cache between the stages), cached (stage 1 and the owner
+// access memory plainly), or cached with the partials read non-temporally.
+// launch_stage1 takes the policy; the owner (OwnerArgs::streaming) and
+// launch_decode only distinguish streaming from the cached two.
+enum CallPolicy { kCallCached = 0, kCallCachedStreamIn = 1, kCallStreaming = 2 };
+CallPolicy call_policy(int P, int64_t numel, bool bf16_input);
 // group: 32, 64 or 128 elements per scale
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, bool streaming,
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, CallPolicy policy,
                          hipStream_t s);
 // state_bf16: m_fast / m_slow hold bfloat16 (the variant), else fp32;
 // own_exact: a.own_src / a.own_chunks are set

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kBlock) void echo_zero_k(float* __restrict__ p, int
 // non-temporal decode stores took 0.44 ms against 0.39 at 1 GiB, P = 8); calls
 // whose data stays in the last-level cache between the stages run stage 1 and
 // the owner plain, so that the owner finds the payload in the cache, and the
-// decode stores non-temporally.
+// decode stores non-temporally; the largest of them also read the partials
+// non-temporally (see call_policy).
 constexpr int kStage1Unroll = 2;
 constexpr int kStage1Pol = kNtIn | kNtOut;
 constexpr int kDecodeUnroll = 2;
@@ -265,8 +266,12 @@ hipError_t stage1_gp(const Stage1Args& a, int P, bool bf16, hipStream_t s) {
 }
 
 template <int LPG>
-hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, bool streaming, hipStream_t s) {
-  return streaming ? stage1_gp<LPG, kStage1Pol>(a, P, bf16, s) : stage1_gp<LPG, 0>(a, P, bf16, s);
+hipError_t stage1_g(const Stage1Args& a, int P, bool bf16, CallPolicy policy, hipStream_t s) {
+  switch (policy) {
+    case kCallStreaming: return stage1_gp<LPG, kStage1Pol>(a, P, bf16, s);
+    case kCallCachedStreamIn: return stage1_gp<LPG, kNtIn>(a, P, bf16, s);
+    default: return stage1_gp<LPG, 0>(a, P, bf16, s);
+  }
 }
 
 template <int U, int POL, int LPG>
@@ -292,18 +297,22 @@ hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64
 // 640 MB keeps the stage-1 payload in the 256 MB last-level cache until the
 // owner reads it if stage 1 and the owner access memory plainly: measured
 // 10-14 % faster there (P = 4 and 8, 100 to 550 MB per call), equal below, and
-// 2-5 % slower above, where streaming wins.
-bool streaming_call(int P, int64_t numel, bool bf16_input) {
+// 2-5 % slower above, where streaming wins.  From 480 MB on, stage 1 also reads
+// the partials non-temporally, so that they do not push the payload out of the
+// cache: 5-6 % faster at 533 and 575 MB per call (P = 4), equal at 466 MB and
+// 3-8 % slower below (P = 2, 4, 8 and 16, graph-replayed calls on one box).
+CallPolicy call_policy(int P, int64_t numel, bool bf16_input) {
   const double bytes = static_cast<double>(numel) * (P * ((bf16_input ? 2.0 : 4.0) + 0.625) + 21.25);
-  return !(bytes >= 96e6 && bytes <= 640e6);
+  if (bytes < 96e6 || bytes > 640e6) return kCallStreaming;
+  return bytes >= 480e6 ? kCallCachedStreamIn : kCallCached;
 }
 
-hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, bool streaming,
+hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, CallPolicy policy,
                          hipStream_t s) {
   switch (group) {
-    case 32: return stage1_g<4>(a, P, bf16, streaming, s);
-    case 64: return stage1_g<8>(a, P, bf16, streaming, s);
-    case 128: return stage1_g<16>(a, P, bf16, streaming, s);
+    case 32: return stage1_g<4>(a, P, bf16, policy, s);
+    case 64: return stage1_g<8>(a, P, bf16, policy, s);
+    case 128: return stage1_g<16>(a, P, bf16, policy, s);
     default: return hipErrorInvalidValue;
   }
 }
