@@ -293,17 +293,20 @@ hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64
 
 }  // namespace
 
-// A call whose bytes (stage 1 + owner + decode, group 32) lie between 96 MB and
-// 640 MB keeps the stage-1 payload in the 256 MB last-level cache until the
-// owner reads it if stage 1 and the owner access memory plainly: measured
-// 10-14 % faster there (P = 4 and 8, 100 to 550 MB per call), equal below, and
-// 2-5 % slower above, where streaming wins.  From 480 MB on, stage 1 also reads
-// the partials non-temporally, so that they do not push the payload out of the
-// cache: 5-6 % faster at 533 and 575 MB per call (P = 4), equal at 466 MB and
-// 3-8 % slower below (P = 2, 4, 8 and 16, graph-replayed calls on one box).
+// Cache policy of a call, from the bytes it touches (stage 1 + owner + decode,
+// group 32).  Between 96 MB and 1.2 GB stage 1 and the owner access memory
+// plainly, so that much of the stage-1 payload is still in the 256 MB
+// last-level cache when the owner reads it: 10-14 % faster than streaming at
+// 100-550 MB per call (P = 4 and 8), equal below 96 MB.  From 480 MB on, stage 1
+// reads the partials non-temporally so that they do not push the payload out
+// of the cache: against all-plain accesses 5-6 % faster at 533-575 MB, equal at
+// 466 MB and 3-8 % slower below; against streaming 7-14 % faster at 666-932 MB,
+// 2-4 % at 1.06-1.11 GB and equal at 1.2-1.33 GB, while streaming is 1-5 %
+// faster from 1.4 GB on (and at 1 GB for P = 16).  P = 2, 4, 8 and 16,
+// graph-replayed calls, each comparison measured on one box.
 CallPolicy call_policy(int P, int64_t numel, bool bf16_input) {
   const double bytes = static_cast<double>(numel) * (P * ((bf16_input ? 2.0 : 4.0) + 0.625) + 21.25);
-  if (bytes < 96e6 || bytes > 640e6) return kCallStreaming;
+  if (bytes < 96e6 || bytes > 1200e6) return kCallStreaming;
   return bytes >= 480e6 ? kCallCachedStreamIn : kCallCached;
 }
 

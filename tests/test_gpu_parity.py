@@ -468,6 +468,14 @@ def test_prefill_config_every_group_with_variants(cuda):
     _full_run(cuda, 2, 3, (0,), own_exact=True, out_bf16=True, state_bf16=True)
 
 
+@pytest.mark.parametrize("P,N", [(4, 14 << 20), (2, 25 << 20), (8, 26 << 20), (8, 29 << 20)])
+def test_cache_policy_boundaries(cuda, P, N):
+    """Message sizes on both sides of the cache-policy switches at 480 MB and
+    1.2 GB per call (466 MB all plain; 695 MB and 1.15 GB with the partials
+    streamed in; 1.28 GB streaming), three calls, sampled windows."""
+    _windowed_run(cuda, 4, 3, (0,), P=P, N=N, n_win=6, width=1 << 16)
+
+
 def test_largest_rank_count_large_message(cuda):
     """P = 16 (the most ranks the library takes), 2^27 bf16 elements per rank."""
     _windowed_run(cuda, 5, 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
