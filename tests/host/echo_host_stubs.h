@@ -1,0 +1,24 @@
+// Record of the launches the C-ABI host code makes when it runs against the
+// host-only stand-ins of echo_host_stubs.cpp.
+#pragma once
+
+#include <vector>
+
+#include "echo_internal.h"
+
+struct HostLaunch {
+  enum Kind { kStage1, kOwner, kDecode, kZero, kGemm } kind;
+  echo::Stage1Args stage1;
+  echo::OwnerArgs owner;
+  echo::GemmArgs gemm;
+  const uint32_t* codes;  // decode: broadcast codes
+  const float* scales;    // decode: broadcast scales
+  void* out;              // decode: output; zero: the filled floats
+  int64_t n;              // decode: elements; zero: floats
+  int P, group;
+  bool flag;              // stage 1: bf16 input; owner: compensate; decode: bf16 output; gemm: fused
+  bool state_bf16, own_exact;
+};
+
+extern std::vector<HostLaunch> g_launches;
+extern int g_device;  // what hipGetDevice reports
