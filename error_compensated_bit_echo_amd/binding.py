@@ -138,11 +138,23 @@ def _check(status: int, what: str):
         raise EchoError(status, what)
 
 
+_raw_stream = None  # torch's getter of the current stream's raw handle, if it has one
+
+
 def _stream_handle(stream, device):
+    """The hipStream_t of ``stream``, or of torch's current stream on ``device``.
+    The current stream is read through torch's raw-handle getter when torch
+    provides it (a twentieth of the time of building a Stream object)."""
+    global _raw_stream
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    if _raw_stream:
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        return ctypes.c_void_p(_raw_stream(index))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
 class EchoState:
@@ -153,6 +165,7 @@ class EchoState:
         self.cfg = cfg
         self.workspace = workspace
         self.device = device
+        self.ptr_array_type = ctypes.c_void_p * cfg.P  # the host array of P device pointers
 
     @property
     def P(self) -> int:
@@ -198,16 +211,17 @@ def echo_init_state(cfg: EchoConfig, workspace=None, stream=None, device=None) -
 def _partials_array(partials: Sequence, state: EchoState):
     import torch
     cfg = state.cfg
+    P, N = cfg.P, cfg.numel
     want = torch.bfloat16 if cfg.dtype == ECHO_BF16 else torch.float32
-    if len(partials) != cfg.P:
-        raise EchoError(ECHO_ERR_ARG, f"expected {cfg.P} partials, got {len(partials)}")
+    if len(partials) != P:
+        raise EchoError(ECHO_ERR_ARG, f"expected {P} partials, got {len(partials)}")
+    dev = state.device
     for t in partials:
         if t.dtype != want:
             raise EchoError(ECHO_ERR_DTYPE, f"partial dtype {t.dtype}, expected {want}")
-        if t.numel() != cfg.numel or not t.is_contiguous() or t.device != state.device:
+        if t.numel() != N or not t.is_contiguous() or t.device != dev:
             raise EchoError(ECHO_ERR_ARG, "partials must be contiguous, numel == N, on the state's device")
-    arr = (ctypes.c_void_p * cfg.P)(*[t.data_ptr() for t in partials])
-    return arr
+    return state.ptr_array_type(*[t.data_ptr() for t in partials])
 
 
 def _out_ptr(out, state: EchoState):
