@@ -628,7 +628,7 @@ def main():
                     help="variant: bfloat16 output, the owner's error measured against it")
     ap.add_argument("--own-exact", action="store_true",
                     help="variant: each owner adds its own partial exactly (not quantized)")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 25,
+    ap.add_argument("--cpu-sample", type=int, default=1 << 26,
                     help="elements per rank in the CPU oracle's timed sample")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle leg")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
