@@ -37,24 +37,51 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTileN = 128, kTileK = 64;
 constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the written-out tile (padded)
-constexpr int kGemmThreads = 256;
-// a slab row is 128 bytes; each wavefront loads BM/32 blocks of 8 rows of A and 4 of W
-static_assert(kTileK == 64 && kTileN == 4 * 8 * (kGemmThreads / 64),
-              "the slab loads assume 64-element rows and four wavefronts");
+static_assert(kTileK == 64, "the slab loads assume 64-element (128-byte) rows");
 
 // Element offset of (row, 16-byte chunk c) in a swizzled slab of 64-element rows.
 __device__ __forceinline__ int slab_at(int row, int c) { return row * kTileK + 8 * (c ^ ((row >> 1) & 7)); }
 
-// BM: rows of the block tile, 128 (2 x 2 MFMA tiles per wavefront) or 64 (1 x 2,
-// for short products that would otherwise leave CUs without a second block).
-template <int BM, bool FUSED>
-__global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
-  static_assert(BM == 128 || BM == 64, "block tile of 128 or 64 rows");
-  constexpr int MI = BM / 64;                      // 32-row MFMA tiles per wavefront
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (lgkm and export counts not waited on):
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15.
+constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier for the slab pipeline.  __syncthreads() would also make
+// every wavefront wait for all its outstanding global loads (its release fence
+// covers the loads that write LDS), which would drain the loads of the later
+// slabs at every step; here each wavefront first waits, with vmcnt_at_most,
+// for the loads of the slab about to be read only.  The empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void slab_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// BM: rows of the block tile; NW: wavefronts, laid out (NW/2) x 2 over the
+// tile, each computing (2 BM / NW) rows x 64 columns; S: LDS slabs in the
+// pipeline (S - 1 K steps of loads in flight while one is multiplied).
+//   128 x 128, 4 wavefronts, 2 slabs (64 KiB): two blocks per CU;
+//   64 x 128, 4 wavefronts, 2 slabs: for short products that would otherwise
+//     leave CUs without a second block;
+//   256 x 128, 8 wavefronts, 2 slabs (96 KiB): one block per CU, half the
+//     slab loads per multiply-add of the 128-row tile (the fastest of these
+//     where M allows it; a third slab, which hides twice the load latency,
+//     measured slower).
+template <int BM, int NW, int S, bool FUSED>
+__global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int RW = 2 * BM / NW;                  // rows per wavefront
+  constexpr int MI = RW / 32;                      // 32-row MFMA tiles per wavefront
+  static_assert(MI == 1 || MI == 2, "one or two 32-row MFMA tiles per wavefront");
+  constexpr int JA = BM / (8 * NW), JW = kTileN / (8 * NW);  // 1 KiB slab blocks per wavefront
+  static_assert(JA * 8 * NW == BM && JW * 8 * NW == kTileN, "slab blocks split evenly");
+  constexpr int kLoads = JA + JW;                  // global loads per wavefront per slab
   constexpr int kSlabA = BM * kTileK;              // bf16 of one A slab
   constexpr int kSlab = (BM + kTileN) * kTileK;    // bf16 of one A + W slab
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kSlab];
-  static_assert(2 * kSlab >= BM * kLdsN, "the written-out tile reuses the slabs' LDS");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[S * kSlab];
+  static_assert(S * kSlab >= BM * kLdsN, "the written-out tile reuses the slabs' LDS");
   const int r = blockIdx.z;
   const uint16_t* A = a.A[0];
   const uint16_t* W = a.W[0];
@@ -69,8 +96,8 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTileN;
   const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
 
-  // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks (BM/32) w ... of the
-  // A slab and 4w .. 4w+3 of the W slab; in block i lane l writes slot l, i.e. row
+  // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks JA w ... of the A
+  // slab and JW w ... of the W slab; in block i lane l writes slot l, i.e. row
   // 8i + l/8, slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row
   const int wave = t >> 6;
   auto issue = [&](int buf, int64_t k0) {
@@ -78,15 +105,15 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
     uint16_t* Ws = As + kSlabA;
     const int sub = (lane & 7);
 #pragma unroll
-    for (int j = 0; j < BM / 32; ++j) {
-      const int i = (BM / 32) * wave + j;
+    for (int j = 0; j < JA; ++j) {
+      const int i = JA * wave + j;
       const int row = 8 * i + (lane >> 3);
       __builtin_amdgcn_global_load_lds(A + (m0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), As + 512 * i,
                                        16, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * wave + j;
+    for (int j = 0; j < JW; ++j) {
+      const int i = JW * wave + j;
       const int row = 8 * i + (lane >> 3);
       __builtin_amdgcn_global_load_lds(W + (n0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), Ws + 512 * i,
                                        16, 0, 0);
@@ -100,14 +127,22 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int cur = 0;
-  for (int64_t k0 = 0; k0 < K; k0 += kTileK) {
-    const bool more = k0 + kTileK < K;
-    // the other slab was last read before the previous barrier, so it is free
-    if (more) issue(cur ^ 1, k0 + kTileK);  // in flight during the products below
+  // K step `it` multiplies slab it % S; the loads of step it + S - 1 are issued
+  // at its start into the slab step it - 1 used, which every wavefront has
+  // finished reading at the barrier that ended step it - 1
+  const int64_t steps = K / kTileK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < steps) issue(s, static_cast<int64_t>(s) * kTileK);
+  if (steps >= S - 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most((S - 2) * kLoads));  // step 0's slab has landed
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+  slab_barrier();
+  for (int64_t it = 0; it < steps; ++it) {
+    const int cur = static_cast<int>(it % S);
+    const bool more = it + S - 1 < steps;
+    if (more) issue(static_cast<int>((it + S - 1) % S), (it + S - 1) * kTileK);  // in flight below
     const uint16_t* As = lds + cur * kSlab;
     const uint16_t* Ws = As + kSlabA;
 #pragma unroll
@@ -116,7 +151,7 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
       bf16x8 af[MI], bf[2];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at((BM / 2) * wm + 32 * i + (lane & 31), c));
+        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at(RW * wm + 32 * i + (lane & 31), c));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         bf[j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(64 * wn + 32 * j + (lane & 31), c));
@@ -126,9 +161,12 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);  // C^T tile
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads into the other slab have landed
-    __syncthreads();
-    cur ^= 1;
+    // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
+    if (more)
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most((S - 2) * kLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    slab_barrier();
   }
 
   // Epilogue straight from the accumulators (no LDS round trip).  The product
@@ -142,14 +180,14 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t m = m0 + (BM / 2) * wm + 32 * i + (lane & 31);
+      const int64_t m = m0 + RW * wm + 32 * i + (lane & 31);
       const int64_t e = m * H + n0 + 64 * wn + 32 * j;  // first element of the row's group
       float v[16];  // the bf16-rounded partial, widened
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(static_cast<uint32_t>(bf16_rne(acc[i][j][k])) << 16);
       if constexpr (!FUSED) {
         // into the row-major LDS tile, 4 columns (8 bytes) per store; written out below
-        const int row = (BM / 2) * wm + 32 * i + (lane & 31);
+        const int row = RW * wm + 32 * i + (lane & 31);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {  // columns 8q + 4 half .. + 3
           const uint32_t lo = (__float_as_uint(v[4 * q + 1]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q]) >> 16);
@@ -193,8 +231,8 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
     for (int q = 1; q < kMaxRanks; ++q)
       if (r == q) out = a.out[q];
 #pragma unroll
-    for (int u = 0; u < BM * kTileN / 8 / kGemmThreads; ++u) {
-      const int chunk = t + kGemmThreads * u;
+    for (int u = 0; u < BM * kTileN / 8 / kThreads; ++u) {
+      const int chunk = t + kThreads * u;
       const int row = chunk >> 4, cc = (chunk & 15) * 8;
       *reinterpret_cast<u32x4*>(out + (m0 + row) * H + n0 + cc) =
           *reinterpret_cast<const u32x4*>(lds + row * kLdsN + cc);
@@ -206,25 +244,29 @@ __global__ __launch_bounds__(kGemmThreads) void echo_gemm_k(const GemmArgs a) {
 
 namespace {
 
-template <int BM>
-hipError_t gemm_bm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+template <int BM, int NW, int S>
+hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
   if (fused)
-    hipLaunchKernelGGL((echo_gemm_k<BM, true>), grid, dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_gemm_k<BM, false>), grid, dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, false>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 128-row tiles unless that grid would give the 256 CUs fewer than two blocks
-// each; then 64-row tiles.
+// 256-row tiles of 8 wavefronts when M allows them, else 128-row tiles, unless
+// 128-row tiles would give the 256 CUs fewer than two blocks each; then 64-row
+// tiles.  Measured at P = 4, M = 2048, K = 3072, H = 4096 (fused / product only,
+// us): 256 rows, 2 slabs 208.2 / 201.4; 128 rows, 2 slabs 214.5 / 204.8; 256 rows,
+// 3 slabs 226.0 / 208.7; 128 rows, 3 slabs (one block per CU) 280.6 / 267.3.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const int64_t blocks128 = (a.M / kGemmTileM) * (a.H / kTileN) * P;
-  if (blocks128 < 512) return gemm_bm<64>(a, P, fused, s);
-  return gemm_bm<128>(a, P, fused, s);
+  if (blocks128 < 512) return gemm_cfg<64, 4, 2>(a, P, fused, s);
+  if (a.M % 256 == 0) return gemm_cfg<256, 8, 2>(a, P, fused, s);
+  return gemm_cfg<128, 4, 2>(a, P, fused, s);
 }
 
 }  // namespace echo
