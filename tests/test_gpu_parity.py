@@ -132,6 +132,46 @@ def test_edge_cases(cuda, case, variant):
                         own_exact=kw.get("own_exact", False)) == 0
 
 
+def _random_configs(n, seed=2026):
+    """n seeded random configurations: rank count, message size (whole groups,
+    often ragged against the 2048-element tiles), group, dtype, betas, and every
+    switch at random."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        group = int(rng.choice([32, 64, 128]))
+        P = int(rng.integers(1, 17))
+        N = group * int(rng.integers(1, 2000))
+        out.append(dict(P=P, N=N, group=group, dtype=str(rng.choice(["bf16", "f32"])),
+                        compensate=bool(rng.random() < 0.8),
+                        beta=(float(np.float32(rng.choice([0.0, 0.25, 0.5, 0.75]))),
+                              float(np.float32(rng.choice([0.5, 0.9, 0.95, 0.99])))),
+                        sender_feedback=bool(rng.random() < 0.4), state_bf16=bool(rng.random() < 0.4),
+                        out_bf16=bool(rng.random() < 0.4), own_exact=bool(rng.random() < 0.4)))
+    return out
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_configurations(cuda, k):
+    """Seeded random combinations of rank count, size, group, dtype, betas and
+    the variants, both directions interleaved, against the oracle every call."""
+    import error_compensated_bit_echo_amd as E
+    c = _random_configs(24)[k]
+    P, N, G, dt = c["P"], c["N"], c["group"], c["dtype"]
+    kw = {key: c[key] for key in ("sender_feedback", "state_bf16", "out_bf16", "own_exact")}
+    st = _state(P, N, dt, c["compensate"], beta=c["beta"], group=G, **kw)
+    so = eo.OracleState(N)
+    out = _out_tensor(st, cuda)
+    for t in range(3):
+        for d in (0, 1):
+            raw, vals = synth.host_partials(4, d, 10 * k + t, P=P, n=N, dtype=dt)
+            E.echo_reduce(_upload(raw, dt, cuda), out, st, d)
+            o = eo.echo_call(vals, so, d, compensate=c["compensate"], beta_fast=c["beta"][0],
+                             beta_slow=c["beta"][1], group=G, **kw)
+            assert _compare(_fetch(st, out, d), o, so, d, c["compensate"], f"{c} call {t} dir {d}",
+                            own_exact=kw["own_exact"]) == 0
+
+
 def test_empty_message_is_a_no_op(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
