@@ -652,6 +652,13 @@ def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
                             f"G={group} P={P} sfb={sfb} call {t} dir {d}") == 0
 
 
+def test_sender_feedback_bf16_state_headline_size(cuda):
+    """1 GiB bf16 per rank, P = 8 (streaming cache policy), sender feedback with
+    the bf16 state: three calls on the same partials, sampled windows."""
+    _windowed_run(cuda, 5, 3, (0,), same_partials=True, n_win=6, width=1 << 16, sender_feedback=True,
+                  state_bf16=True, threads=6)
+
+
 @pytest.mark.parametrize("sfb", [False, True])
 def test_bf16_state_full_size(cuda, sfb):
     """Prefill size; with sender feedback the ranks' stage-1 errors are bf16 too."""
