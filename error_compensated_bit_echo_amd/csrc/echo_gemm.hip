@@ -11,8 +11,10 @@
 // The payload is therefore bit-identical to stage 1 applied to the unfused
 // bf16 partial, which the same kernel writes when asked to.
 //
-// Tiling: a block computes a 128 x 128 tile of one rank's [M, H] partial with 4
-// wavefronts, each a 64 x 64 sub-tile of 2 x 2 v_mfma_f32_32x32x16_bf16 tiles.
+// Tiling: a block computes a 256 x 128 tile of one rank's [M, H] partial with 8
+// wavefronts (128 x 128 with 4 where M is not a multiple of 256, 64 x 128 for
+// short products), each wavefront a 64 x 64 sub-tile of 2 x 2
+// v_mfma_f32_32x32x16_bf16 tiles (32 x 64, 1 x 2, in the 64-row tile).
 // K advances 64 at a time through two LDS slabs: while the matrix cores work on
 // one slab, the next one streams from global memory straight into the other
 // (global_load_lds_dwordx4: each wavefront instruction fills 1 KiB of LDS, eight
@@ -20,8 +22,7 @@
 // The slabs are unpadded; within a row the 16-byte chunk c of row r sits in slot
 // c ^ ((r / 2) % 8), which spreads the 32 rows a fragment read touches over all
 // LDS banks.  (Measured at P = 4, M = 2048, K = 3072, H = 4096: 11 % faster than
-// staging through registers into padded rows; 256 x 128 tiles, at one wavefront
-// per SIMD, and 128 x 64 tiles were slower.)
+// staging through registers into padded rows; 128 x 64 tiles were slower.)
 // Lane layout of the 32x32x16 bf16 product (checked on the device): lane l
 // supplies A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8, and
 // accumulator v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
