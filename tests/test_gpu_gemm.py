@@ -16,9 +16,10 @@ from parity_helpers import _compare, _fetch, _state, _torch
 
 pytestmark = pytest.mark.gpu
 
-# the first four launch 64-row tiles (fewer than 512 blocks of 128 x 128), the last 128-row tiles
+# the first four launch 64-row tiles (fewer than 512 blocks of 128 x 128), the fifth 256-row tiles
+# (M a multiple of 256), the last 128-row tiles (M an odd multiple of 128)
 SHAPES = [(1, 128, 64, 128), (2, 256, 512, 384), (3, 384, 1024, 256), (8, 128, 3072, 512),
-          (2, 2048, 128, 2048)]
+          (2, 2048, 128, 2048), (2, 2176, 192, 2048)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
@@ -78,7 +79,8 @@ def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
         assert np.array_equal(vf["scales1"][r].cpu().numpy().view(np.uint32), s.view(np.uint32))
 
 
-@pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (2, 2048, 128, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (2, 2048, 128, 2048),
+                                     (2, 2176, 128, 2048)])
 def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
