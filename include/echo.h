@@ -32,9 +32,12 @@
  *                            m <- fl(fl(beta*m) + fl((1-beta)*e)) for both;
  *   output:                  out = B (fp32; no third rounding).
  * With compensate == 0 the correction is zero and the state is not touched.
- * Two variants change this chain: out_bf16 delivers bf16(B) and measures
+ * Four variants change this chain: out_bf16 delivers bf16(B) and measures
  * e = fl(V - bf16(B)); own_exact lets the owner of a segment add its own
- * partial x_j in place of d_j (rank j quantizes every segment but its own).
+ * partial x_j in place of d_j (rank j quantizes every segment but its own);
+ * sender_feedback has every rank quantize x + e_r and keep its own stage-1
+ * error e_r <- fl(x + e_r - fl(q*s)) for its next call; state_bf16 keeps all
+ * carried state (both estimates and the ranks' errors) in bfloat16.
  *
  * Conventions for every entry point
  *   - Device pointers point to the memory of the device that was current when
