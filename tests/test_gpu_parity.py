@@ -288,6 +288,47 @@ def test_graph_capture_replays_match_eager(cuda):
         _ = (oe * 2).sum().item()  # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("variant", [{"sender_feedback": True, "state_bf16": True},
+                                     {"own_exact": True, "out_bf16": True, "group": 64},
+                                     {"sender_feedback": True, "compensate": False}])
+def test_graph_capture_of_variants_and_resets(cuda, variant):
+    """A graph holding a forward call, a backward call and a reset of the
+    backward state, replayed 4 times with eager work in between, leaves the same
+    outputs and carried state as the same sequence issued eagerly."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    kw = dict(variant)
+    comp = kw.pop("compensate", True)
+    P, N = 4, 2048 * 9 + 64 * 3
+    raw0, _ = synth.host_partials(4, 0, 1, P=P, n=N)
+    raw1, _ = synth.host_partials(4, 1, 1, P=P, n=N)
+    p0, p1 = _upload(raw0, "bf16", cuda), _upload(raw1, "bf16", cuda)
+    se, sg = _state(P, N, "bf16", comp, **kw), _state(P, N, "bf16", comp, **kw)
+    oe, og = _out_tensor(se, cuda), _out_tensor(sg, cuda)
+    oe1, og1 = _out_tensor(se, cuda), _out_tensor(sg, cuda)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        E.echo_reduce(p0, og, sg, E.ECHO_FWD)
+        E.echo_reduce(p1, og1, sg, E.ECHO_BWD)
+        E.echo_reset(sg, 2)
+    torch.cuda.synchronize()
+    E.echo_reset(sg, 3)  # capture does not execute; start from a fresh state
+    for k in range(4):
+        E.echo_reduce(p0, oe, se, E.ECHO_FWD)
+        E.echo_reduce(p1, oe1, se, E.ECHO_BWD)
+        E.echo_reset(se, 2)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oe, og) and torch.equal(oe1, og1), f"replay {k}"
+        for d in (0, 1):
+            ve, vg = E.echo_debug_views(se, d), E.echo_debug_views(sg, d)
+            for key in ("m_fast", "m_slow", "sender_err"):
+                if ve[key] is not None:
+                    assert torch.equal(ve[key], vg[key]), f"replay {k} dir {d} {key}"
+        _ = (oe * 2).sum().item()  # unrelated eager work between replays
+
+
 # ---------------------------------------------------------------------------
 # argument errors are reported and launch nothing
 # ---------------------------------------------------------------------------
