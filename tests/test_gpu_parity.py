@@ -914,3 +914,53 @@ def test_independent_states_on_two_streams(cuda):
     both = run([torch.cuda.Stream(), torch.cuda.Stream()])
     for a, b in zip(alone[0] + alone[1], both[0] + both[1]):
         assert torch.equal(a, b)
+
+
+def test_states_driven_from_two_host_threads(cuda):
+    """Two host threads, each with its own state and stream, calling the C ABI at
+    the same time, give what the same calls give from one thread."""
+    import threading
+
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, N = 4, 2048 * 17 + 96
+    parts = [_upload(synth.host_partials(4, d, 3, P=P, n=N)[0], "bf16", cuda) for d in (0, 1)]
+
+    def drive(st, out, stream, dirs, log):
+        torch.cuda.set_device(cuda)
+        with torch.cuda.stream(stream):
+            for t in range(20):
+                d = dirs[t % len(dirs)]
+                E.echo_reduce(parts[d], out, st, d, stream=stream)
+                if t % 5 == 4:
+                    E.echo_reset(st, 1 << d, stream=stream)
+            stream.synchronize()
+        log.append(out.clone())
+
+    def run(threaded):
+        sts = [_state(P, N, "bf16", sender_feedback=True), _state(P, N, "bf16", state_bf16=True)]
+        outs = [_out_tensor(st, cuda) for st in sts]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        logs = [[], []]
+        torch.cuda.synchronize()
+        args = [(sts[i], outs[i], streams[i], (0, 1) if i == 0 else (1,), logs[i]) for i in range(2)]
+        if threaded:
+            ths = [threading.Thread(target=drive, args=a) for a in args]
+            for th in ths:
+                th.start()
+            for th in ths:
+                th.join()
+        else:
+            for a in args:
+                drive(*a)
+        torch.cuda.synchronize()
+        views = [[E.echo_debug_views(st, d)[k].clone() for d in (0, 1) for k in ("m_fast", "m_slow")]
+                 for st in sts]
+        return [lg[0] for lg in logs], views
+
+    seq, par = run(False), run(True)
+    for a, b in zip(seq[0], par[0]):
+        assert torch.equal(a, b)
+    for va, vb in zip(seq[1], par[1]):
+        for a, b in zip(va, vb):
+            assert torch.equal(a, b)
