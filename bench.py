@@ -370,6 +370,13 @@ def tp_report(torch, dev) -> dict:
 
     for mode in ("exact", "echo", "echo_off"):
         res[mode], ms[mode] = timed(model, tp.EchoGroup(P, T * H, mode=mode, device=dev))
+    # variants of the all-reduce (fp32 products)
+    variants = {"echo_sender_feedback": {"sender_feedback": True},
+                "echo_own_exact": {"own_exact": True},
+                "echo_sender_feedback_own_exact_bf16_state": {"sender_feedback": True, "own_exact": True,
+                                                              "state_bf16": True}}
+    for name, kw in variants.items():
+        res[name], ms[name] = timed(model, tp.EchoGroup(P, T * H, mode="echo", device=dev, **kw))
 
     # the row-parallel product in bfloat16 on libecho's kernel, written out then
     # reduced, or with stage 1 in its epilogue (bit-identical results)
@@ -382,7 +389,7 @@ def tp_report(torch, dev) -> dict:
         return float((x - y).float().norm() / y.float().norm())
 
     errs = {}
-    for mode in ("echo", "echo_off", "echo_bf16", "echo_bf16_fused"):
+    for mode in ("echo", "echo_off", *variants, "echo_bf16", "echo_bf16_fused"):
         loss, dx, dw = res[mode]
         errs[mode] = {"loss_rel_err": abs(float(loss - res["exact"][0])) / float(res["exact"][0]),
                       "dx0_rel_err": rel(dx, res["exact"][1]),

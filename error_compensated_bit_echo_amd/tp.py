@@ -35,18 +35,26 @@ from . import binding as B
 
 class EchoGroup:
     """P emulated ranks sharing one Echo state (forward and backward directions)
-    for messages of ``numel`` elements in bfloat16 on the wire."""
+    for messages of ``numel`` elements in bfloat16 on the wire.  ``variant``
+    passes the configuration switches ``sender_feedback``, ``state_bf16``,
+    ``own_exact`` and ``group`` through to the state (the output stays fp32)."""
 
-    def __init__(self, P: int, numel: int, mode: str = "echo", device=None, record: bool = False):
+    VARIANT_KEYS = ("sender_feedback", "state_bf16", "own_exact", "group")
+
+    def __init__(self, P: int, numel: int, mode: str = "echo", device=None, record: bool = False,
+                 **variant):
         import torch
 
         if mode not in ("echo", "echo_off", "exact"):
             raise ValueError(f"mode {mode!r}")
-        self.P, self.numel, self.mode = P, numel, mode
+        unknown = set(variant) - set(self.VARIANT_KEYS)
+        if unknown:
+            raise ValueError(f"unknown variant switches {sorted(unknown)}")
+        self.P, self.numel, self.mode, self.variant = P, numel, mode, dict(variant)
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         self.state = None
         if mode != "exact":
-            cfg = B.EchoConfig.make(P, numel, "bf16", compensate=(mode == "echo"))
+            cfg = B.EchoConfig.make(P, numel, "bf16", compensate=(mode == "echo"), **variant)
             self.state = B.echo_init_state(cfg, device=self.device)
         # when recording, every reduction appends (direction, [partials], out)
         self.record = record
@@ -66,6 +74,9 @@ class EchoGroup:
 
         if self.mode == "exact":
             raise ValueError("the bf16 product path needs an Echo state")
+        if fused and (self.variant.get("sender_feedback") or self.variant.get("own_exact")
+                      or self.variant.get("group", 32) != 32):
+            raise ValueError("the fused product takes group 32 without sender feedback or own shares")
         T, H = A[0].shape[0], W[0].shape[0]
         out = torch.empty(self.numel, dtype=torch.float32, device=self.device)
         if fused:

@@ -43,6 +43,21 @@ def test_tp_step_reductions_match_the_oracle(cuda, mode):
         assert np.array_equal(got.view(np.uint32), o["out"].view(np.uint32)), f"call {k} dir {d}"
 
 
+@pytest.mark.parametrize("variant", [{"sender_feedback": True}, {"own_exact": True, "state_bf16": True},
+                                     {"sender_feedback": True, "state_bf16": True, "group": 64}])
+def test_tp_step_with_variants_matches_the_oracle(cuda, variant):
+    """The same teacher-forced replay with the variants passed through the group."""
+    tp, model, x0, target = _setup(cuda)
+    group = tp.EchoGroup(P, T * H, mode="echo", device=cuda, record=True, **variant)
+    tp.train_step(model, group, x0, target)
+    assert [d for d, _, _ in group.log] == [0] * L + [1] * L
+    st = eo.OracleState(T * H)
+    for k, (d, parts, out) in enumerate(group.log):
+        host = np.stack([p.reshape(-1).float().cpu().numpy() for p in parts])
+        o = eo.echo_call(host, st, d, **variant)
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), o["out"].view(np.uint32)), f"call {k} dir {d}"
+
+
 def test_tp_step_errors_against_exact_allreduce(cuda):
     """Loss and gradients of Echo (on/off) against the same step with exact
     all-reduces: finite, and compensation does not make them worse."""
