@@ -263,8 +263,9 @@ def stream_report(name, E, synth, torch, dev, group: int = 32) -> dict:
 
 def decode_report(E, synth, torch, dev) -> dict:
     """The decode-shaped chain: 128 layers, P = 8, [64, 4096] bf16 partials from
-    a pre-norm random map per layer; three chains from the same h_0 (Echo with
-    compensation, without, and an exact all-reduce in float64).  Per-call
+    a pre-norm random map per layer; four chains from the same h_0 (Echo with
+    compensation, without, with compensation and sender feedback, and an exact
+    all-reduce in float64).  Per-call
     latency of echo_reduce: eager from Python (includes the binding's host
     time), one captured call replayed per layer, and 32 back-to-back calls in
     one graph (the library's own per-call time)."""
@@ -272,10 +273,12 @@ def decode_report(E, synth, torch, dev) -> dict:
     P, rows, hd, L = 8, c["rows"], c["hidden"], c["layers"]
     N = rows * hd
     h0 = synth.decode_h0(dev)
-    h = {"on": h0.clone(), "off": h0.clone()}
+    modes = ("on", "off", "sfb")
+    h = {m: h0.clone() for m in modes}
     hx = h0.double()
-    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=(m == "on")), device=dev)
-          for m in ("on", "off")}
+    st = {m: E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=(m != "off"),
+                                                 sender_feedback=(m == "sfb")), device=dev)
+          for m in modes}
     out = torch.empty(N, dtype=torch.float32, device=dev)
     # graph path: fixed partial buffers, its own state fed the same partials as "on"
     pbuf = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(P)]
@@ -291,7 +294,7 @@ def decode_report(E, synth, torch, dev) -> dict:
     graph_equal = True
     for layer in range(1, L + 1):
         w = synth.decode_weight(layer, dev)
-        for m in ("on", "off"):
+        for m in modes:
             parts = synth.decode_partials(h[m], w, P)
             if m == "on":
                 for b, p in zip(pbuf, parts):
@@ -315,7 +318,7 @@ def decode_report(E, synth, torch, dev) -> dict:
         if layer & (layer - 1) == 0 or layer == L:
             scale = hx.pow(2).mean().sqrt().item()
             rel[str(layer)] = {m: round((h[m].double() - hx).pow(2).mean().sqrt().item() / scale, 8)
-                               for m in ("on", "off")}
+                               for m in modes}
     torch.cuda.synchronize()
     eager = [a.elapsed_time(b) * 1e3 for a, b in ev_e]
     graph = [a.elapsed_time(b) * 1e3 for a, b in ev_g]
