@@ -53,3 +53,42 @@ def test_decode_chain_teacher_forced_parity_and_bounded_error(cuda):
         assert np.all(excess <= 0), f"layer {layer}: accumulated error beyond the bound by {excess.max()}"
         worst = max(worst, float(np.max(np.abs(D) / (11.0 * rmax + slack))))
     print(f"decode chain: {L} layers match the oracle; max |D|/bound = {worst:.3f}", flush=True)
+
+
+def test_decode_chain_with_sender_feedback_keeps_the_end_to_end_error_flat(cuda):
+    """The same chain with sender feedback (every rank carries its own stage-1
+    error into its next call), teacher-forced against the oracle at every layer,
+    and driven against a chain whose all-reduce is exact (float64): its
+    end-to-end error stops growing with depth (layers 16 to 128 within 10 %),
+    while the chain with owner compensation alone keeps growing."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    c = synth.DECODE_CHAIN
+    P, rows, hd, L = 8, c["rows"], c["hidden"], c["layers"]
+    N = rows * hd
+    sts = {"sfb": _state(P, N, "bf16", sender_feedback=True), "on": _state(P, N, "bf16")}
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    h0 = synth.decode_h0(cuda)
+    h = {m: h0.clone() for m in sts}
+    hx = h0.double()
+    rel = {m: {} for m in sts}
+    for layer in range(1, L + 1):
+        w = synth.decode_weight(layer, cuda)
+        for m, st in sts.items():
+            parts = synth.decode_partials(h[m], w, P)
+            E.echo_reduce(parts, out, st, E.ECHO_FWD)
+            if m == "sfb":
+                host = np.stack([p.float().cpu().numpy() for p in parts])
+                o = eo.echo_call(host, so, eo.FWD, sender_feedback=True)
+                assert _compare(_fetch(st, out, 0), o, so, 0, True, f"layer {layer}") == 0
+            h[m] += out.view(rows, hd)
+        hx += sum(p.double() for p in synth.decode_partials(hx.float(), w, P)).view(rows, hd)
+        scale = hx.pow(2).mean().sqrt().item()
+        for m in sts:
+            rel[m][layer] = (h[m].double() - hx).pow(2).mean().sqrt().item() / scale
+    print(f"decode chain relative error at 16 / 128 layers: sender feedback {rel['sfb'][16]:.4f} / "
+          f"{rel['sfb'][128]:.4f}, owner compensation only {rel['on'][16]:.4f} / {rel['on'][128]:.4f}", flush=True)
+    assert rel["sfb"][128] <= 1.1 * rel["sfb"][16]
+    assert rel["on"][128] >= 1.1 * rel["on"][16]
+    assert rel["sfb"][128] < rel["on"][128]
