@@ -104,7 +104,8 @@ def load_library():
         "echo_reduce": (i32, [ctypes.POINTER(vp), vp, vp, i32, vp]),
         "echo_stage1": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
         "echo_owner": (i32, [ctypes.POINTER(vp), vp, i32, vp]),
-        "echo_gemm_stage1": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int64, ctypes.c_int64, vp, vp]),
+        "echo_gemm_stage1": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int64, ctypes.c_int64, vp, i32,
+                                   vp]),
         "echo_gemm_bf16": (i32, [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int32,
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]),
         "echo_decode": (i32, [vp, vp, vp]),
@@ -257,9 +258,10 @@ def _bf16_matrices(mats, rows, cols, what):
     return (ctypes.c_void_p * len(mats))(*[t.data_ptr() for t in mats])
 
 
-def echo_gemm_stage1(A: Sequence, W: Sequence, state: EchoState, stream=None):
+def echo_gemm_stage1(A: Sequence, W: Sequence, state: EchoState, direction: int = ECHO_FWD, stream=None):
     """Stage 1 fused into the producing product: the payload of bf16(A_r @ W_r.T)
-    for every rank (A_r [M, K], W_r [H, K] bfloat16, M*H == N)."""
+    for every rank (A_r [M, K], W_r [H, K] bfloat16, M*H == N); with sender
+    feedback the ranks' stage-1 errors of ``direction`` are used and updated."""
     P = state.cfg.P
     if len(A) != P or len(W) != P:
         raise EchoError(ECHO_ERR_ARG, f"expected {P} A and {P} W matrices")
@@ -267,7 +269,7 @@ def echo_gemm_stage1(A: Sequence, W: Sequence, state: EchoState, stream=None):
     H = W[0].shape[0]
     a = _bf16_matrices(A, M, K, "A")
     w = _bf16_matrices(W, H, K, "W")
-    _check(load_library().echo_gemm_stage1(a, w, M, K, state.handle,
+    _check(load_library().echo_gemm_stage1(a, w, M, K, state.handle, int(direction),
                                            _stream_handle(stream, state.device)), "echo_gemm_stage1")
 
 

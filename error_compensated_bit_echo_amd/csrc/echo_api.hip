@@ -270,11 +270,12 @@ echo_status gemm_inputs(const void* const* A, const void* const* W, int P, echo:
 }  // namespace
 
 echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
-                             echo_state* st, echo_stream_t stream) {
+                             echo_state* st, echo_dir dir, echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
+  if (dir != ECHO_FWD && dir != ECHO_BWD) return ECHO_ERR_ARG;
   if (st->cfg.dtype != ECHO_BF16) return ECHO_ERR_DTYPE;
-  if (st->cfg.sender_feedback || st->cfg.own_exact) return ECHO_ERR_ARG;
+  if (st->cfg.own_exact) return ECHO_ERR_ARG;
   if (st->cfg.group != 32 || M <= 0 || st->cfg.numel % M != 0) return ECHO_ERR_SHAPE;
   const int64_t H = st->cfg.numel / M;
   if (!gemm_shape_ok(M, K, H)) return ECHO_ERR_SHAPE;
@@ -293,6 +294,9 @@ echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t
   a.M = M;
   a.K = K;
   a.H = H;
+  a.err = st->sender_err[dir];  // sender feedback: the ranks' stage-1 errors of `dir`
+  a.err_stride = st->err_words;
+  a.err_bf16 = st->cfg.state_bf16;
   return echo::launch_gemm(a, st->cfg.P, true, static_cast<hipStream_t>(stream)) == hipSuccess
              ? ECHO_OK
              : ECHO_ERR_HIP;

@@ -70,8 +70,11 @@ __device__ __forceinline__ void slab_barrier() {
 //     slab loads per multiply-add of the 128-row tile (the fastest of these
 //     where M allows it; a third slab, which hides twice the load latency,
 //     measured slower).
-template <int BM, int NW, int S, bool FUSED>
+// SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
+// 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
+template <int BM, int NW, int S, bool FUSED, int SFB>
 __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
+  static_assert(FUSED || SFB == 0, "sender feedback only in the fused epilogue");
   constexpr int kThreads = 64 * NW;
   constexpr int RW = 2 * BM / NW;                  // rows per wavefront
   constexpr int MI = RW / 32;                      // 32-row MFMA tiles per wavefront
@@ -196,6 +199,30 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
           *reinterpret_cast<uint2*>(lds + row * kLdsN + 64 * wn + 32 * j + 8 * q + 4 * half) = make_uint2(lo, hi);
         }
       } else {
+        // sender feedback: x' = fl(x + e) with the rank's carried stage-1 error of
+        // these 16 elements (runs of 4 at columns 8q + 4 half, q < 4)
+        [[maybe_unused]] float* err = nullptr;
+        if constexpr (SFB != 0) {
+          err = a.err + static_cast<int64_t>(r) * a.err_stride;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t at = e + 8 * q + 4 * half;  // element index of the run
+            float ev[4];
+            if constexpr (SFB == 2) {
+              const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(err) + at);
+              ev[0] = __uint_as_float(b.x << 16);
+              ev[1] = __uint_as_float(b.x & 0xFFFF0000u);
+              ev[2] = __uint_as_float(b.y << 16);
+              ev[3] = __uint_as_float(b.y & 0xFFFF0000u);
+            } else {
+              const f32x4 f = *reinterpret_cast<const f32x4*>(err + at);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) ev[k] = f[k];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * q + k] = v[4 * q + k] + ev[k];
+          }
+        }
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) amax = fmaxf(amax, __builtin_fabsf(v[k]));
@@ -209,8 +236,29 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
         }
         // w0: columns 4 half + {0..3} (low half-word) and 8 + 4 half + {0..3} (high);
         // w1: the same plus 16
+        float kf1[8];
         const uint32_t w0 = quantize8(v0, s, kf);
-        const uint32_t w1 = quantize8(v1, s, kf);
+        const uint32_t w1 = quantize8(v1, s, kf1);
+        if constexpr (SFB != 0) {
+          // e <- x' - fl(q * s), exact; written back where it was read
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t at = e + 8 * q + 4 * half;
+            float en[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int i = 4 * q + k;
+              en[k] = i < 8 ? v0[i] - kf[i] * s : v1[i - 8] - kf1[i - 8] * s;
+            }
+            if constexpr (SFB == 2) {
+              const uint32_t lo = __builtin_amdgcn_perm(bf16_rne_carry(en[1]), bf16_rne_carry(en[0]), 0x07060302u);
+              const uint32_t hi = __builtin_amdgcn_perm(bf16_rne_carry(en[3]), bf16_rne_carry(en[2]), 0x07060302u);
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(err) + at) = make_uint2(lo, hi);
+            } else {
+              *reinterpret_cast<f32x4*>(err + at) = f32x4{en[0], en[1], en[2], en[3]};
+            }
+          }
+        }
         // code word q of the group holds columns 8q .. 8q + 7, its low half-word from
         // the lower lane; the lower lane writes words 0 and 1, the upper 2 and 3
         const uint32_t got = __shfl_xor(half ? w0 : w1, 32);
@@ -249,10 +297,14 @@ template <int BM, int NW, int S>
 hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
-  if (fused)
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true>), grid, dim3(64 * NW), 0, s, a);
+  if (!fused)
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, false, 0>), grid, dim3(64 * NW), 0, s, a);
+  else if (a.err == nullptr)
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 0>), grid, dim3(64 * NW), 0, s, a);
+  else if (a.err_bf16)
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 2>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, false>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 1>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 

@@ -74,13 +74,12 @@ class EchoGroup:
 
         if self.mode == "exact":
             raise ValueError("the bf16 product path needs an Echo state")
-        if fused and (self.variant.get("sender_feedback") or self.variant.get("own_exact")
-                      or self.variant.get("group", 32) != 32):
-            raise ValueError("the fused product takes group 32 without sender feedback or own shares")
+        if fused and (self.variant.get("own_exact") or self.variant.get("group", 32) != 32):
+            raise ValueError("the fused product takes group 32 without the owners' own shares")
         T, H = A[0].shape[0], W[0].shape[0]
         out = torch.empty(self.numel, dtype=torch.float32, device=self.device)
         if fused:
-            B.echo_gemm_stage1(A, W, self.state)
+            B.echo_gemm_stage1(A, W, self.state, B.ECHO_FWD)
             B.echo_owner(self.state, B.ECHO_FWD)
             B.echo_decode(out, self.state)
         else:

@@ -150,17 +150,18 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
  * are output features), accumulated in fp32 on the matrix cores and rounded to
  * nearest-even; N = M*H.  Each rank's stage-1 payload is written into the
  * state exactly as echo_stage1 would write it from that bf16 partial, which
- * itself never reaches memory.  Follow with echo_owner and echo_decode.
+ * itself never reaches memory; with sender_feedback the ranks' stage-1 errors
+ * of direction `dir` are added and updated as echo_stage1 does (otherwise
+ * `dir` is only validated).  Follow with echo_owner and echo_decode on `dir`.
  * A, W: host arrays of P device pointers, 16-byte aligned, read-only.
- * Requires a bf16 state with group 32, no sender feedback and no own_exact
- * (the owner would need the partial itself), M and H multiples of 128
- * (M/128 <= 65535), K a multiple of 64.  Errors: ECHO_ERR_ARG (null or
- * misaligned pointer, A or W overlapping the workspace, sender feedback or
- * own_exact on), ECHO_ERR_SHAPE (sizes,
+ * Requires a bf16 state with group 32 and no own_exact (the owner would need
+ * the partial itself), M and H multiples of 128 (M/128 <= 65535), K a
+ * multiple of 64.  Errors: ECHO_ERR_ARG (null or misaligned pointer, A or W
+ * overlapping the workspace, own_exact on, bad dir), ECHO_ERR_SHAPE (sizes,
  * M*H != N, group != 32), ECHO_ERR_DTYPE (state not bf16), ECHO_ERR_STATE,
  * ECHO_ERR_HIP. */
 echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
-                             echo_state* st, echo_stream_t stream);
+                             echo_state* st, echo_dir dir, echo_stream_t stream);
 
 /* The same product written out, for comparison: out[r] = bf16(A_r * W_r^T),
  * [M, H] bfloat16 row-major, for r < P (1..16).  Same shape rules; out[r] must

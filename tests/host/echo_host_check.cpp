@@ -353,10 +353,10 @@ void run_case(const Case& c, u64 ws_offset) {
   }
 
   // the fused product writes the same stage-1 regions
-  if (c.dtype == ECHO_BF16 && c.group == 32 && !c.sfb && !c.own && N % (128 * 128) == 0) {
+  if (c.dtype == ECHO_BF16 && c.group == 32 && !c.own && N % (128 * 128) == 0) {
     const int64_t M = 128, K = 256, H = c.N / M;
     g_launches.clear();
-    CHECK(echo_gemm_stage1(parts, parts, M, K, st, nullptr) == ECHO_OK, "fused product");
+    CHECK(echo_gemm_stage1(parts, parts, M, K, st, ECHO_BWD, nullptr) == ECHO_OK, "fused product");
     if (g_launches.size() == 1 && g_launches[0].kind == HostLaunch::kGemm) {
       const echo::GemmArgs& a = g_launches[0].gemm;
       CHECK(a.M == M && a.K == K && a.H == H && g_launches[0].flag && g_launches[0].P == c.P, "gemm shape");
@@ -365,10 +365,20 @@ void run_case(const Case& c, u64 ws_offset) {
         const Region* rsc = find(rs, "scales1[" + std::to_string(r) + "]");
         CHECK(rc && addr(a.codes) + 4ull * r * a.codes_stride_words == rc->lo, "gemm codes of rank %d", r);
         CHECK(rsc && addr(a.scales) + 4ull * r * a.scales_stride == rsc->lo, "gemm scales of rank %d", r);
+        if (c.sfb) {  // the backward direction's errors, whole-message extent
+          const Region* re = find(rs, "sender_err bwd[" + std::to_string(r) + "]");
+          const u64 lo = addr(a.err) + 4ull * r * a.err_stride;
+          CHECK(re && lo == re->lo && lo + (c.sb16 ? 2 : 4) * N <= re->hi, "gemm errors of rank %d", r);
+        }
       }
+      CHECK(c.sfb ? (a.err != nullptr && a.err_bf16 == c.sb16) : a.err == nullptr, "gemm error pointer");
     } else {
       CHECK(false, "fused product launches one kernel");
     }
+    g_launches.clear();
+    CHECK(echo_gemm_stage1(parts, parts, M, K, st, static_cast<echo_dir>(2), nullptr) == ECHO_ERR_ARG &&
+              g_launches.empty(),
+          "fused product with a bad direction");
   }
   echo_destroy_state(st);
 }

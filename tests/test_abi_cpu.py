@@ -139,7 +139,7 @@ def test_product_entry_point_rejects_bad_shapes_without_touching_the_gpu():
     assert lib.echo_gemm_bf16(nulls, fake, outs, 2, 128, 64, 128, None) == B.ECHO_ERR_ARG
     misaligned = (ctypes.c_void_p * 2)(4096 + 2, 8192)
     assert lib.echo_gemm_bf16(misaligned, fake, outs, 2, 128, 64, 128, None) == B.ECHO_ERR_ARG
-    assert lib.echo_gemm_stage1(fake, fake, 128, 64, None, None) == B.ECHO_ERR_STATE
+    assert lib.echo_gemm_stage1(fake, fake, 128, 64, None, 0, None) == B.ECHO_ERR_STATE
 
 
 def test_header_is_strict_c_and_matches_the_binding_layout(tmp_path):

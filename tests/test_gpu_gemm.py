@@ -99,6 +99,31 @@ def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
 
 
+@pytest.mark.parametrize("sb16", [False, True])
+def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16):
+    """Sender feedback in the fused epilogue: each rank's carried stage-1 error
+    (fp32, or bfloat16 with the bf16 state) is added to its product before the
+    quantizer and updated after it, per direction; whole calls in both
+    directions, interleaved, against the oracle fed the written-out partials."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, M, K, H = 3, 256, 512, 384
+    N = M * H
+    st = _state(P, N, "bf16", sender_feedback=True, state_bf16=sb16)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    _, W = _inputs(P, M, K, H, 5, cuda)
+    for t in range(4):
+        for d in (0, 1):
+            A, _ = _inputs(P, M, K, H, 20 + 2 * t + d, cuda, w=W)
+            E.echo_gemm_stage1(A, W, st, d)
+            E.echo_owner(st, d)
+            E.echo_decode(out, st)
+            host = np.stack([p.reshape(-1).float().cpu().numpy() for p in _unfused(A, W)])
+            o = eo.echo_call(host, so, d, sender_feedback=True, state_bf16=sb16)
+            assert _compare(_fetch(st, out, d), o, so, d, True, f"call {t} dir {d}") == 0
+
+
 def test_argument_errors(cuda):
     import ctypes
     import error_compensated_bit_echo_amd as E
@@ -110,20 +135,20 @@ def test_argument_errors(cuda):
     arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     st = _state(P, M * H, "f32")
-    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_DTYPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_DTYPE
     st = _state(P, M * H, "bf16", sender_feedback=True)
-    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, 2, s) == B.ECHO_ERR_ARG  # bad direction
     st = _state(P, M * H, "bf16", own_exact=True)  # the owner would need the partial itself
-    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
     st = _state(P, M * H, "bf16", group=64)
-    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, s) == B.ECHO_ERR_SHAPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_SHAPE
     st = _state(P, M * H, "bf16")
-    assert lib.echo_gemm_stage1(arr(A), arr(W), 64, K, st.handle, s) == B.ECHO_ERR_SHAPE
-    assert lib.echo_gemm_stage1(arr(A), arr(W), M, 96, st.handle, s) == B.ECHO_ERR_SHAPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), 64, K, st.handle, 0, s) == B.ECHO_ERR_SHAPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), M, 96, st.handle, 0, s) == B.ECHO_ERR_SHAPE
     bad = (ctypes.c_void_p * P)(A[0].data_ptr(), A[1].data_ptr() + 2)
-    assert lib.echo_gemm_stage1(bad, arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(bad, arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
     # an input inside the workspace the payload is written to (rejected before any launch)
     inside = (ctypes.c_void_p * P)(A[0].data_ptr(), st.workspace.data_ptr())
-    assert lib.echo_gemm_stage1(inside, arr(W), M, K, st.handle, s) == B.ECHO_ERR_ARG
-    assert lib.echo_gemm_stage1(arr(A), inside, M, K, st.handle, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(inside, arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
+    assert lib.echo_gemm_stage1(arr(A), inside, M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
     torch.cuda.synchronize()

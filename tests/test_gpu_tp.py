@@ -81,7 +81,8 @@ def test_tp_step_errors_against_exact_allreduce(cuda):
         assert e_loss < 0.05 and e_dx < 0.5 and e_dw < 0.5
 
 
-def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda):
+@pytest.mark.parametrize("variant", [{}, {"sender_feedback": True, "state_bf16": True}])
+def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant):
     """Row-parallel products in bfloat16 on libecho's kernel: with stage 1 in the
     product's epilogue the whole training step (loss, input and weight
     gradients) is bit-identical to the product written out and reduced by
@@ -97,7 +98,7 @@ def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda):
         g.manual_seed(12)
         x0 = torch.randn(T, H, generator=g, device=cuda)
         target = torch.randn(T, H, generator=g, device=cuda)
-        group = tp.EchoGroup(P, T * H, mode="echo", device=cuda, record=(prod == "bf16_fused"))
+        group = tp.EchoGroup(P, T * H, mode="echo", device=cuda, record=(prod == "bf16_fused"), **variant)
         res[prod] = (tp.train_step(model, group, x0, target), group)
     (lf, dxf, dwf), gf = res["bf16_fused"]
     (lu, dxu, dwu), _ = res["bf16"]
@@ -114,5 +115,5 @@ def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda):
             E.echo_gemm_bf16(A, W, written)
             parts = written
         host = np.stack([p.reshape(-1).float().cpu().numpy() for p in parts])
-        o = eo.echo_call(host, st, d)
+        o = eo.echo_call(host, st, d, **variant)
         assert np.array_equal(out.cpu().numpy().view(np.uint32), o["out"].view(np.uint32)), f"call {k} dir {d}"
