@@ -386,13 +386,18 @@ def tp_report(torch, dev) -> dict:
     for prod in ("bf16", "bf16_fused"):
         m2 = tp.TPMLPStack(L, H, F, P, seed=21, device=dev, product=prod)
         res["echo_" + prod], ms["echo_" + prod] = timed(m2, tp.EchoGroup(P, T * H, mode="echo", device=dev))
+        if prod == "bf16_fused":  # the fused product with sender feedback and bf16 state
+            name = "echo_bf16_fused_sender_feedback_bf16_state"
+            res[name], ms[name] = timed(m2, tp.EchoGroup(P, T * H, mode="echo", device=dev, sender_feedback=True,
+                                                         state_bf16=True))
         del m2
 
     def rel(x, y):
         return float((x - y).float().norm() / y.float().norm())
 
     errs = {}
-    for mode in ("echo", "echo_off", *variants, "echo_bf16", "echo_bf16_fused"):
+    for mode in ("echo", "echo_off", *variants, "echo_bf16", "echo_bf16_fused",
+                 "echo_bf16_fused_sender_feedback_bf16_state"):
         loss, dx, dw = res[mode]
         errs[mode] = {"loss_rel_err": abs(float(loss - res["exact"][0])) / float(res["exact"][0]),
                       "dx0_rel_err": rel(dx, res["exact"][1]),
