@@ -139,8 +139,8 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
 # ---------------------------------------------------------------------------
 # the other workloads: latency, effective bandwidth and accuracy reports
 # ---------------------------------------------------------------------------
-CONFIG_IDS = {"tiny": 1, "prefill": 2, "decode": 3, "training": 4, "tp": 0, "groups": 2, "variants": 2,
-              "gemm": 0}
+# the reports of --config; the first four are the synthetic workloads of the same name
+REPORTS = ("tiny", "prefill", "decode", "training", "tp", "groups", "variants", "gemm")
 CACHE_BYTES = 256 * 2**20  # MI355X Infinity Cache
 
 
@@ -189,17 +189,16 @@ def stream_report(name, E, synth, torch, dev, group: int = 32) -> dict:
     stream h* = sum of all partials (float64); compensation on and off."""
     import numpy as np
 
-    cid = CONFIG_IDS[name]
-    c = synth.CONFIGS[cid]
-    P, N, dtype = c["P"], synth.numel(cid), c["dtype"]
+    c = synth.WORKLOADS[name]
+    P, N, dtype = c["P"], synth.numel(name), c["dtype"]
     dirs = (0, 1) if name == "training" else (0,)
     b_in = 4 if dtype == "f32" else 2
 
     def parts_for(d, t):
         if dtype == "f32":
-            raw, _ = synth.host_partials(cid, d, t)
+            raw, _ = synth.host_partials(name, d, t)
             return [torch.from_numpy(np.ascontiguousarray(raw[r])).to(dev) for r in range(P)]
-        return synth.device_partials(cid, d, t, device=dev)
+        return synth.device_partials(name, d, t, device=dev)
 
     st = {m: E.echo_init_state(E.EchoConfig.make(P, N, dtype, compensate=(m == "on"), group=group),
                                device=dev)
@@ -415,8 +414,8 @@ def sender_report(E, synth, torch, dev) -> dict:
     outputs against the exact stream, by call count T, for compensation on/off,
     sender feedback on/off, fp32 or bf16 state, fp32 or bf16 output and the
     owner adding its own partial exactly or not; per-call latency of each."""
-    c = synth.CONFIGS[2]
-    P, N, calls = c["P"], synth.numel(2), c["calls"]
+    c = synth.WORKLOADS["prefill"]
+    P, N, calls = c["P"], synth.numel("prefill"), c["calls"]
     # (compensate, sender feedback, bf16 state, bf16 output, own partial exact)
     combos = [(True, False, False, False, False), (False, False, False, False, False),
               (True, True, False, False, False), (False, True, False, False, False),
@@ -443,7 +442,7 @@ def sender_report(E, synth, torch, dev) -> dict:
     hx = torch.zeros(N, dtype=torch.float64, device=dev)
     err = {name(k): {} for k in modes}
     for t in range(calls):
-        parts = synth.device_partials(2, 0, t, device=dev)
+        parts = synth.device_partials("prefill", 0, t, device=dev)
         for k, st in modes.items():
             E.echo_reduce(parts, outs[k], st, E.ECHO_FWD)
             h[k] += outs[k].double()
@@ -654,7 +653,7 @@ def main():
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of this benchmark, then exit")
     ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
-    ap.add_argument("--config", choices=sorted(CONFIG_IDS) + ["all"],
+    ap.add_argument("--config", choices=sorted(REPORTS) + ["all"],
                     help="instead of the 1 GiB headline, report latency, bandwidth and accuracy of "
                          "another workload (one JSON line each)")
     args = ap.parse_args()
@@ -710,12 +709,12 @@ def main():
             print(json.dumps(rep), flush=True)
             torch.cuda.empty_cache()
         return
-    cfg_id = 5
-    c = synth.CONFIGS[cfg_id]
-    P, N = c["P"], synth.numel(cfg_id)
+    msg = "headline_1GiB"
+    c = synth.WORKLOADS[msg]
+    P, N = c["P"], synth.numel(msg)
     comp = not args.no_comp
     print(f"# generating {P} x {N} bf16 partials on the device", file=sys.stderr, flush=True)
-    parts = synth.device_partials(cfg_id, 0, 0, device=dev)
+    parts = synth.device_partials(msg, 0, 0, device=dev)
     G = args.group
     SFB, SB16, OBF, OWN = args.sender_feedback, args.bf16_state, args.out_bf16, args.own_exact
     cfg = E.EchoConfig.make(P, N, "bf16", compensate=comp, group=G, sender_feedback=SFB,

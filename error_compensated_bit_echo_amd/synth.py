@@ -5,7 +5,7 @@ holds none of the all-reduce's own arithmetic, so both the HIP path's tests and
 the CPU oracle can be fed from it without sharing any code of the method.
 
 Recipe (host side, numpy):
-  seed(cfg, dir, call, rank) = cfg*10**9 + dir*10**8 + call*10**3 + rank;
+  seed(id, dir, call, rank) = id*10**9 + dir*10**8 + call*10**3 + rank;
   x = Generator(PCG64(seed)).standard_normal(n, float32) * std;
   outliers: mask = rng.random(n) < p from the same generator, x[mask] *= k;
   bf16 partials are x rounded to bfloat16 (round to nearest even).
@@ -24,28 +24,28 @@ import numpy as np
 
 F32 = np.float32
 
-# name, P, shape, dtype, value distribution, calls per run
-CONFIGS = {
-    1: dict(name="tiny", P=2, shape=(8, 256), dtype="f32", std=1.0,
-            outlier_p=0.0, outlier_mult=1.0, calls=16),
-    2: dict(name="prefill", P=4, shape=(2048, 4096), dtype="bf16", std=0.02,
-            outlier_p=1e-3, outlier_mult=50.0, calls=72),
-    3: dict(name="decode", P=8, shape=(64, 4096), dtype="bf16", std=0.02,
-            outlier_p=0.0, outlier_mult=1.0, calls=128),
-    4: dict(name="training", P=4, shape=(4096, 4096), dtype="bf16", std=0.02,
-            std_bwd=1e-3, outlier_p=0.0, outlier_mult=1.0, calls=56),
-    5: dict(name="headline_1GiB", P=8, shape=(131072, 4096), dtype="bf16",
-            std=1.0, outlier_p=1e-4, outlier_mult=100.0, calls=10),
+# the workloads by name: seed id, P, shape per rank, dtype, value distribution, calls per run
+WORKLOADS = {
+    "tiny": dict(seed_id=1, P=2, shape=(8, 256), dtype="f32", std=1.0,
+                 outlier_p=0.0, outlier_mult=1.0, calls=16),
+    "prefill": dict(seed_id=2, P=4, shape=(2048, 4096), dtype="bf16", std=0.02,
+                    outlier_p=1e-3, outlier_mult=50.0, calls=72),
+    "decode": dict(seed_id=3, P=8, shape=(64, 4096), dtype="bf16", std=0.02,
+                   outlier_p=0.0, outlier_mult=1.0, calls=128),
+    "training": dict(seed_id=4, P=4, shape=(4096, 4096), dtype="bf16", std=0.02,
+                     std_bwd=1e-3, outlier_p=0.0, outlier_mult=1.0, calls=56),
+    "headline_1GiB": dict(seed_id=5, P=8, shape=(131072, 4096), dtype="bf16",
+                          std=1.0, outlier_p=1e-4, outlier_mult=100.0, calls=10),
 }
 
 
-def numel(cfg_id: int) -> int:
-    r, c = CONFIGS[cfg_id]["shape"]
+def numel(workload: str) -> int:
+    r, c = WORKLOADS[workload]["shape"]
     return r * c
 
 
-def seed_of(cfg_id: int, direction: int, call: int, rank: int) -> int:
-    return cfg_id * 10**9 + direction * 10**8 + call * 10**3 + rank
+def seed_of(workload: str, direction: int, call: int, rank: int) -> int:
+    return WORKLOADS[workload]["seed_id"] * 10**9 + direction * 10**8 + call * 10**3 + rank
 
 
 def normal_f32(seed: int, n: int, std: float = 1.0, outlier_p: float = 0.0,
@@ -73,20 +73,20 @@ def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
 
 
-def host_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | None = None,
+def host_partials(workload: str, direction: int = 0, call: int = 0, P: int | None = None,
                   n: int | None = None, dtype: str | None = None, std: float | None = None):
     """Rank partials for one call, drawn on the host.
 
     Returns ``(raw, values)``: ``raw`` is what is uploaded ([P, n] float32, or
     uint16 bfloat16 bit patterns), ``values`` the same numbers as float32.
     """
-    c = CONFIGS[cfg_id]
+    c = WORKLOADS[workload]
     P = c["P"] if P is None else P
-    n = numel(cfg_id) if n is None else n
+    n = numel(workload) if n is None else n
     dtype = c["dtype"] if dtype is None else dtype
     if std is None:
         std = c.get("std_bwd", c["std"]) if direction == 1 else c["std"]
-    rows = [normal_f32(seed_of(cfg_id, direction, call, r), n, std,
+    rows = [normal_f32(seed_of(workload, direction, call, r), n, std,
                        c["outlier_p"], c["outlier_mult"]) for r in range(P)]
     x = np.stack(rows) if P else np.zeros((0, n), F32)
     if dtype == "f32":
@@ -95,7 +95,7 @@ def host_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | None 
     return bits, bf16_bits_as_f32(bits)
 
 
-def device_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | None = None,
+def device_partials(workload: str, direction: int = 0, call: int = 0, P: int | None = None,
                     n: int | None = None, device: str = "cuda"):
     """Rank partials drawn on the device with torch (for messages of gigabytes).
 
@@ -103,14 +103,14 @@ def device_partials(cfg_id: int, direction: int = 0, call: int = 0, P: int | Non
     """
     import torch
 
-    c = CONFIGS[cfg_id]
+    c = WORKLOADS[workload]
     P = c["P"] if P is None else P
-    n = numel(cfg_id) if n is None else n
+    n = numel(workload) if n is None else n
     std = c.get("std_bwd", c["std"]) if direction == 1 else c["std"]
     out = []
     for r in range(P):
         g = torch.Generator(device=device)
-        g.manual_seed(seed_of(cfg_id, direction, call, r))
+        g.manual_seed(seed_of(workload, direction, call, r))
         x = torch.randn(n, generator=g, device=device, dtype=torch.float32)
         if std != 1.0:
             x.mul_(std)
@@ -138,7 +138,7 @@ def decode_h0(device="cuda"):
 
     c = DECODE_CHAIN
     g = torch.Generator(device=device)
-    g.manual_seed(seed_of(3, 0, 0, 0))
+    g.manual_seed(seed_of("decode", 0, 0, 0))
     return torch.randn(c["rows"], c["hidden"], generator=g, device=device) * c["h0_std"]
 
 
@@ -148,7 +148,7 @@ def decode_weight(layer: int, device="cuda"):
 
     hd = DECODE_CHAIN["hidden"]
     g = torch.Generator(device=device)
-    g.manual_seed(3 * 10**9 + 9 * 10**8 + layer)
+    g.manual_seed(WORKLOADS["decode"]["seed_id"] * 10**9 + 9 * 10**8 + layer)
     w = torch.randn(hd, hd, generator=g, device=device)
     w.mul_(1.0 / hd ** 0.5)
     return w.to(torch.bfloat16)

@@ -22,14 +22,14 @@ pytestmark = pytest.mark.gpu
 def test_tiny_config_every_call(cuda, compensate):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    c = synth.CONFIGS[1]
-    P, N = c["P"], synth.numel(1)
+    c = synth.WORKLOADS["tiny"]
+    P, N = c["P"], synth.numel("tiny")
     st = _state(P, N, "f32", compensate)
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     inexact = 0
     for t in range(c["calls"]):
-        raw, vals = synth.host_partials(1, 0, t)
+        raw, vals = synth.host_partials("tiny", 0, t)
         E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, compensate=compensate)
         inexact += _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}")
@@ -49,7 +49,7 @@ def test_multi_tile_ragged(cuda, P, dtype):
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     for t in range(3):
-        raw, vals = synth.host_partials(2, 0, t, P=P, n=N, dtype=dtype)
+        raw, vals = synth.host_partials("prefill", 0, t, P=P, n=N, dtype=dtype)
         E.echo_reduce(_upload(raw, dtype, cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD)
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"P={P} {dtype} call {t}") == 0
@@ -72,7 +72,7 @@ def test_larger_groups_multi_tile_ragged(cuda, P, dtype, group):
             vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
             raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
         else:
-            raw, vals = synth.host_partials(2, 0, t, P=P, n=N, dtype=dtype)
+            raw, vals = synth.host_partials("prefill", 0, t, P=P, n=N, dtype=dtype)
         E.echo_reduce(_upload(raw, dtype, cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, group=group)
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"G={group} P={P} {dtype} call {t}") == 0
@@ -164,7 +164,7 @@ def test_random_configurations(cuda, k):
     out = _out_tensor(st, cuda)
     for t in range(3):
         for d in (0, 1):
-            raw, vals = synth.host_partials(4, d, 10 * k + t, P=P, n=N, dtype=dt)
+            raw, vals = synth.host_partials("training", d, 10 * k + t, P=P, n=N, dtype=dt)
             E.echo_reduce(_upload(raw, dt, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, compensate=c["compensate"], beta_fast=c["beta"][0],
                              beta_slow=c["beta"][1], group=G, **kw)
@@ -192,7 +192,7 @@ def test_beta_zero_error_feedback(cuda):
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     for t in range(5):
-        raw, vals = synth.host_partials(3, 0, t, P=P, n=N)
+        raw, vals = synth.host_partials("decode", 0, t, P=P, n=N)
         E.echo_reduce(_upload(raw, "bf16", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, beta_fast=0.0, beta_slow=0.0)
         assert _compare(_fetch(st, out, 0), o, so, 0, True) == 0
@@ -208,8 +208,8 @@ def test_directions_reset_checkpoint_and_determinism(cuda):
     st = _state(P, N, "bf16")
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
-    fw = [synth.host_partials(4, 0, t, P=P, n=N) for t in range(6)]
-    bw = [synth.host_partials(4, 1, t, P=P, n=N) for t in range(6)]
+    fw = [synth.host_partials("training", 0, t, P=P, n=N) for t in range(6)]
+    bw = [synth.host_partials("training", 1, t, P=P, n=N) for t in range(6)]
     snap = None
     for t in range(6):
         E.echo_reduce(_upload(fw[t][0], "bf16", cuda), out, st, E.ECHO_FWD)
@@ -250,7 +250,7 @@ def test_stage_entry_points_equal_reduce(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     P, N = 8, 32 * 4096
-    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    raw, _ = synth.host_partials("decode", 0, 0, P=P, n=N)
     parts = _upload(raw, "bf16", cuda)
     s1, s2 = _state(P, N, "bf16"), _state(P, N, "bf16")
     o1 = torch.empty(N, dtype=torch.float32, device=cuda)
@@ -269,7 +269,7 @@ def test_graph_capture_replays_match_eager(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     P, N = 8, 64 * 4096
-    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    raw, _ = synth.host_partials("decode", 0, 0, P=P, n=N)
     parts = _upload(raw, "bf16", cuda)
     se, sg = _state(P, N, "bf16"), _state(P, N, "bf16")
     oe = torch.empty(N, dtype=torch.float32, device=cuda)
@@ -300,8 +300,8 @@ def test_graph_capture_of_variants_and_resets(cuda, variant):
     kw = dict(variant)
     comp = kw.pop("compensate", True)
     P, N = 4, 2048 * 9 + 64 * 3
-    raw0, _ = synth.host_partials(4, 0, 1, P=P, n=N)
-    raw1, _ = synth.host_partials(4, 1, 1, P=P, n=N)
+    raw0, _ = synth.host_partials("training", 0, 1, P=P, n=N)
+    raw1, _ = synth.host_partials("training", 1, 1, P=P, n=N)
     p0, p1 = _upload(raw0, "bf16", cuda), _upload(raw1, "bf16", cuda)
     se, sg = _state(P, N, "bf16", comp, **kw), _state(P, N, "bf16", comp, **kw)
     oe, og = _out_tensor(se, cuda), _out_tensor(sg, cuda)
@@ -337,7 +337,7 @@ def test_argument_errors_launch_nothing(cuda):
     torch = _torch()
     P, N = 2, 32 * 64
     st = _state(P, N, "bf16")
-    raw, _ = synth.host_partials(1, 0, 0, P=P, n=N, dtype="bf16")
+    raw, _ = synth.host_partials("tiny", 0, 0, P=P, n=N, dtype="bf16")
     parts = _upload(raw, "bf16", cuda)
     out = torch.zeros(N, dtype=torch.float32, device=cuda)
     E.echo_reduce(parts, out, st, E.ECHO_FWD)
@@ -406,7 +406,7 @@ def _window_segments(N, P, group, w, width):
             for a, b in eo.owner_segments(N // group, P)]
 
 
-def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6, width=1 << 14,
+def _windowed_run(cuda, workload, calls, directions, same_partials=False, n_win=6, width=1 << 14,
                   P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
                   out_bf16=False, own_exact=False, extra_windows=(), group=32, threads=1):
     """The configuration's calls at full size; the oracle checks sampled windows.
@@ -415,13 +415,14 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
     threads > 1 runs the oracle on the windows in parallel (each has its own state)."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    c = synth.CONFIGS[cfg_id]
+    c = synth.WORKLOADS[workload]
     P = c["P"] if P is None else P
-    N = synth.numel(cfg_id) if N is None else N
+    N = synth.numel(workload) if N is None else N
     st = _state(P, N, c["dtype"], compensate=compensate, poison=False, sender_feedback=sender_feedback,
                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group)
     out = _out_tensor(st, cuda)
-    wins = sorted(set(_windows(N, n_win, width, cfg_id, align=group)) | set(extra_windows))
+    seed = synth.WORKLOADS[workload]["seed_id"]
+    wins = sorted(set(_windows(N, n_win, width, seed, align=group)) | set(extra_windows))
     if own_exact:  # add a window on every segment boundary
         per = eo.owner_segments(N // group, P)
         wins = sorted(set(wins) | {max(0, min(N - width, g0 * group - width // 2)) // group * group
@@ -432,7 +433,7 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
         for d in directions:
             if parts is None or not same_partials:
                 parts = None
-                parts = synth.device_partials(cfg_id, d, t, P=P, n=N, device=cuda)
+                parts = synth.device_partials(workload, d, t, P=P, n=N, device=cuda)
             E.echo_reduce(parts, out, st, d)
             torch.cuda.synchronize()
 
@@ -443,7 +444,7 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
                                  segments=_window_segments(N, P, group, w, width) if own_exact else None)
                 g = _fetch(st, out, d, w, w + width)
                 return _compare(g, o, so[w], d, compensate,
-                                f"cfg{cfg_id} P={P} N={N} call {t} dir {d} window {w}", own_exact)
+                                f"{workload} P={P} N={N} call {t} dir {d} window {w}", own_exact)
 
             if threads > 1:
                 from concurrent.futures import ThreadPoolExecutor
@@ -451,22 +452,22 @@ def _windowed_run(cuda, cfg_id, calls, directions, same_partials=False, n_win=6,
                     assert sum(ex.map(check, wins)) == 0
             else:
                 assert sum(check(w) for w in wins) == 0
-        print(f"cfg{cfg_id} P={P} N={N}: call {t} ok", flush=True)
+        print(f"{workload} P={P} N={N}: call {t} ok", flush=True)
 
 
 def test_prefill_config_full_size(cuda):
-    _windowed_run(cuda, 2, 24, (0,))
+    _windowed_run(cuda, "prefill", 24, (0,))
 
 
 def test_training_config_full_size_interleaved(cuda):
-    _windowed_run(cuda, 4, 12, (0, 1))
+    _windowed_run(cuda, "training", 12, (0, 1))
 
 
 def test_headline_config_full_size(cuda):
     """All 10 calls of the 1 GiB P = 8 message, 16 group-aligned windows of 2^20
     elements (the first, the last and 14 random ones) checked after every call."""
-    _windowed_run(cuda, 5, synth.CONFIGS[5]["calls"], (0,), same_partials=True, n_win=16, width=1 << 20,
-                  threads=16)
+    calls = synth.WORKLOADS["headline_1GiB"]["calls"]
+    _windowed_run(cuda, "headline_1GiB", calls, (0,), same_partials=True, n_win=16, width=1 << 20, threads=16)
 
 
 def test_headline_config_every_group_of_the_first_two_calls(cuda):
@@ -478,13 +479,13 @@ def test_headline_config_every_group_of_the_first_two_calls(cuda):
 
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    cfg_id = 5
-    c = synth.CONFIGS[cfg_id]
-    P, N = c["P"], synth.numel(cfg_id)
+    workload = "headline_1GiB"
+    c = synth.WORKLOADS[workload]
+    P, N = c["P"], synth.numel(workload)
     W = 1 << 23
     st = _state(P, N, c["dtype"], poison=False)
     out = _out_tensor(st, cuda)
-    parts = synth.device_partials(cfg_id, 0, 0, device=cuda)
+    parts = synth.device_partials(workload, 0, 0, device=cuda)
     so = {w: eo.OracleState(W) for w in range(0, N, W)}
 
     def check(w, t):
@@ -502,7 +503,7 @@ def test_headline_config_every_group_of_the_first_two_calls(cuda):
         print(f"call {t}: all {N // 32} groups ok", flush=True)
 
 
-def _full_run(cuda, cfg_id, calls, directions, W=1 << 21, **variant):
+def _full_run(cuda, workload, calls, directions, W=1 << 21, **variant):
     """The configuration's first calls at full size, every group checked after each
     call: the oracle runs on 16 threads over the windows of W elements that tile
     the message, each with its own state (given the whole message's owner split
@@ -511,8 +512,8 @@ def _full_run(cuda, cfg_id, calls, directions, W=1 << 21, **variant):
 
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    c = synth.CONFIGS[cfg_id]
-    P, N = c["P"], synth.numel(cfg_id)
+    c = synth.WORKLOADS[workload]
+    P, N = c["P"], synth.numel(workload)
     assert N % W == 0
     st = _state(P, N, c["dtype"], poison=False, **variant)
     out = _out_tensor(st, cuda)
@@ -521,7 +522,7 @@ def _full_run(cuda, cfg_id, calls, directions, W=1 << 21, **variant):
     group = variant.get("group", 32)
     for t in range(calls):
         for d in directions:
-            parts = synth.device_partials(cfg_id, d, t, device=cuda)
+            parts = synth.device_partials(workload, d, t, device=cuda)
             E.echo_reduce(parts, out, st, d)
             torch.cuda.synchronize()
 
@@ -530,23 +531,23 @@ def _full_run(cuda, cfg_id, calls, directions, W=1 << 21, **variant):
                 o = eo.echo_call(host, so[w], d, segments=_window_segments(N, P, group, w, W) if own else None,
                                  **variant)
                 return _compare(_fetch(st, out, d, w, w + W), o, so[w], d, True,
-                                f"cfg{cfg_id} call {t} dir {d} window {w}", own)
+                                f"{workload} call {t} dir {d} window {w}", own)
 
             with ThreadPoolExecutor(max_workers=16) as ex:
                 assert sum(ex.map(check, sorted(so))) == 0
-            print(f"cfg{cfg_id} call {t} dir {d}: all {N // group} groups ok", flush=True)
+            print(f"{workload} call {t} dir {d}: all {N // group} groups ok", flush=True)
 
 
 def test_prefill_config_every_group(cuda):
-    _full_run(cuda, 2, 3, (0,))
+    _full_run(cuda, "prefill", 3, (0,))
 
 
 def test_training_config_every_group_interleaved(cuda):
-    _full_run(cuda, 4, 2, (0, 1))
+    _full_run(cuda, "training", 2, (0, 1))
 
 
 def test_prefill_config_every_group_with_variants(cuda):
-    _full_run(cuda, 2, 3, (0,), own_exact=True, out_bf16=True, state_bf16=True)
+    _full_run(cuda, "prefill", 3, (0,), own_exact=True, out_bf16=True, state_bf16=True)
 
 
 @pytest.mark.parametrize("P,N", [(4, 14 << 20), (2, 25 << 20), (8, 26 << 20), (8, 29 << 20)])
@@ -554,29 +555,29 @@ def test_cache_policy_boundaries(cuda, P, N):
     """Message sizes on both sides of the cache-policy switches at 480 MB and
     1.2 GB per call (466 MB all plain; 695 MB and 1.15 GB with the partials
     streamed in; 1.28 GB streaming), three calls, sampled windows."""
-    _windowed_run(cuda, 4, 3, (0,), P=P, N=N, n_win=6, width=1 << 16)
+    _windowed_run(cuda, "training", 3, (0,), P=P, N=N, n_win=6, width=1 << 16)
 
 
 def test_largest_rank_count_large_message(cuda):
     """P = 16 (the most ranks the library takes), 2^27 bf16 elements per rank."""
-    _windowed_run(cuda, 5, 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
+    _windowed_run(cuda, "headline_1GiB", 3, (0,), P=16, N=1 << 27, n_win=8, width=1 << 14)
 
 
 def test_fp32_partials_of_2GiB(cuda):
     """fp32 partials of 2^29 elements (2 GiB each, so byte offsets pass 2^31)."""
-    _windowed_run(cuda, 1, 3, (0,), P=2, N=1 << 29, n_win=8, width=1 << 14)
+    _windowed_run(cuda, "tiny", 3, (0,), P=2, N=1 << 29, n_win=8, width=1 << 14)
 
 
 @pytest.mark.parametrize("group", [64, 128])
 def test_larger_groups_full_size(cuda, group):
     """The group-size variants at the prefill size, where every kernel takes its
     two-chunks-per-lane launch (small messages take one)."""
-    _windowed_run(cuda, 2, 4, (0,), group=group)
+    _windowed_run(cuda, "prefill", 4, (0,), group=group)
 
 
 def test_full_size_without_compensation(cuda):
     """The plain two-rounding all-reduce (state untouched) at the prefill size."""
-    _windowed_run(cuda, 2, 4, (0,), compensate=False)
+    _windowed_run(cuda, "prefill", 4, (0,), compensate=False)
 
 
 # ---------------------------------------------------------------------------
@@ -587,13 +588,13 @@ def test_full_size_without_compensation(cuda):
 def test_sender_feedback_tiny_config_every_call(cuda, compensate):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    c = synth.CONFIGS[1]
-    P, N = c["P"], synth.numel(1)
+    c = synth.WORKLOADS["tiny"]
+    P, N = c["P"], synth.numel("tiny")
     st = _state(P, N, "f32", compensate, sender_feedback=True)
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     for t in range(c["calls"]):
-        raw, vals = synth.host_partials(1, 0, t)
+        raw, vals = synth.host_partials("tiny", 0, t)
         E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, sender_feedback=True)
         assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}") == 0
@@ -620,7 +621,7 @@ def test_sender_feedback_multi_tile_both_directions(cuda, P, dtype, group):
                 vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
                 raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
             else:
-                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+                raw, vals = synth.host_partials("training", d, t, P=P, n=N, dtype=dtype)
             E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, group=group, sender_feedback=True)
             assert _compare(_fetch(st, out, d), o, so, d, True, f"G={group} P={P} call {t} dir {d}") == 0
@@ -630,7 +631,7 @@ def test_sender_feedback_stage_entry_points_equal_reduce(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     P, N = 8, 32 * 4096
-    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    raw, _ = synth.host_partials("decode", 0, 0, P=P, n=N)
     parts = _upload(raw, "bf16", cuda)
     s1 = _state(P, N, "bf16", sender_feedback=True)
     s2 = _state(P, N, "bf16", sender_feedback=True)
@@ -648,7 +649,7 @@ def test_sender_feedback_stage_entry_points_equal_reduce(cuda):
 
 
 def test_sender_feedback_full_size(cuda):
-    _windowed_run(cuda, 2, 4, (0,), sender_feedback=True)
+    _windowed_run(cuda, "prefill", 4, (0,), sender_feedback=True)
 
 
 # ---------------------------------------------------------------------------
@@ -657,13 +658,13 @@ def test_sender_feedback_full_size(cuda):
 def test_bf16_state_tiny_config_every_call(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    c = synth.CONFIGS[1]
-    P, N = c["P"], synth.numel(1)
+    c = synth.WORKLOADS["tiny"]
+    P, N = c["P"], synth.numel("tiny")
     st = _state(P, N, "f32", state_bf16=True)
     so = eo.OracleState(N)
     out = torch.empty(N, dtype=torch.float32, device=cuda)
     for t in range(c["calls"]):
-        raw, vals = synth.host_partials(1, 0, t)
+        raw, vals = synth.host_partials("tiny", 0, t)
         E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, state_bf16=True)
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
@@ -686,7 +687,7 @@ def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
                 vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
                 raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
             else:
-                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+                raw, vals = synth.host_partials("training", d, t, P=P, n=N, dtype=dtype)
             E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, group=group, sender_feedback=sfb, state_bf16=True)
             assert _compare(_fetch(st, out, d), o, so, d, True,
@@ -696,14 +697,14 @@ def test_bf16_state_multi_tile_both_directions(cuda, P, dtype, group, sfb):
 def test_sender_feedback_bf16_state_headline_size(cuda):
     """1 GiB bf16 per rank, P = 8 (streaming cache policy), sender feedback with
     the bf16 state: three calls on the same partials, sampled windows."""
-    _windowed_run(cuda, 5, 3, (0,), same_partials=True, n_win=6, width=1 << 16, sender_feedback=True,
+    _windowed_run(cuda, "headline_1GiB", 3, (0,), same_partials=True, n_win=6, width=1 << 16, sender_feedback=True,
                   state_bf16=True, threads=6)
 
 
 @pytest.mark.parametrize("sfb", [False, True])
 def test_bf16_state_full_size(cuda, sfb):
     """Prefill size; with sender feedback the ranks' stage-1 errors are bf16 too."""
-    _windowed_run(cuda, 2, 6, (0,), state_bf16=True, sender_feedback=sfb)
+    _windowed_run(cuda, "prefill", 6, (0,), state_bf16=True, sender_feedback=sfb)
 
 
 # ---------------------------------------------------------------------------
@@ -712,13 +713,13 @@ def test_bf16_state_full_size(cuda, sfb):
 @pytest.mark.parametrize("compensate", [True, False])
 def test_bf16_output_tiny_config_every_call(cuda, compensate):
     import error_compensated_bit_echo_amd as E
-    c = synth.CONFIGS[1]
-    P, N = c["P"], synth.numel(1)
+    c = synth.WORKLOADS["tiny"]
+    P, N = c["P"], synth.numel("tiny")
     st = _state(P, N, "f32", compensate, out_bf16=True)
     so = eo.OracleState(N)
     out = _out_tensor(st, cuda)
     for t in range(c["calls"]):
-        raw, vals = synth.host_partials(1, 0, t)
+        raw, vals = synth.host_partials("tiny", 0, t)
         E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, out_bf16=True)
         assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}") == 0
@@ -740,7 +741,7 @@ def test_bf16_output_multi_tile_both_directions(cuda, P, dtype, group, sfb, sb16
                 vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
                 raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
             else:
-                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+                raw, vals = synth.host_partials("training", d, t, P=P, n=N, dtype=dtype)
             E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, group=group, sender_feedback=sfb, state_bf16=sb16, out_bf16=True)
             assert _compare(_fetch(st, out, d), o, so, d, True,
@@ -748,7 +749,7 @@ def test_bf16_output_multi_tile_both_directions(cuda, P, dtype, group, sfb, sb16
 
 
 def test_bf16_output_full_size(cuda):
-    _windowed_run(cuda, 2, 6, (0,), out_bf16=True)
+    _windowed_run(cuda, "prefill", 6, (0,), out_bf16=True)
 
 
 # ---------------------------------------------------------------------------
@@ -757,13 +758,13 @@ def test_bf16_output_full_size(cuda):
 @pytest.mark.parametrize("compensate", [True, False])
 def test_own_exact_tiny_config_every_call(cuda, compensate):
     import error_compensated_bit_echo_amd as E
-    c = synth.CONFIGS[1]
-    P, N = c["P"], synth.numel(1)
+    c = synth.WORKLOADS["tiny"]
+    P, N = c["P"], synth.numel("tiny")
     st = _state(P, N, "f32", compensate, own_exact=True)
     so = eo.OracleState(N)
     out = _out_tensor(st, cuda)
     for t in range(c["calls"]):
-        raw, vals = synth.host_partials(1, 0, t)
+        raw, vals = synth.host_partials("tiny", 0, t)
         E.echo_reduce(_upload(raw, "f32", cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(vals, so, eo.FWD, compensate=compensate, own_exact=True)
         assert _compare(_fetch(st, out, 0), o, so, 0, compensate, f"call {t}", own_exact=True) == 0
@@ -780,7 +781,7 @@ def test_own_exact_multi_tile_ragged(cuda, P, dtype):
     out = _out_tensor(st, cuda)
     for t in range(3):
         for d in (0, 1):
-            raw, vals = synth.host_partials(2, d, t, P=P, n=N, dtype=dtype)
+            raw, vals = synth.host_partials("prefill", d, t, P=P, n=N, dtype=dtype)
             E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, own_exact=True)
             assert _compare(_fetch(st, out, d), o, so, d, True, f"P={P} {dtype} call {t} dir {d}",
@@ -805,7 +806,7 @@ def test_own_exact_with_other_variants(cuda, P, dtype, group, sfb, comp, sb16, o
                 vals = (rng.integers(-12, 13, (P, N)) * 0.25).astype(F32)
                 raw = vals if dtype == "f32" else synth.f32_to_bf16_bits(vals)
             else:
-                raw, vals = synth.host_partials(4, d, t, P=P, n=N, dtype=dtype)
+                raw, vals = synth.host_partials("training", d, t, P=P, n=N, dtype=dtype)
             E.echo_reduce(_upload(raw, dtype, cuda), out, st, d)
             o = eo.echo_call(vals, so, d, compensate=comp, group=group, sender_feedback=sfb,
                              state_bf16=sb16, out_bf16=obf, own_exact=True)
@@ -821,7 +822,7 @@ def test_own_exact_fewer_groups_than_owners(cuda, P, N):
     so = eo.OracleState(N)
     out = _out_tensor(st, cuda)
     for t in range(3):
-        raw, vals = synth.host_partials(2, 0, t, P=P, n=N)
+        raw, vals = synth.host_partials("prefill", 0, t, P=P, n=N)
         E.echo_reduce(_upload(raw, "bf16", cuda), out, st, 0)
         o = eo.echo_call(vals, so, 0, own_exact=True)
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"P={P} N={N} call {t}", own_exact=True) == 0
@@ -835,7 +836,7 @@ def test_own_exact_stage_entry_points_and_graph(cuda):
     from error_compensated_bit_echo_amd import binding as B
     torch = _torch()
     P, N = 8, 64 * 4096 + 32 * 3
-    raw, _ = synth.host_partials(3, 0, 0, P=P, n=N)
+    raw, _ = synth.host_partials("decode", 0, 0, P=P, n=N)
     parts = _upload(raw, "bf16", cuda)
     kw = dict(own_exact=True, out_bf16=True)
     s1, s2, sg = _state(P, N, "bf16", **kw), _state(P, N, "bf16", **kw), _state(P, N, "bf16", **kw)
@@ -867,12 +868,12 @@ def test_own_exact_stage_entry_points_and_graph(cuda):
 
 
 def test_own_exact_full_size(cuda):
-    _windowed_run(cuda, 2, 6, (0,), own_exact=True)
+    _windowed_run(cuda, "prefill", 6, (0,), own_exact=True)
 
 
 def test_own_exact_headline_size(cuda):
     """1 GiB bf16 per rank, P = 8, the same partials every call."""
-    _windowed_run(cuda, 5, 4, (0,), same_partials=True, n_win=6, width=1 << 14, own_exact=True)
+    _windowed_run(cuda, "headline_1GiB", 4, (0,), same_partials=True, n_win=6, width=1 << 14, own_exact=True)
 
 
 def test_element_indices_beyond_2_32(cuda):
@@ -881,7 +882,7 @@ def test_element_indices_beyond_2_32(cuda):
     pass 2^32, 2^29 and 2^27, byte offsets pass 2^33.  Windows at both ends (the
     last one spans element 2^32), on the owner boundary and just below 2^32."""
     N, width = (1 << 32) + 96, 1 << 13
-    _windowed_run(cuda, 5, 2, (0,), P=2, N=N, n_win=4, width=width, state_bf16=True,
+    _windowed_run(cuda, "headline_1GiB", 2, (0,), P=2, N=N, n_win=4, width=width, state_bf16=True,
                   out_bf16=True, own_exact=True, extra_windows=((1 << 32) - 2 * width,))
 
 
@@ -891,8 +892,8 @@ def test_independent_states_on_two_streams(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     P1, N1, P2, N2 = 8, 32 * 4096 * 3, 3, 64 * 1024 + 192
-    raw1, _ = synth.host_partials(3, 0, 0, P=P1, n=N1)
-    raw2, _ = synth.host_partials(2, 1, 0, P=P2, n=N2, dtype="f32")
+    raw1, _ = synth.host_partials("decode", 0, 0, P=P1, n=N1)
+    raw2, _ = synth.host_partials("prefill", 1, 0, P=P2, n=N2, dtype="f32")
     p1, p2 = _upload(raw1, "bf16", cuda), _upload(raw2, "f32", cuda)
     cfg = [dict(P=P1, N=N1, dtype="bf16", kw=dict(own_exact=True)),
            dict(P=P2, N=N2, dtype="f32", kw=dict(state_bf16=True, out_bf16=True, group=64))]
@@ -924,7 +925,7 @@ def test_states_driven_from_two_host_threads(cuda):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     P, N = 4, 2048 * 17 + 96
-    parts = [_upload(synth.host_partials(4, d, 3, P=P, n=N)[0], "bf16", cuda) for d in (0, 1)]
+    parts = [_upload(synth.host_partials("training", d, 3, P=P, n=N)[0], "bf16", cuda) for d in (0, 1)]
 
     def drive(st, out, stream, dirs, log):
         torch.cuda.set_device(cuda)

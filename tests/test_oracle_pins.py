@@ -162,7 +162,7 @@ def test_quantizer_special_cases():
 def test_error_is_exact_and_bounded():
     st = eo.OracleState(2048)
     for t in range(8):
-        _, x = synth.host_partials(1, 0, t)
+        _, x = synth.host_partials("tiny", 0, t)
         o = eo.echo_call(x, st)
         V, B, r = o["V"].astype(F64), o["B"].astype(F64), o["r"].astype(F64)
         assert np.array_equal(r + B, V)
@@ -220,11 +220,11 @@ def test_payload_is_about_a_quarter_of_bf16():
 # ---------------------------------------------------------------------------
 # P5: closed form of the compensator
 # ---------------------------------------------------------------------------
-def _run(T, compensate, P=2, N=2048, cfg=1, same=False, beta_fast=0.5, beta_slow=0.95):
+def _run(T, compensate, P=2, N=2048, workload="tiny", same=False, beta_fast=0.5, beta_slow=0.95):
     st = eo.OracleState(N)
     outs = []
     for t in range(T):
-        _, x = synth.host_partials(cfg, 0, 0 if same else t, P=P, n=N)
+        _, x = synth.host_partials(workload, 0, 0 if same else t, P=P, n=N)
         outs.append(eo.echo_call(x, st, compensate=compensate,
                                  beta_fast=beta_fast, beta_slow=beta_slow))
     return outs
@@ -267,7 +267,7 @@ def test_no_compensation_grows_linearly_on_repeated_input():
 
 
 def test_single_rank_without_compensation_is_idempotent():
-    _, x = synth.host_partials(1, 0, 0, P=1, n=4096)
+    _, x = synth.host_partials("tiny", 0, 0, P=1, n=4096)
     o = eo.echo_call(x, None, compensate=False)
     assert np.array_equal(o["q1"][0], o["q2"])
     s1, s2 = o["scales1"][0], o["scales2"]
@@ -298,7 +298,7 @@ def test_two_roundings_for_every_P(P):
     # both quantizations land on exact grid points: nothing else may round
     assert np.array_equal(o["out"].astype(F64), exact_sum)
     # random data: error within one half-step per stage-1 rank plus one stage-2 half-step
-    _, xr = synth.host_partials(1, 0, 3, P=P, n=4096)
+    _, xr = synth.host_partials("tiny", 0, 3, P=P, n=4096)
     o = eo.echo_call(xr, None, compensate=False)
     bound = (np.sum(o["scales1"].astype(F64), axis=0) / 2 + o["scales2"].astype(F64) / 2)
     err = np.abs(o["out"].astype(F64) - eo.plain_sum(xr)).reshape(-1, 32).max(axis=1)
@@ -340,13 +340,13 @@ def _compare_exact(x, T, compensate, beta=(0.5, 0.95), group=32):
 
 @pytest.mark.parametrize("compensate", [True, False])
 def test_whole_call_matches_exact_rationals(compensate):
-    xs = [synth.host_partials(1, 0, t, P=2, n=64)[1] for t in range(16)]
+    xs = [synth.host_partials("tiny", 0, t, P=2, n=64)[1] for t in range(16)]
     _compare_exact(xs, 16, compensate)
 
 
 @pytest.mark.parametrize("group", [64, 128])
 def test_whole_call_matches_exact_rationals_larger_groups(group):
-    xs = [synth.host_partials(2, 0, t, P=3, n=256)[1] for t in range(6)]
+    xs = [synth.host_partials("prefill", 0, t, P=3, n=256)[1] for t in range(6)]
     _compare_exact(xs, 6, True, group=group)
     rng = np.random.default_rng(group)
     xs = [(rng.integers(-12, 13, (2, 256)) * 0.25).astype(F32) for _ in range(4)]
@@ -363,7 +363,7 @@ def test_whole_call_matches_exact_rationals_tie_rich():
 def test_whole_call_matches_exact_rationals_bf16_and_small_scales():
     xs = []
     for t in range(6):
-        bits, vals = synth.host_partials(2, 0, t, P=3, n=64)
+        bits, vals = synth.host_partials("prefill", 0, t, P=3, n=64)
         vals = vals.copy()
         vals[:, :32] *= F32(2.0 ** -120)  # scales near the bottom of the normal range
         xs.append(vals)
@@ -379,7 +379,7 @@ def _d_rms(outs):
 
 
 def test_bounded_accumulated_error_tiny_config():
-    T = synth.CONFIGS[1]["calls"]
+    T = synth.WORKLOADS["tiny"]["calls"]
     on, off = _run(T, True), _run(T, False)
     d_on, d_off = _d_rms(on), _d_rms(off)
     sig_r = np.sqrt(np.mean(np.stack([o["r"].astype(F64) for o in on]) ** 2))
@@ -419,7 +419,7 @@ def test_bounded_accumulated_error_deep_chain():
 # ---------------------------------------------------------------------------
 def test_group_aligned_windows_equal_whole_tensor():
     P, N = 3, 32 * 40
-    xs = [synth.host_partials(2, 0, t, P=P, n=N)[1] for t in range(5)]
+    xs = [synth.host_partials("prefill", 0, t, P=P, n=N)[1] for t in range(5)]
     st = eo.OracleState(N)
     whole = [eo.echo_call(x, st) for x in xs]
     for lo, hi in ((0, 32 * 7), (32 * 7, 32 * 8), (32 * 8, N)):
@@ -434,8 +434,8 @@ def test_group_aligned_windows_equal_whole_tensor():
 
 def test_directions_are_isolated_and_reset_is_fresh():
     N = 2048
-    fw = [synth.host_partials(4, 0, t, P=2, n=N)[1] for t in range(4)]
-    bw = [synth.host_partials(4, 1, t, P=2, n=N)[1] for t in range(4)]
+    fw = [synth.host_partials("training", 0, t, P=2, n=N)[1] for t in range(4)]
+    bw = [synth.host_partials("training", 1, t, P=2, n=N)[1] for t in range(4)]
     inter = eo.OracleState(N)
     outs_i = []
     for t in range(4):
@@ -463,12 +463,12 @@ def test_rejects_bad_input():
 
 
 def test_synth_recipe_is_deterministic_and_rounds_to_bf16():
-    a = synth.host_partials(2, 0, 5, P=2, n=4096)
-    b = synth.host_partials(2, 0, 5, P=2, n=4096)
+    a = synth.host_partials("prefill", 0, 5, P=2, n=4096)
+    b = synth.host_partials("prefill", 0, 5, P=2, n=4096)
     assert np.array_equal(a[0], b[0])
     bits, vals = a
     assert bits.dtype == np.uint16
-    raw = np.stack([synth.normal_f32(synth.seed_of(2, 0, 5, r), 4096, 0.02, 1e-3, 50.0)
+    raw = np.stack([synth.normal_f32(synth.seed_of("prefill", 0, 5, r), 4096, 0.02, 1e-3, 50.0)
                     for r in range(2)])
     # nearest bfloat16: no representable bf16 value is closer than the chosen one
     err = np.abs(vals.astype(F64) - raw.astype(F64))
@@ -487,7 +487,7 @@ def test_sender_feedback_matches_exact_rationals(compensate):
     mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
     se = [[Fraction(0)] * N for _ in range(P)]
     for t in range(T):
-        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        _, x = synth.host_partials("prefill", 0, t, P=P, n=N)
         o = eo.echo_call(x, st, compensate=compensate, sender_feedback=True)
         e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, sender_err=se)
         for r in range(P):
@@ -506,7 +506,7 @@ def test_sender_feedback_telescopes():
     lhs = [Fraction(0)] * N
     rounding = [Fraction(0)] * N
     for t in range(T):
-        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        _, x = synth.host_partials("tiny", 0, t, P=P, n=N)
         e_before = st.sender_err[0].copy() if st.sender_err[0] is not None else np.zeros((P, N), F32)
         o = eo.echo_call(x, st, sender_feedback=True)
         deq = eo.dequantize_groups(o["q1"].reshape(P, -1), o["scales1"].reshape(-1)).reshape(P, N)
@@ -531,7 +531,7 @@ def test_sender_feedback_bounds_end_to_end_error():
         acc = np.zeros(N, F64)
         rms = []
         for t in range(T):
-            _, x = synth.host_partials(1, 0, t, P=P, n=N)
+            _, x = synth.host_partials("tiny", 0, t, P=P, n=N)
             o = eo.echo_call(x, st, sender_feedback=sfb)
             acc += o["out"].astype(F64) - eo.plain_sum(x)
             rms.append(np.sqrt(np.mean(acc ** 2)))
@@ -573,7 +573,7 @@ def test_bf16_state_matches_exact_rationals(compensate):
     st = eo.OracleState(N)
     mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
     for t in range(T):
-        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        _, x = synth.host_partials("prefill", 0, t, P=P, n=N)
         o = eo.echo_call(x, st, compensate=compensate, state_bf16=True)
         e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, state_bf16=True)
         for key in ("S", "V", "B", "out"):
@@ -592,7 +592,7 @@ def test_bf16_output_matches_exact_rationals(compensate):
     st = eo.OracleState(N)
     mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
     for t in range(T):
-        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        _, x = synth.host_partials("prefill", 0, t, P=P, n=N)
         o = eo.echo_call(x, st, compensate=compensate, out_bf16=True)
         e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate, out_bf16=True)
         for key in ("S", "V", "B", "r", "out"):
@@ -611,7 +611,7 @@ def test_bf16_output_compensator_closed_form():
     st = eo.OracleState(N)
     outs = []
     for t in range(T):
-        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        _, x = synth.host_partials("tiny", 0, t, P=P, n=N)
         outs.append(eo.echo_call(x, st, out_bf16=True))
     assert all(np.all((o["out"].view(np.uint32) & 0xFFFF) == 0) for o in outs)
     r = np.stack([o["r"].astype(F64) for o in outs])
@@ -647,7 +647,7 @@ def test_own_exact_matches_exact_rationals(compensate, sfb):
     mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
     se = [[Fraction(0)] * N for _ in range(P)] if sfb else None
     for t in range(T):
-        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        _, x = synth.host_partials("prefill", 0, t, P=P, n=N)
         o = eo.echo_call(x, st, compensate=compensate, sender_feedback=sfb, own_exact=True)
         e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, compensate=compensate,
                          sender_err=se, own_exact=True)
@@ -685,7 +685,7 @@ def test_own_exact_single_contributor():
     """Only rank j non-zero: on j's own segment the sum is x_j itself, on the
     other segments it is x_j through one stage-1 rounding."""
     P, N = 4, 32 * 8
-    _, base = synth.host_partials(1, 0, 5, P=1, n=N)
+    _, base = synth.host_partials("tiny", 0, 5, P=1, n=N)
     segs = eo.owner_segments(N // 32, P)
     for j in range(P):
         x = np.zeros((P, N), F32)
@@ -700,7 +700,7 @@ def test_own_exact_single_contributor():
 
 
 def test_own_exact_single_rank_is_one_rounding():
-    _, x = synth.host_partials(1, 0, 2, P=1, n=4096)
+    _, x = synth.host_partials("tiny", 0, 2, P=1, n=4096)
     o = eo.echo_call(x, None, compensate=False, own_exact=True)
     q, s = eo.quantize_groups(x[0])
     assert np.array_equal(o["S"], x[0])
@@ -712,7 +712,7 @@ def test_own_exact_removes_one_rank_of_stage1_error():
     share exact leaves P - 1 of the P, so the owner-sum error shrinks by about
     sqrt((P - 1) / P)."""
     for P in (2, 4):
-        _, x = synth.host_partials(1, 0, 9, P=P, n=1 << 14)
+        _, x = synth.host_partials("tiny", 0, 9, P=P, n=1 << 14)
         exact = eo.plain_sum(x)
         e_all = eo.echo_call(x, None, compensate=False)["S"].astype(F64) - exact
         e_own = eo.echo_call(x, None, compensate=False, own_exact=True)["S"].astype(F64) - exact
@@ -724,7 +724,7 @@ def test_own_exact_window_with_the_message_split_equals_whole_message():
     """Groups are independent once the owner of each group is fixed: a window
     given the whole message's owner split reproduces the whole call there."""
     P, N, G = 3, 32 * 40, 32
-    _, x = synth.host_partials(1, 0, 4, P=P, n=N)
+    _, x = synth.host_partials("tiny", 0, 4, P=P, n=N)
     whole = eo.echo_call(x, eo.OracleState(N), own_exact=True)
     segs = eo.owner_segments(N // G, P)
     for g_lo, g_hi in ((0, 40), (5, 19), (13, 14), (12, 33)):
@@ -743,12 +743,12 @@ def test_reset_clears_the_sender_errors_too():
     P, N = 3, 32 * 20
     st = eo.OracleState(N)
     for t in range(3):
-        _, x = synth.host_partials(1, 0, t, P=P, n=N)
+        _, x = synth.host_partials("tiny", 0, t, P=P, n=N)
         eo.echo_call(x, st, sender_feedback=True)
     assert np.any(st.sender_err[0] != 0)
     st.reset(1)
     fresh = eo.OracleState(N)
-    _, x = synth.host_partials(1, 0, 7, P=P, n=N)
+    _, x = synth.host_partials("tiny", 0, 7, P=P, n=N)
     a = eo.echo_call(x, st, sender_feedback=True)
     b = eo.echo_call(x, fresh, sender_feedback=True)
     assert np.array_equal(a["out"], b["out"])
@@ -764,7 +764,7 @@ def test_bf16_state_with_sender_feedback_matches_exact_rationals(own):
     mf, ms = [Fraction(0)] * N, [Fraction(0)] * N
     se = [[Fraction(0)] * N for _ in range(P)]
     for t in range(T):
-        _, x = synth.host_partials(2, 0, t, P=P, n=N)
+        _, x = synth.host_partials("prefill", 0, t, P=P, n=N)
         o = eo.echo_call(x, st, sender_feedback=True, state_bf16=True, own_exact=own)
         e = ex.echo_call([_fr(x[r]) for r in range(P)], mf, ms, sender_err=se, state_bf16=True,
                          own_exact=own)
@@ -786,7 +786,7 @@ def test_bf16_sender_errors_still_bound_the_end_to_end_error():
         acc = np.zeros(N, F64)
         rms = []
         for t in range(T):
-            _, x = synth.host_partials(1, 0, t, P=P, n=N)
+            _, x = synth.host_partials("tiny", 0, t, P=P, n=N)
             o = eo.echo_call(x, st, sender_feedback=True, state_bf16=sb16)
             acc += o["out"].astype(F64) - eo.plain_sum(x)
             rms.append(np.sqrt(np.mean(acc ** 2)))
