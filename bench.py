@@ -493,14 +493,14 @@ def gemm_report(E, torch, dev) -> dict:
             E.echo_gemm_bf16(A, W, out)
 
         # sustained load first (clocks ramp up over the first tens of milliseconds),
-        # then five interleaved rounds of 20 calls per variant; the median round counts
+        # then five interleaved batches of 20 calls per variant; the median batch counts
         fns = (("fused", fused), ("ours_then_stage1", ours_unfused),
                ("library_then_stage1", library_unfused), ("ours_product_only", product_only))
         for _ in range(100):
             product_only()
             library_unfused()
         torch.cuda.synchronize()
-        rounds = {name: [] for name, _ in fns}
+        batches = {name: [] for name, _ in fns}
         reps = 20
         for _ in range(5):
             for name, fn in fns:
@@ -510,8 +510,8 @@ def gemm_report(E, torch, dev) -> dict:
                     fn()
                 b.record()
                 torch.cuda.synchronize()
-                rounds[name].append(a.elapsed_time(b) * 1e3 / reps)
-        t = {name: sorted(v)[len(v) // 2] for name, v in rounds.items()}
+                batches[name].append(a.elapsed_time(b) * 1e3 / reps)
+        t = {name: sorted(v)[len(v) // 2] for name, v in batches.items()}
         flop = 2.0 * P * M * K * H
         res.append({"P": P, "M": M, "K": K, "H": H, "us": {k: round(v, 2) for k, v in t.items()},
                     "TFLOPs": {k: round(flop / (v * 1e-6) / 1e12, 1) for k, v in t.items()},
