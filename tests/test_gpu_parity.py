@@ -97,6 +97,7 @@ def _special_values(P, N, rng):
     g[:, 4 % ng] = (rng.integers(-80, 80, (P, 32)) * 2.0 ** -149).astype(F32)  # subnormal
     g[:, 5 % ng] = (rng.integers(-3, 4, (P, 32)) * 2.0 ** -149).astype(F32)    # scale underflows
     g[:, 6 % ng, 1:] = 0.0                            # single nonzero element
+    g[:, 7 % ng] = (rng.integers(-127, 128, (P, 32)) * 2.0 ** -133).astype(F32)  # subnormal, exact in bf16
     return g.reshape(P, N)
 
 
@@ -104,9 +105,13 @@ EDGE_VARIANTS = [{}, {"own_exact": True, "out_bf16": True},
                  {"state_bf16": True, "sender_feedback": True, "group": 64}]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", range(len(EDGE_VARIANTS)))
 @pytest.mark.parametrize("case", ["ties", "special", "one_group", "fewer_groups_than_ranks"])
-def test_edge_cases(cuda, case, variant):
+def test_edge_cases(cuda, case, variant, dtype):
+    """Partials built to hit the quantizer's special cases, as fp32 and rounded
+    to bfloat16 (ties and the special groups stay exact or become other special
+    values: zeros, subnormals, single nonzero elements)."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     rng = np.random.default_rng(5)
@@ -121,14 +126,18 @@ def test_edge_cases(cuda, case, variant):
     kw = EDGE_VARIANTS[variant]
     if N % kw.get("group", 32):
         N = 2 * N if case == "one_group" else N + 32  # whole groups of 64
-    st = _state(P, N, "f32", **kw)
+    st = _state(P, N, dtype, **kw)
     so = eo.OracleState(N)
     out = _out_tensor(st, cuda)
     for t in range(6):
         x = gen(P, N, rng)
-        E.echo_reduce(_upload(x, "f32", cuda), out, st, E.ECHO_FWD)
+        raw = x
+        if dtype == "bf16":
+            raw = synth.f32_to_bf16_bits(x)
+            x = synth.bf16_bits_as_f32(raw)
+        E.echo_reduce(_upload(raw, dtype, cuda), out, st, E.ECHO_FWD)
         o = eo.echo_call(x, so, eo.FWD, **kw)
-        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} {kw} call {t}",
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} {kw} {dtype} call {t}",
                         own_exact=kw.get("own_exact", False)) == 0
 
 
