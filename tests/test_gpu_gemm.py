@@ -124,6 +124,59 @@ def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16):
             assert _compare(_fetch(st, out, d), o, so, d, True, f"call {t} dir {d}") == 0
 
 
+def _special_inputs(case, P, M, K, H, seed, dev):
+    """Inputs whose products hit the quantizer's special cases: zero rows (whole
+    zero groups) and groups with one nonzero column, or every partial scaled
+    by a power of two into huge, tiny or subnormal magnitudes."""
+    torch = _torch()
+    A, W = _inputs(P, M, K, H, seed, dev)
+    for r in range(P):
+        a, w = A[r].float(), W[r].float()
+        if case == "zeros_and_single_columns":
+            a[r::3] = 0.0                                   # these output rows are zero
+            h = torch.arange(H, device=dev)
+            w[((h // 32) % 2 == 0) & (h % 32 != 5 + r)] = 0.0  # every other group: one nonzero column
+        elif case == "huge":
+            w *= 2.0 ** 100
+        elif case == "tiny":
+            w *= 2.0 ** -120
+        else:  # subnormal partials (and subnormal weights)
+            a *= 2.0 ** -6
+            w *= 2.0 ** -126
+        A[r], W[r] = a.to(torch.bfloat16), w.to(torch.bfloat16)
+    return A, W
+
+
+@pytest.mark.parametrize("sfb", [False, True])
+@pytest.mark.parametrize("case", ["zeros_and_single_columns", "huge", "tiny", "subnormal"])
+@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 2048, 64, 2048)])
+def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
+    """The fused epilogue on special values, 64-row and 256-row tiles, with and
+    without sender feedback (bf16 state): whole calls against the oracle fed
+    the written-out partials."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = M * H
+    kw = {"sender_feedback": True, "state_bf16": True} if sfb else {}
+    st = _state(P, N, "bf16", **kw)
+    so = eo.OracleState(N)
+    out = torch.empty(N, dtype=torch.float32, device=cuda)
+    for t in range(3):
+        A, W = _special_inputs(case, P, M, K, H, 40 + t, cuda)
+        E.echo_gemm_stage1(A, W, st, E.ECHO_FWD)
+        E.echo_owner(st, E.ECHO_FWD)
+        E.echo_decode(out, st)
+        host = np.stack([p.reshape(-1).float().cpu().numpy() for p in _unfused(A, W)])
+        if case == "zeros_and_single_columns":
+            assert np.all(host.reshape(P, M, H)[0, 0::3] == 0)
+        if case == "subnormal" and t == 0:
+            sub = (host != 0) & (np.abs(host) < np.finfo(np.float32).tiny)
+            print(f"subnormal partials: {sub.mean():.3f} of all, {np.mean(host == 0):.3f} zero", flush=True)
+            assert sub.any()
+        o = eo.echo_call(host, so, eo.FWD, **kw)
+        assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
+
+
 def test_argument_errors(cuda):
     import ctypes
     import error_compensated_bit_echo_amd as E
