@@ -11,10 +11,11 @@
 // The payload is therefore bit-identical to stage 1 applied to the unfused
 // bf16 partial, which the same kernel writes when asked to.
 //
-// Tiling: a block computes a 256 x 128 tile of one rank's [M, H] partial with 8
-// wavefronts (128 x 128 with 4 where M is not a multiple of 256, 64 x 128 for
-// short products), each wavefront a 64 x 64 sub-tile of 2 x 2
-// v_mfma_f32_32x32x16_bf16 tiles (32 x 64, 1 x 2, in the 64-row tile).
+// Tiling: a block computes a 256 x 256 tile of one rank's [M, H] partial with 8
+// wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles
+// (256 x 128 tiles, 64 x 64 per wavefront, where H is not a multiple of 256 or
+// the larger tiles would leave CUs idle; 128 x 128 with 4 wavefronts where M is
+// not a multiple of 256; 64 x 128 for short products, 32 x 64 per wavefront).
 // K advances 64 at a time through two LDS slabs: while the matrix cores work on
 // one slab, the next one streams from global memory straight into the other
 // (global_load_lds_dwordx4: each wavefront instruction fills 1 KiB of LDS, eight
@@ -36,8 +37,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kTileN = 128, kTileK = 64;
-constexpr int kLdsN = kTileN + 8;    // bf16 per LDS row of the written-out tile (padded)
+constexpr int kTileK = 64;
 static_assert(kTileK == 64, "the slab loads assume 64-element (128-byte) rows");
 
 // Element offset of (row, 16-byte chunk c) in a swizzled slab of 64-element rows.
@@ -60,32 +60,39 @@ __device__ __forceinline__ void slab_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// BM: rows of the block tile; NW: wavefronts, laid out (NW/2) x 2 over the
-// tile, each computing (2 BM / NW) rows x 64 columns; S: LDS slabs in the
+// BM x TN: the block tile; NW: wavefronts, laid out (NW/2) x 2 over the
+// tile, each computing (2 BM / NW) rows x TN/2 columns; S: LDS slabs in the
 // pipeline (S - 1 K steps of loads in flight while one is multiplied).
 //   128 x 128, 4 wavefronts, 2 slabs (64 KiB): two blocks per CU;
 //   64 x 128, 4 wavefronts, 2 slabs: for short products that would otherwise
 //     leave CUs without a second block;
 //   256 x 128, 8 wavefronts, 2 slabs (96 KiB): one block per CU, half the
-//     slab loads per multiply-add of the 128-row tile (the fastest of these
-//     where M allows it; a third slab, which hides twice the load latency,
-//     measured slower).
+//     slab loads per multiply-add of the 128-row tile (a third slab, which
+//     hides twice the load latency, measured slower);
+//   256 x 256, 8 wavefronts, 2 slabs (128 KiB; 132 KiB when the written-out
+//     tile needs more): one block per CU, a third fewer slab bytes per
+//     multiply-add than 256 x 128 (the fastest of these where M and H allow
+//     it and the grid still covers the CUs).
 // SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
-template <int BM, int NW, int S, bool FUSED, int SFB>
+template <int BM, int TN, int NW, int S, bool FUSED, int SFB>
 __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   static_assert(FUSED || SFB == 0, "sender feedback only in the fused epilogue");
   constexpr int kThreads = 64 * NW;
   constexpr int RW = 2 * BM / NW;                  // rows per wavefront
   constexpr int MI = RW / 32;                      // 32-row MFMA tiles per wavefront
+  constexpr int CW = TN / 2;                       // columns per wavefront
+  constexpr int NJ = CW / 32;                      // 32-column MFMA tiles per wavefront
   static_assert(MI == 1 || MI == 2, "one or two 32-row MFMA tiles per wavefront");
-  constexpr int JA = BM / (8 * NW), JW = kTileN / (8 * NW);  // 1 KiB slab blocks per wavefront
-  static_assert(JA * 8 * NW == BM && JW * 8 * NW == kTileN, "slab blocks split evenly");
+  static_assert(TN == 128 || TN == 256, "128- or 256-column block tiles");
+  constexpr int JA = BM / (8 * NW), JW = TN / (8 * NW);  // 1 KiB slab blocks per wavefront
+  static_assert(JA * 8 * NW == BM && JW * 8 * NW == TN, "slab blocks split evenly");
   constexpr int kLoads = JA + JW;                  // global loads per wavefront per slab
   constexpr int kSlabA = BM * kTileK;              // bf16 of one A slab
-  constexpr int kSlab = (BM + kTileN) * kTileK;    // bf16 of one A + W slab
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[S * kSlab];
-  static_assert(S * kSlab >= BM * kLdsN, "the written-out tile reuses the slabs' LDS");
+  constexpr int kSlab = (BM + TN) * kTileK;        // bf16 of one A + W slab
+  constexpr int kLdsN = TN + 8;                    // bf16 per LDS row of the written-out tile (padded)
+  constexpr int kLdsTotal = (!FUSED && BM * kLdsN > S * kSlab) ? BM * kLdsN : S * kSlab;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsTotal];  // the written-out tile reuses the slabs
   const int r = blockIdx.z;
   const uint16_t* A = a.A[0];
   const uint16_t* W = a.W[0];
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
     }
   const int64_t K = a.K, H = a.H;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kTileN;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TN;
   const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
 
   // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks JA w ... of the A
@@ -123,11 +130,11 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
                                        16, 0, 0);
     }
   };
-  f32x16 acc[MI][2];
+  f32x16 acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -152,17 +159,17 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kTileK / 16; ++ks) {
       const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
-      bf16x8 af[MI], bf[2];
+      bf16x8 af[MI], bf[NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at(RW * wm + 32 * i + (lane & 31), c));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(64 * wn + 32 * j + (lane & 31), c));
+      for (int j = 0; j < NJ; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(CW * wn + 32 * j + (lane & 31), c));
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);  // C^T tile
     }
     // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
@@ -176,16 +183,16 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   // Epilogue straight from the accumulators (no LDS round trip).  The product
   // is computed transposed, C^T = W * A^T, so lane l of tile (i, j) holds
   // output row m = (BM/2) wm + 32 i + l % 32 and the 16 columns
-  // h = 64 wn + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4: a group of 32 columns of
+  // h = (TN/2) wn + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4: a group of 32 columns of
   // one row lives in lanes l and l ^ 32 (16 values each), and each run of 4
   // consecutive columns in one lane.
   const int half = lane >> 5;
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int64_t m = m0 + RW * wm + 32 * i + (lane & 31);
-      const int64_t e = m * H + n0 + 64 * wn + 32 * j;  // first element of the row's group
+      const int64_t e = m * H + n0 + CW * wn + 32 * j;  // first element of the row's group
       float v[16];  // the bf16-rounded partial, widened
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(static_cast<uint32_t>(bf16_rne(acc[i][j][k])) << 16);
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
         for (int q = 0; q < 4; ++q) {  // columns 8q + 4 half .. + 3
           const uint32_t lo = (__float_as_uint(v[4 * q + 1]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q]) >> 16);
           const uint32_t hi = (__float_as_uint(v[4 * q + 3]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q + 2]) >> 16);
-          *reinterpret_cast<uint2*>(lds + row * kLdsN + 64 * wn + 32 * j + 8 * q + 4 * half) = make_uint2(lo, hi);
+          *reinterpret_cast<uint2*>(lds + row * kLdsN + CW * wn + 32 * j + 8 * q + 4 * half) = make_uint2(lo, hi);
         }
       } else {
         // sender feedback: x' = fl(x + e) with the rank's carried stage-1 error of
@@ -273,16 +280,16 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
       }
     }
   if constexpr (!FUSED) {
-    // the bf16 tile from LDS to the rank's partial: 16 lanes per 256-byte row
+    // the bf16 tile from LDS to the rank's partial: TN / 8 lanes per row, 16 bytes each
     __syncthreads();
     uint16_t* out = a.out[0];
 #pragma unroll
     for (int q = 1; q < kMaxRanks; ++q)
       if (r == q) out = a.out[q];
 #pragma unroll
-    for (int u = 0; u < BM * kTileN / 8 / kThreads; ++u) {
+    for (int u = 0; u < BM * TN / 8 / kThreads; ++u) {
       const int chunk = t + kThreads * u;
-      const int row = chunk >> 4, cc = (chunk & 15) * 8;
+      const int row = chunk / (TN / 8), cc = (chunk % (TN / 8)) * 8;
       *reinterpret_cast<u32x4*>(out + (m0 + row) * H + n0 + cc) =
           *reinterpret_cast<const u32x4*>(lds + row * kLdsN + cc);
     }
@@ -293,33 +300,38 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 
 namespace {
 
-template <int BM, int NW, int S>
+template <int BM, int TN, int NW, int S>
 hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(a.H / kTileN), static_cast<unsigned>(a.M / BM),
+  const dim3 grid(static_cast<unsigned>(a.H / TN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
   if (!fused)
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, false, 0>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, false, 0>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err == nullptr)
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 0>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 0>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err_bf16)
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 2>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 2>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_gemm_k<BM, NW, S, true, 1>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 1>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 256-row tiles of 8 wavefronts when M allows them, else 128-row tiles, unless
-// 128-row tiles would give the 256 CUs fewer than two blocks each; then 64-row
-// tiles.  Measured at P = 4, M = 2048, K = 3072, H = 4096 (fused / product only,
-// us): 256 rows, 2 slabs 208.2 / 201.4; 128 rows, 2 slabs 214.5 / 204.8; 256 rows,
-// 3 slabs 226.0 / 208.7; 128 rows, 3 slabs (one block per CU) 280.6 / 267.3.
+// 256 x 256 tiles of 8 wavefronts when M and H allow them and every CU still
+// gets a block, else 256 x 128 tiles when M allows them, else 128 x 128, unless
+// 128 x 128 tiles would give the 256 CUs fewer than two blocks each; then
+// 64 x 128.  Measured at P = 4, M = 2048, K = 3072, H = 4096 (fused / product
+// only, us): 256 x 256, 2 slabs 188.0 / 183.3 against 215.4 / 206.6 for 256 x 128
+// on the same box (each K step moves 2/3 of the bytes per multiply-add);
+// 256 x 128, 2 slabs 208.2 / 201.4 against 128 x 128, 2 slabs 214.5 / 204.8;
+// 256 x 128, 3 slabs 226.0 / 208.7; 128 x 128, 3 slabs (one block per CU)
+// 280.6 / 267.3.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
-  const int64_t blocks128 = (a.M / kGemmTileM) * (a.H / kTileN) * P;
-  if (blocks128 < 512) return gemm_cfg<64, 4, 2>(a, P, fused, s);
-  if (a.M % 256 == 0) return gemm_cfg<256, 8, 2>(a, P, fused, s);
-  return gemm_cfg<128, 4, 2>(a, P, fused, s);
+  const int64_t blocks128 = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
+  if (blocks128 < 512) return gemm_cfg<64, 128, 4, 2>(a, P, fused, s);
+  if (a.M % 256 == 0 && a.H % 256 == 0 && blocks128 / 4 >= 256) return gemm_cfg<256, 256, 8, 2>(a, P, fused, s);
+  if (a.M % 256 == 0) return gemm_cfg<256, 128, 8, 2>(a, P, fused, s);
+  return gemm_cfg<128, 128, 4, 2>(a, P, fused, s);
 }
 
 }  // namespace echo

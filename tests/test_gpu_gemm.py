@@ -16,10 +16,11 @@ from parity_helpers import _compare, _fetch, _state, _torch
 
 pytestmark = pytest.mark.gpu
 
-# the first four launch 64-row tiles (fewer than 512 blocks of 128 x 128), the fifth 256-row tiles
-# (M a multiple of 256), the last 128-row tiles (M an odd multiple of 128)
+# the first four launch 64 x 128 tiles (fewer than 512 blocks of 128 x 128), the fifth 256 x 128 tiles
+# (M and H multiples of 256, but 256 x 256 tiles would leave CUs idle), the sixth 128 x 128 tiles
+# (M an odd multiple of 128), the last 256 x 256 tiles
 SHAPES = [(1, 128, 64, 128), (2, 256, 512, 384), (3, 384, 1024, 256), (8, 128, 3072, 512),
-          (2, 2048, 128, 2048), (2, 2176, 192, 2048)]
+          (2, 2048, 128, 2048), (2, 2176, 192, 2048), (4, 2048, 128, 2048)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
@@ -80,7 +81,7 @@ def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
 
 
 @pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (2, 2048, 128, 2048),
-                                     (2, 2176, 128, 2048)])
+                                     (2, 2176, 128, 2048), (4, 2048, 192, 2048)])
 def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
@@ -99,15 +100,15 @@ def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
 
 
+@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (4, 2048, 128, 2048)])
 @pytest.mark.parametrize("sb16", [False, True])
-def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16):
+def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16, P, M, K, H):
     """Sender feedback in the fused epilogue: each rank's carried stage-1 error
     (fp32, or bfloat16 with the bf16 state) is added to its product before the
     quantizer and updated after it, per direction; whole calls in both
     directions, interleaved, against the oracle fed the written-out partials."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
-    P, M, K, H = 3, 256, 512, 384
     N = M * H
     st = _state(P, N, "bf16", sender_feedback=True, state_bf16=sb16)
     so = eo.OracleState(N)
@@ -149,9 +150,9 @@ def _special_inputs(case, P, M, K, H, seed, dev):
 
 @pytest.mark.parametrize("sfb", [False, True])
 @pytest.mark.parametrize("case", ["zeros_and_single_columns", "huge", "tiny", "subnormal"])
-@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 2048, 64, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 2048, 64, 2048), (4, 2048, 64, 2048)])
 def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
-    """The fused epilogue on special values, 64-row and 256-row tiles, with and
+    """The fused epilogue on special values, 64 x 128, 256 x 128 and 256 x 256 tiles, with and
     without sender feedback (bf16 state): whole calls against the oracle fed
     the written-out partials."""
     import error_compensated_bit_echo_amd as E
