@@ -178,6 +178,57 @@ def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
 
 
+@pytest.mark.parametrize("P,M,K,H", [(8, 128, 256, 1024), (4, 2048, 128, 2048)])
+def test_fused_calls_in_a_graph_match_eager_calls(cuda, P, M, K, H):
+    """A graph holding a fused forward call (product with stage 1 and sender
+    feedback, owner step, decode), a fused backward call and the written-out
+    product, replayed 4 times on new activations copied into its input tensors
+    with eager work in between, leaves the same outputs, partials and carried
+    state as the same sequence issued eagerly."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    N = M * H
+    kw = {"sender_feedback": True, "state_bf16": True}
+    se, sg = _state(P, N, "bf16", **kw), _state(P, N, "bf16", **kw)
+    A0, W = _inputs(P, M, K, H, 50, cuda)
+    A1, _ = _inputs(P, M, K, H, 51, cuda, w=W)
+    oe, og = [torch.empty(N, dtype=torch.float32, device=cuda) for _ in range(2)]
+    oe1, og1 = [torch.empty(N, dtype=torch.float32, device=cuda) for _ in range(2)]
+    we = [torch.empty(M, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
+    wg = [torch.empty(M, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
+
+    def sequence(A0, A1, st, o, o1, written):
+        E.echo_gemm_stage1(A0, W, st, E.ECHO_FWD)
+        E.echo_owner(st, E.ECHO_FWD)
+        E.echo_decode(o, st)
+        E.echo_gemm_stage1(A1, W, st, E.ECHO_BWD)
+        E.echo_owner(st, E.ECHO_BWD)
+        E.echo_decode(o1, st)
+        E.echo_gemm_bf16(A0, W, written)
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sequence(A0, A1, sg, og, og1, wg)
+    torch.cuda.synchronize()
+    E.echo_reset(sg, 3)  # capture does not execute; start from a fresh state
+    for k in range(4):
+        N0, _ = _inputs(P, M, K, H, 60 + 2 * k, cuda, w=W)
+        N1, _ = _inputs(P, M, K, H, 61 + 2 * k, cuda, w=W)
+        for dst, src in zip(A0 + A1, N0 + N1):
+            dst.copy_(src)
+        sequence(N0, N1, se, oe, oe1, we)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oe, og) and torch.equal(oe1, og1), f"replay {k}"
+        assert all(torch.equal(a, b) for a, b in zip(we, wg)), f"replay {k} written-out product"
+        for d in (0, 1):
+            ve, vg = E.echo_debug_views(se, d), E.echo_debug_views(sg, d)
+            for key in ("m_fast", "m_slow", "sender_err"):
+                assert torch.equal(ve[key], vg[key]), f"replay {k} dir {d} {key}"
+        _ = (oe * 2).sum().item()  # unrelated eager work between replays
+
+
 def test_argument_errors(cuda):
     import ctypes
     import error_compensated_bit_echo_amd as E
