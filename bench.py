@@ -629,7 +629,7 @@ def cpu_baseline(parts, n_sample: int, gpu_window=None, **variant) -> dict:
     }
 
 
-def main():
+def make_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
@@ -656,7 +656,11 @@ def main():
     ap.add_argument("--config", choices=sorted(REPORTS) + ["all"],
                     help="instead of the 1 GiB headline, report latency, bandwidth and accuracy of "
                          "another workload (one JSON line each)")
-    args = ap.parse_args()
+    return ap
+
+
+def main():
+    args = make_parser().parse_args()
 
     if args.ingest_counters:
         rec = ingest_counters(*args.ingest_counters,
