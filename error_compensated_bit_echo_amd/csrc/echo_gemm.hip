@@ -322,7 +322,7 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 // 128 x 128 tiles would give the 256 CUs fewer than two blocks each; then
 // 64 x 128.  Measured at P = 4, M = 2048, K = 3072, H = 4096 (fused / product
 // only, us): 256 x 256, 2 slabs 188.0 / 183.3 against 215.4 / 206.6 for 256 x 128
-// on the same box (each K step moves 2/3 of the bytes per multiply-add);
+// on the same machine (each K step moves 2/3 of the bytes per multiply-add);
 // 256 x 128, 2 slabs 208.2 / 201.4 against 128 x 128, 2 slabs 214.5 / 204.8;
 // 256 x 128, 3 slabs 226.0 / 208.7; 128 x 128, 3 slabs (one block per CU)
 // 280.6 / 267.3.

@@ -303,7 +303,7 @@ hipError_t decode_u(const uint32_t* codes, const float* scales, void* out, int64
 // 466 MB and 3-8 % slower below; against streaming 7-14 % faster at 666-932 MB,
 // 2-4 % at 1.06-1.11 GB and equal at 1.2-1.33 GB, while streaming is 1-5 %
 // faster from 1.4 GB on (and at 1 GB for P = 16).  P = 2, 4, 8 and 16,
-// graph-replayed calls, each comparison measured on one box.
+// graph-replayed calls, each comparison measured on one machine.
 CallPolicy call_policy(int P, int64_t numel, bool bf16_input) {
   const double bytes = static_cast<double>(numel) * (P * ((bf16_input ? 2.0 : 4.0) + 0.625) + 21.25);
   if (bytes < 96e6 || bytes > 1200e6) return kCallStreaming;
