@@ -512,8 +512,20 @@ def gemm_report(E, torch, dev) -> dict:
                 torch.cuda.synchronize()
                 batches[name].append(a.elapsed_time(b) * 1e3 / reps)
         t = {name: sorted(v)[len(v) // 2] for name, v in batches.items()}
+        # what the timed fused kernel wrote must be stage 1 of the written-out product
+        ref = E.echo_init_state(E.EchoConfig.make(P, M * H, "bf16"), device=dev)
+        E.echo_gemm_stage1(A, W, st)
+        E.echo_gemm_bf16(A, W, out)
+        E.echo_stage1(flat, ref)
+        vf, vr = E.echo_debug_views(st), E.echo_debug_views(ref)
+        torch.cuda.synchronize()
+        same = torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
+        if not same:
+            raise RuntimeError(f"fused payload differs from stage 1 of the written-out product at "
+                               f"P={P} M={M} K={K} H={H}")
         flop = 2.0 * P * M * K * H
-        res.append({"P": P, "M": M, "K": K, "H": H, "us": {k: round(v, 2) for k, v in t.items()},
+        res.append({"P": P, "M": M, "K": K, "H": H, "payload_equals_stage1_of_written_out": same,
+                    "us": {k: round(v, 2) for k, v in t.items()},
                     "TFLOPs": {k: round(flop / (v * 1e-6) / 1e12, 1) for k, v in t.items()},
                     "bf16_peak_TFLOPs": 2500.0,
                     "partial_bytes_not_written_or_read": 2 * 2 * P * M * H})

@@ -4,12 +4,15 @@
  * partial buffers in the GPU's HBM and the int4 payload buffers standing in
  * for the wire.
  *
- * The method (described in prose, with no code or formulas, in the rit.work
- * blog post "echo-4-bit-gpu-communication", sections «Почему обычное 4-битное
- * суммирование портит модель» and «Как Echo возвращает ошибку в следующие
- * вызовы», and in the heraldofai.com article «Come Echo permette ai modelli AI
- * di grandi dimensioni di allenarsi più velocemente usando dati ultra-leggeri a
- * 4 bit», section «Come Echo evita che gli errori si accumulino»):
+ * The method is described in prose, with no code or formulas, on two pages,
+ * cited below as
+ *   Page R: the rit.work blog post "echo-4-bit-gpu-communication";
+ *   Page H: the heraldofai.com article «Come Echo permette ai modelli AI di
+ *           grandi dimensioni di allenarsi più velocemente usando dati
+ *           ultra-leggeri a 4 bit».
+ * In short (Page R, «Почему обычное 4-битное суммирование портит модель» and
+ * «Как Echo возвращает ошибку в следующие вызовы»; Page H, «Come Echo evita
+ * che gli errori si accumulino»):
  *   - every rank cuts its partial sum into owner segments and sends them as
  *     4-bit integers (here: groups of 32 elements, one fp32 scale per group;
  *     groups of 64 or 128 are a configurable variant);
@@ -44,10 +47,17 @@
  *     the state was created; that device must be current at every call.
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and is asynchronous; nothing synchronises the host.
- *   - Every argument is validated before anything is enqueued: on any error
- *     nothing is launched and the state is unchanged.  No exception crosses
- *     the ABI; the library allocates no device memory and keeps no global
- *     mutable state.
+ *   - Every argument is validated before anything is enqueued: on every
+ *     error but ECHO_ERR_HIP nothing is launched and the state is unchanged.
+ *     ECHO_ERR_HIP reports a failed HIP call.  An entry point that launches
+ *     several kernels (echo_reduce: stage 1, owner, decode; echo_reset: one
+ *     fill per region) stops at the first failed launch, and the launches
+ *     before it stay enqueued and run: after a failed owner launch the
+ *     stage-1 payload and, with sender_feedback, the ranks' stage-1 errors of
+ *     the direction have advanced; after a failed decode the compensator has
+ *     too and `out` is not written.  Reset the direction before using it
+ *     again.  No exception crosses the ABI; the library allocates no device
+ *     memory and keeps no global mutable state.
  *   - A state may be used by one stream at a time (not re-entrant).
  *   - Inputs must be finite; for NaN or Inf the results are unspecified.
  */
@@ -108,7 +118,10 @@ typedef struct echo_state echo_state; /* opaque host handle */
 
 typedef void* echo_stream_t; /* a hipStream_t */
 
-/* Bytes of device workspace a state needs: stage-1 payloads of the P ranks
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (ranks send
+ * their segments as 4-bit integers; the owner keeps fast and slow error
+ * estimates, separately for the forward and the backward pass).
+ * Bytes of device workspace a state needs: stage-1 payloads of the P ranks
  * (codes N/2 B + scales 4N/group B each), the broadcast payload, the two
  * compensator vectors of both directions (2 x 2 x 4N B, or 2 x 2 x 2N B with
  * state_bf16) and, with
@@ -116,7 +129,10 @@ typedef void* echo_stream_t; /* a hipStream_t */
  * (2 x P x 4N B, or 2 x P x 2N B with state_bf16), plus alignment slack.  Returns 0 for an invalid configuration and for N == 0. */
 size_t echo_workspace_bytes(const echo_config* cfg);
 
-/* Create a state over a caller-owned device workspace of `ws_bytes` bytes
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (the
+ * compensator's two smoothed estimates, one pair per pass direction, start
+ * from nothing).
+ * Create a state over a caller-owned device workspace of `ws_bytes` bytes
  * (at least echo_workspace_bytes(cfg); any alignment) and zero the
  * compensator of both directions on `stream`.  The workspace must outlive
  * the state; the library only carves it.  On success *out receives a host
@@ -126,7 +142,14 @@ size_t echo_workspace_bytes(const echo_config* cfg);
 echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_bytes,
                             echo_stream_t stream, echo_state** out);
 
-/* One whole all-reduce: echo_stage1, then echo_owner on direction `dir`,
+/* Source: Page R «Почему обычное 4-битное суммирование портит модель» (the
+ * all-reduce that adds the ranks' partial results of a tensor-parallel layer
+ * and hands every rank the total) with the arithmetic of «Как Echo возвращает
+ * ошибку в следующие вызовы»; Page H «Come Echo evita che gli errori si
+ * accumulino» (4-bit transfer, high-precision sum, at most two roundings).
+ * `dir` selects the forward or backward estimates, which Page R «Как Echo
+ * возвращает ошибку в следующие вызовы» keeps apart for the two passes.
+ * One whole all-reduce: echo_stage1, then echo_owner on direction `dir`,
  * then echo_decode.  partials: host array of P device pointers, each to N
  * contiguous elements of cfg.dtype, 16-byte aligned, read-only for the call.
  * out: device pointer to N fp32 (N bfloat16 with out_bf16), 16-byte aligned,
@@ -136,14 +159,20 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
 echo_status echo_reduce(const void* const* partials, void* out, echo_state* st,
                         echo_dir dir, echo_stream_t stream);
 
-/* Stage 1 on every rank: quantize each rank's partial to int4 codes and fp32
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (every GPU
+ * sends its segments as 4-bit integers).
+ * Stage 1 on every rank: quantize each rank's partial to int4 codes and fp32
  * group scales in the state's stage-1 payload buffers (the "wire").  `dir`
  * selects the ranks' stage-1 errors when sender_feedback is on (otherwise it
  * is only validated). */
 echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir dir,
                         echo_stream_t stream);
 
-/* Stage 1 fused into the producing product (the step before the all-reduce in
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (the authors
+ * fuse compensation, quantization and exchange into their kernels) and
+ * «Почему обычное 4-битное суммирование портит модель» (each GPU computes its
+ * part of a layer's product, which the all-reduce then adds).
+ * Stage 1 fused into the producing product (the step before the all-reduce in
  * a tensor-parallel layer: each rank's partial is the output of its slice of a
  * row-parallel product).  For every rank r the partial is
  * bf16(A_r * W_r^T), A_r [M, K] and W_r [H, K] bfloat16 row-major (W_r's rows
@@ -163,13 +192,19 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
 echo_status echo_gemm_stage1(const void* const* A, const void* const* W, int64_t M, int64_t K,
                              echo_state* st, echo_dir dir, echo_stream_t stream);
 
-/* The same product written out, for comparison: out[r] = bf16(A_r * W_r^T),
+/* Source: Page R «Почему обычное 4-битное суммирование портит модель» (each
+ * GPU computes its own part of the layer's result).
+ * The same product written out, for comparison: out[r] = bf16(A_r * W_r^T),
  * [M, H] bfloat16 row-major, for r < P (1..16).  Same shape rules; out[r] must
  * not overlap A or W.  Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_HIP. */
 echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* const* out, int32_t P,
                            int64_t M, int64_t K, int64_t H, echo_stream_t stream);
 
-/* Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (the owner of
+ * a segment restores the 4-bit values, adds them in high precision, measures
+ * the error its rounding just made and folds it into the fast and slow
+ * estimates); Page H «Come Echo evita che gli errori si accumulino».
+ * Owner stage for all segments: decode the P stage-1 payloads, sum in fp32,
  * apply the correction of direction `dir`, re-quantize into the broadcast
  * payload and update the compensator of `dir`.  partials: with own_exact, the
  * same P device pointers the preceding echo_stage1 received (the owners read
@@ -178,27 +213,38 @@ echo_status echo_gemm_bf16(const void* const* A, const void* const* W, void* con
 echo_status echo_owner(const void* const* partials, echo_state* st, echo_dir dir,
                        echo_stream_t stream);
 
-/* Every rank's decode of the broadcast payload into `out` (N fp32, or N
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (the
+ * compressed total is sent to the other GPUs, which restore it).
+ * Every rank's decode of the broadcast payload into `out` (N fp32, or N
  * bfloat16 with out_bf16; 16-byte aligned, not in the workspace). */
 echo_status echo_decode(void* out, const echo_state* st, echo_stream_t stream);
 
-/* Zero the compensator (and, with sender_feedback, the ranks' stage-1 errors)
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (separate
+ * estimates for the forward and the backward pass; each pass over the layer
+ * stack starts its own).
+ * Zero the compensator (and, with sender_feedback, the ranks' stage-1 errors)
  * of the directions in dir_mask (1 = fwd, 2 = bwd, 3 = both), e.g. at the
  * start of every pass over the layer stack.
  * Uses a fill kernel (no memset node), so it may be captured in a graph. */
 echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream);
 
-/* Free the host handle (not the workspace).  NULL is accepted. */
+/* Source: none on the pages (host bookkeeping of the state above).
+ * Free the host handle (not the workspace).  NULL is accepted. */
 void echo_destroy_state(echo_state* st);
 
-/* Bytes one rank would send per call over a real interconnect: rs = the
+/* Source: Page H «I fatti principali» (4-bit transfer at about a quarter of
+ * the 16-bit cost); Page R «Почему обычное 4-битное суммирование портит
+ * модель» (almost four times less data than 16-bit values).
+ * Bytes one rank would send per call over a real interconnect: rs = the
  * largest stage-1 payload share a rank sends to the other owners, ag = the
  * largest broadcast an owner sends to the other ranks, bf16 = a ring
  * all-reduce of the same message in bfloat16 (2(P-1)/P * 2N). */
 echo_status echo_wire_bytes(const echo_state* st, uint64_t* rs_per_rank, uint64_t* ag_per_rank,
                             uint64_t* bf16_allreduce_per_rank);
 
-/* Device pointers into the workspace, for inspection, checkpoint and restore
+/* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (the
+ * payloads on the wire and the two smoothed estimates the owner keeps).
+ * Device pointers into the workspace, for inspection, checkpoint and restore
  * of the state (copy m_fast/m_slow out and back). */
 typedef struct {
   const void* stage1_codes;    /* rank r: stage1_codes + r*stage1_codes_stride bytes, N/2 B  */
@@ -216,7 +262,8 @@ typedef struct {
 
 echo_status echo_debug_views(const echo_state* st, echo_dir dir, echo_views* out);
 
-/* Static description of a status code. */
+/* Source: none on the pages (error reporting of this library).
+ * Static description of a status code. */
 const char* echo_status_str(echo_status s);
 
 #ifdef __cplusplus

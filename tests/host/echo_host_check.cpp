@@ -285,6 +285,23 @@ void run_case(const Case& c, u64 ws_offset) {
     }
   }
 
+  // a launch that fails stops the call there: ECHO_ERR_HIP, the launches before
+  // it were made (and stay enqueued), none after it
+  for (int k = 0; k < 3; ++k) {
+    g_launches.clear();
+    g_attempts = 0;
+    g_fail_at = k;
+    CHECK(echo_reduce(parts, out, st, ECHO_BWD, nullptr) == ECHO_ERR_HIP, "reduce with launch %d failing", k);
+    CHECK(static_cast<int>(g_launches.size()) == k && g_attempts == k + 1,
+          "launch %d failing: %zu launches made, %d attempted", k, g_launches.size(), g_attempts);
+    g_launches.clear();
+    g_attempts = 0;
+    CHECK(echo_reset(st, 3, nullptr) == (k < (c.sfb ? 4 : 2) ? ECHO_ERR_HIP : ECHO_OK), "reset with fill %d failing", k);
+    CHECK(static_cast<int>(g_launches.size()) == std::min(k, c.sfb ? 4 : 2), "reset with fill %d failing: %zu fills", k,
+          g_launches.size());
+  }
+  g_fail_at = -1;
+
   // reset of one direction fills exactly that direction's carried state
   for (int mask = 1; mask <= 3; ++mask) {
     g_launches.clear();

@@ -9,6 +9,12 @@
 
 std::vector<HostLaunch> g_launches;
 int g_device = 0;
+int g_fail_at = -1;
+int g_attempts = 0;
+
+namespace {
+bool fails_now() { return g_attempts++ == g_fail_at; }
+}  // namespace
 
 extern "C" hipError_t hipGetDevice(int* device) {
   if (device == nullptr) return hipErrorInvalidValue;
@@ -21,6 +27,7 @@ namespace echo {
 CallPolicy call_policy(int, int64_t, bool) { return kCallStreaming; }
 
 hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, CallPolicy, hipStream_t) {
+  if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};
   l.kind = HostLaunch::kStage1;
   l.stage1 = a;
@@ -33,6 +40,7 @@ hipError_t launch_stage1(const Stage1Args& a, int P, bool bf16, int group, CallP
 
 hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, bool state_bf16,
                         bool own_exact, hipStream_t) {
+  if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};
   l.kind = HostLaunch::kOwner;
   l.owner = a;
@@ -47,6 +55,7 @@ hipError_t launch_owner(const OwnerArgs& a, int P, bool compensate, int group, b
 
 hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out, int64_t numel,
                          int group, bool out_bf16, bool, hipStream_t) {
+  if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};
   l.kind = HostLaunch::kDecode;
   l.codes = codes;
@@ -60,6 +69,7 @@ hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out, 
 }
 
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t) {
+  if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};
   l.kind = HostLaunch::kZero;
   l.out = p;
@@ -69,6 +79,7 @@ hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t) {
+  if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};
   l.kind = HostLaunch::kGemm;
   l.gemm = a;

@@ -22,3 +22,8 @@ struct HostLaunch {
 
 extern std::vector<HostLaunch> g_launches;
 extern int g_device;  // what hipGetDevice reports
+// Failure injection: the launch attempt whose index (counted from 0 since
+// g_attempts was last cleared) equals g_fail_at returns hipErrorLaunchFailure
+// and records nothing; -1 = every launch succeeds.
+extern int g_fail_at;
+extern int g_attempts;

@@ -28,6 +28,23 @@ def test_header_declares_the_api():
         assert n in names
 
 
+def test_every_entry_point_cites_its_source():
+    """Each declaration's comment names the page section that defines the
+    operation (Page R / Page H with a section title in guillemets), or says
+    that no passage of the pages defines it (host bookkeeping)."""
+    src = open(HEADER).read()
+    for name in declared_functions():
+        m = re.search(r"/\*((?:(?!\*/).)*?)\*/\s*(?:typedef struct \{.*?\} \w+;\s*)?[\w\s\*]*?\b" + name + r"\s*\(",
+                      src, flags=re.S)
+        assert m is not None, f"{name}: no comment right before its declaration"
+        comment = m.group(1)
+        src_line = re.search(r"Source:(.*?)(?:\.\s|\)\.|$)", comment, flags=re.S)
+        assert src_line is not None, f"{name}: no Source: line"
+        text = " ".join(src_line.group(1).split())
+        cited = re.search(r"Page [RH] «[^»]+»", text) is not None
+        assert cited or text.startswith("none on the pages"), f"{name}: {text!r}"
+
+
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()],

@@ -16,11 +16,29 @@ from parity_helpers import _compare, _fetch, _state, _torch
 
 pytestmark = pytest.mark.gpu
 
-# the first four launch 64 x 128 tiles (fewer than 512 blocks of 128 x 128), the fifth 256 x 128 tiles
-# (M and H multiples of 256, but 256 x 256 tiles would leave CUs idle), the sixth 128 x 128 tiles
-# (M an odd multiple of 128), the last 256 x 256 tiles
-SHAPES = [(1, 128, 64, 128), (2, 256, 512, 384), (3, 384, 1024, 256), (8, 128, 3072, 512),
-          (2, 2048, 128, 2048), (2, 2176, 192, 2048), (4, 2048, 128, 2048)]
+# Every block tile the launcher picks, each in its steady state: a K step
+# issues the loads of step + 1 into the slab that step - 1 read, which first
+# happens at the third step, so each tile runs at least 4 (and a ring of two
+# slabs is exercised over many turns).  The launcher takes
+#   64 x 128 when 128 x 128 tiles would give fewer than 512 blocks,
+#   256 x 256 when M and H are multiples of 256 and a quarter of those blocks still covers the 256 CUs,
+#   256 x 128 when M is a multiple of 256, and 128 x 128 otherwise.
+SHAPES = [
+    (1, 128, 64, 128),      # 64 x 128, 1 K step
+    (2, 256, 512, 384),     # 64 x 128, 8 steps
+    (3, 384, 1024, 256),    # 64 x 128, 16 steps
+    (8, 128, 3072, 512),    # 64 x 128, 48 steps
+    (2, 2048, 128, 2048),   # 256 x 128, 2 steps
+    (2, 2048, 512, 2048),   # 256 x 128, 8 steps
+    (2, 2176, 192, 2048),   # 128 x 128, 3 steps
+    (2, 2176, 512, 2048),   # 128 x 128, 8 steps
+    (4, 2048, 128, 2048),   # 256 x 256, 2 steps
+    (4, 2048, 576, 2048),   # 256 x 256, 9 steps (an odd count: the last step reads the other slab)
+    (4, 2048, 3072, 4096),  # 256 x 256, 48 steps: the product the benchmark times
+]
+# one shape per tile configuration in its steady state, for the whole-call tests
+STEADY = [(2, 256, 512, 384), (8, 128, 3072, 512), (2, 2048, 512, 2048), (2, 2176, 512, 2048),
+          (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
@@ -81,7 +99,7 @@ def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
 
 
 @pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (2, 2048, 128, 2048),
-                                     (2, 2176, 128, 2048), (4, 2048, 192, 2048)])
+                                     (2, 2176, 128, 2048), (4, 2048, 192, 2048)] + STEADY)
 def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
@@ -100,7 +118,8 @@ def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
 
 
-@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (4, 2048, 128, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (4, 2048, 128, 2048), (2, 2048, 512, 2048),
+                                     (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)])
 @pytest.mark.parametrize("sb16", [False, True])
 def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16, P, M, K, H):
     """Sender feedback in the fused epilogue: each rank's carried stage-1 error

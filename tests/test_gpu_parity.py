@@ -417,11 +417,15 @@ def _window_segments(N, P, group, w, width):
 
 def _windowed_run(cuda, workload, calls, directions, same_partials=False, n_win=6, width=1 << 14,
                   P=None, N=None, compensate=True, sender_feedback=False, state_bf16=False,
-                  out_bf16=False, own_exact=False, extra_windows=(), group=32, threads=1):
+                  out_bf16=False, own_exact=False, extra_windows=(), group=32, threads=1,
+                  sequential=False):
     """The configuration's calls at full size; the oracle checks sampled windows.
     P and N override the configuration's rank count and message size (same
     value distribution and dtype); extra_windows adds group-aligned window starts;
-    threads > 1 runs the oracle on the windows in parallel (each has its own state)."""
+    threads > 1 runs the oracle on the windows in parallel (each has its own state).
+    With several directions the calls alternate between them, or, with
+    sequential, all calls of the first direction come before the second's (a
+    forward pass, then a backward pass)."""
     import error_compensated_bit_echo_amd as E
     torch = _torch()
     c = synth.WORKLOADS[workload]
@@ -438,38 +442,49 @@ def _windowed_run(cuda, workload, calls, directions, same_partials=False, n_win=
                                    for g0, _ in per[1:]})
     so = {w: eo.OracleState(width) for w in wins}
     parts = None
-    for t in range(calls):
-        for d in directions:
-            if parts is None or not same_partials:
-                parts = None
-                parts = synth.device_partials(workload, d, t, P=P, n=N, device=cuda)
-            E.echo_reduce(parts, out, st, d)
-            torch.cuda.synchronize()
+    order = [(t, d) for d in directions for t in range(calls)] if sequential else \
+        [(t, d) for t in range(calls) for d in directions]
+    for i, (t, d) in enumerate(order):
+        if parts is None or not same_partials:
+            parts = None
+            parts = synth.device_partials(workload, d, t, P=P, n=N, device=cuda)
+        E.echo_reduce(parts, out, st, d)
+        torch.cuda.synchronize()
 
-            def check(w):
-                host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
-                o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
-                                 state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group,
-                                 segments=_window_segments(N, P, group, w, width) if own_exact else None)
-                g = _fetch(st, out, d, w, w + width)
-                return _compare(g, o, so[w], d, compensate,
-                                f"{workload} P={P} N={N} call {t} dir {d} window {w}", own_exact)
+        def check(w):
+            host = np.stack([p[w:w + width].float().cpu().numpy() for p in parts])
+            o = eo.echo_call(host, so[w], d, compensate=compensate, sender_feedback=sender_feedback,
+                             state_bf16=state_bf16, out_bf16=out_bf16, own_exact=own_exact, group=group,
+                             segments=_window_segments(N, P, group, w, width) if own_exact else None)
+            g = _fetch(st, out, d, w, w + width)
+            return _compare(g, o, so[w], d, compensate,
+                            f"{workload} P={P} N={N} call {t} dir {d} window {w}", own_exact)
 
-            if threads > 1:
-                from concurrent.futures import ThreadPoolExecutor
-                with ThreadPoolExecutor(max_workers=threads) as ex:
-                    assert sum(ex.map(check, wins)) == 0
-            else:
-                assert sum(check(w) for w in wins) == 0
-        print(f"{workload} P={P} N={N}: call {t} ok", flush=True)
+        if threads > 1:
+            from concurrent.futures import ThreadPoolExecutor
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                assert sum(ex.map(check, wins)) == 0
+        else:
+            assert sum(check(w) for w in wins) == 0
+        if i + 1 == len(order) or order[i + 1][0] != t:
+            print(f"{workload} P={P} N={N}: call {t} ok", flush=True)
 
 
 def test_prefill_config_full_size(cuda):
-    _windowed_run(cuda, "prefill", 24, (0,))
+    """All 72 calls (36 layers, attention and MLP) of the prefill workload on one
+    forward state, sampled windows after every call."""
+    _windowed_run(cuda, "prefill", synth.WORKLOADS["prefill"]["calls"], (0,))
+
+
+def test_training_config_full_size(cuda):
+    """A training step: the 56 forward calls on the forward state, then the 56
+    backward calls on the backward state."""
+    _windowed_run(cuda, "training", synth.WORKLOADS["training"]["calls"], (0, 1), sequential=True)
 
 
 def test_training_config_full_size_interleaved(cuda):
-    _windowed_run(cuda, "training", 12, (0, 1))
+    """The same 56 + 56 calls with the directions alternating call by call."""
+    _windowed_run(cuda, "training", synth.WORKLOADS["training"]["calls"], (0, 1))
 
 
 def test_headline_config_full_size(cuda):
