@@ -10,6 +10,7 @@ _BINDING_NAMES = {
     "EchoConfig", "EchoError", "EchoState", "ECHO_FWD", "ECHO_BWD",
     "echo_workspace_bytes", "echo_init_state", "echo_reduce", "echo_stage1",
     "echo_owner", "echo_decode", "echo_gemm_stage1", "echo_gemm_bf16", "echo_reset", "echo_destroy_state",
+    "echo_reduce_noalloc", "ECHO_STATIC_SCRATCH_BYTES",
     "echo_wire_bytes", "echo_debug_views", "echo_status_str", "library_path",
     "load_library",
 }

@@ -110,6 +110,7 @@ def load_library():
                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]),
         "echo_decode": (i32, [vp, vp, vp]),
         "echo_reset": (i32, [vp, i32, vp]),
+        "echo_reduce_noalloc": (i32, [cfgp, ctypes.POINTER(vp), vp, vp, vp, vp, vp]),
         "echo_destroy_state": (None, [vp]),
         "echo_wire_bytes": (i32, [vp, u64p, u64p, u64p]),
         "echo_debug_views": (i32, [vp, i32, ctypes.POINTER(EchoViews)]),
@@ -298,6 +299,35 @@ def echo_decode(out, state: EchoState, stream=None):
     optr = _out_ptr(out, state)
     _check(load_library().echo_decode(optr, state.handle, _stream_handle(stream, state.device)),
            "echo_decode")
+    return out
+
+
+ECHO_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def echo_reduce_noalloc(cfg: EchoConfig, partials: Sequence, out, m_fast=None, m_slow=None, sender_err=None,
+                        stream=None):
+    """One all-reduce through the entry point that allocates nothing: the
+    payloads go to the library's static scratch and the carried state is the
+    caller's tensors (m_fast, m_slow: N fp32, or bfloat16 with state_bf16;
+    sender_err: [P, N] with sender feedback), advanced in place."""
+    import torch
+    P, N = cfg.P, cfg.numel
+    want = torch.bfloat16 if cfg.dtype == ECHO_BF16 else torch.float32
+    if len(partials) != P or any(t.dtype != want or t.numel() != N or not t.is_contiguous() for t in partials):
+        raise EchoError(ECHO_ERR_ARG, f"expected {P} contiguous {want} partials of {N} elements")
+    sdt = torch.bfloat16 if cfg.state_bf16 else torch.float32
+    for name, t, n in (("m_fast", m_fast, N), ("m_slow", m_slow, N), ("sender_err", sender_err, P * N)):
+        if t is not None and (t.dtype != sdt or t.numel() != n or not t.is_contiguous()):
+            raise EchoError(ECHO_ERR_ARG, f"{name} must be a contiguous {sdt} tensor of {n} elements")
+    odt = torch.bfloat16 if cfg.out_bf16 else torch.float32
+    if out.dtype != odt or out.numel() != N or not out.is_contiguous():
+        raise EchoError(ECHO_ERR_ARG, f"out must be a contiguous {odt} tensor of {N} elements")
+    arr = (ctypes.c_void_p * P)(*[t.data_ptr() for t in partials])
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(load_library().echo_reduce_noalloc(ctypes.byref(cfg), arr, out.data_ptr(), ptr(m_fast), ptr(m_slow),
+                                              ptr(sender_err), _stream_handle(stream, out.device)),
+           "echo_reduce_noalloc")
     return out
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libecho.so")
 SOURCES = ["echo_kernels.hip"] + [f"echo_owner_p{lo}_{lo + 1}.hip" for lo in range(1, 17, 2)] + \
-    ["echo_gemm.hip", "echo_api.hip"]
+    ["echo_gemm.hip", "echo_scratch.hip", "echo_api.hip"]
 HEADERS = ["echo_internal.h", "echo_div7.h", "echo_quant.h", "echo_device.h", "echo_owner.h"]
 ARCH = "gfx950"
 

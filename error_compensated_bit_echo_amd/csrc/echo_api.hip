@@ -6,6 +6,13 @@
 #include "echo.h"
 #include "echo_internal.h"
 
+namespace echo {
+// The library's static scratch of ECHO_STATIC_SCRATCH_BYTES on `device` (which
+// must be current): its device address, looked up on the first call per device
+// and kept (echo_scratch.hip).
+hipError_t static_scratch(int device, void** ptr);
+}  // namespace echo
+
 struct echo_state {
   echo_config cfg;
   int device;
@@ -59,6 +66,17 @@ Layout make_layout(const echo_config& c) {
   // sender feedback: every rank's stage-1 error, per direction, after the state
   L.total = L.off_sender + (c.sender_feedback ? 2 * P * L.err_bytes : 0);
   return L;
+}
+
+// The payload regions of a state (stage-1 codes and scales of every rank, the
+// broadcast codes and scales) in the layout L, from `base` (256-byte aligned).
+void carve_payload(echo_state* st, char* base, const Layout& L) {
+  st->codes1 = reinterpret_cast<uint32_t*>(base + L.off_codes1);
+  st->scales1 = reinterpret_cast<float*>(base + L.off_scales1);
+  st->codes1_stride_bytes = static_cast<int64_t>(L.codes1_stride);
+  st->scales1_stride_bytes = static_cast<int64_t>(L.scales1_stride);
+  st->codes2 = reinterpret_cast<uint32_t*>(base + L.off_codes2);
+  st->scales2 = reinterpret_cast<float*>(base + L.off_scales2);
 }
 
 echo_status check_cfg(const echo_config* c) {
@@ -209,12 +227,7 @@ echo_status echo_init_state(const echo_config* cfg, void* workspace, size_t ws_b
   if (cfg->numel > 0) {
     const Layout L = make_layout(*cfg);
     char* base = reinterpret_cast<char*>(align_up(reinterpret_cast<uintptr_t>(workspace)));
-    st->codes1 = reinterpret_cast<uint32_t*>(base + L.off_codes1);
-    st->scales1 = reinterpret_cast<float*>(base + L.off_scales1);
-    st->codes1_stride_bytes = static_cast<int64_t>(L.codes1_stride);
-    st->scales1_stride_bytes = static_cast<int64_t>(L.scales1_stride);
-    st->codes2 = reinterpret_cast<uint32_t*>(base + L.off_codes2);
-    st->scales2 = reinterpret_cast<float*>(base + L.off_scales2);
+    carve_payload(st, base, L);
     for (int d = 0; d < 2; ++d) {
       st->m_fast[d] = reinterpret_cast<float*>(base + L.off_state + (2 * d) * L.vec_bytes);
       st->m_slow[d] = reinterpret_cast<float*>(base + L.off_state + (2 * d + 1) * L.vec_bytes);
@@ -359,6 +372,68 @@ echo_status echo_reduce(const void* const* partials, void* out, echo_state* st, 
   return run_decode(out, st, s);
 }
 
+echo_status echo_reduce_noalloc(const echo_config* cfg, const void* const* partials, void* out, void* m_fast,
+                                void* m_slow, void* sender_err, echo_stream_t stream) {
+  echo_status e = check_cfg(cfg);
+  if (e != ECHO_OK) return e;
+  if (cfg->numel == 0) return ECHO_OK;
+  // the payloads go to the static scratch: only messages whose payloads fit
+  const Layout L = make_layout(*cfg);
+  if (L.off_state > ECHO_STATIC_SCRATCH_BYTES) return ECHO_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ECHO_ERR_HIP;
+  void* scratch = nullptr;
+  if (echo::static_scratch(dev, &scratch) != hipSuccess || scratch == nullptr) return ECHO_ERR_HIP;
+
+  // a state on the stack over the scratch, with the caller's carried vectors
+  // standing in for both directions' (nothing is allocated)
+  echo_state st{};
+  st.cfg = *cfg;
+  st.device = dev;
+  st.policy = echo::call_policy(cfg->P, cfg->numel, cfg->dtype == ECHO_BF16);
+  st.ws = static_cast<char*>(scratch);
+  st.ws_bytes = L.off_state;
+  carve_payload(&st, st.ws, L);
+  const size_t N = static_cast<size_t>(cfg->numel);
+  const size_t vb = (cfg->state_bf16 ? 2 : 4) * N;  // one carried vector
+  const size_t eb = static_cast<size_t>(cfg->P) * vb;  // the ranks' stage-1 errors
+  if (cfg->compensate) {
+    if (m_fast == nullptr || m_slow == nullptr || !aligned16(m_fast) || !aligned16(m_slow)) return ECHO_ERR_ARG;
+    if (overlaps(m_fast, vb, m_slow, vb)) return ECHO_ERR_ARG;
+  } else {
+    m_fast = m_slow = nullptr;  // not touched without compensation
+  }
+  if (cfg->sender_feedback) {
+    if (sender_err == nullptr || !aligned16(sender_err)) return ECHO_ERR_ARG;
+    if (overlaps(sender_err, eb, m_fast, m_fast ? vb : 0) || overlaps(sender_err, eb, m_slow, m_slow ? vb : 0))
+      return ECHO_ERR_ARG;
+  } else if (sender_err != nullptr) {
+    return ECHO_ERR_ARG;
+  }
+  for (int d = 0; d < 2; ++d) {
+    st.m_fast[d] = static_cast<float*>(m_fast);
+    st.m_slow[d] = static_cast<float*>(m_slow);
+    st.sender_err[d] = static_cast<float*>(sender_err);
+  }
+  st.err_words = static_cast<int64_t>(vb / 4);  // rank r's errors at sender_err + r * N elements
+  if ((e = check_partials(partials, &st)) != ECHO_OK) return e;
+  if ((e = check_out(out, &st, partials)) != ECHO_OK) return e;
+  // the carried vectors overlap neither the partials nor the output
+  const size_t pb = N * elem_bytes(*cfg), ob = N * (cfg->out_bf16 ? 2 : 4);
+  const void* carried[3] = {m_fast, m_slow, sender_err};
+  const size_t cb[3] = {vb, vb, eb};
+  for (int k = 0; k < 3; ++k) {
+    if (carried[k] == nullptr) continue;
+    if (overlaps(carried[k], cb[k], out, ob) || overlaps(carried[k], cb[k], st.ws, st.ws_bytes)) return ECHO_ERR_ARG;
+    for (int r = 0; r < cfg->P; ++r)
+      if (overlaps(carried[k], cb[k], partials[r], pb)) return ECHO_ERR_ARG;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((e = run_stage1(partials, &st, 0, s)) != ECHO_OK) return e;
+  if ((e = run_owner(partials, &st, 0, s)) != ECHO_OK) return e;
+  return run_decode(out, &st, s);
+}
+
 echo_status echo_reset(echo_state* st, int dir_mask, echo_stream_t stream) {
   echo_status e = check_state(st);
   if (e != ECHO_OK) return e;
@@ -427,7 +502,8 @@ const char* echo_status_str(echo_status s) {
     case ECHO_ERR_SHAPE:
       return "invalid shape (P outside [1,16], group not 32/64/128, numel not a multiple of the group or too large)";
     case ECHO_ERR_DTYPE: return "invalid dtype";
-    case ECHO_ERR_WORKSPACE: return "workspace missing or too small";
+    case ECHO_ERR_WORKSPACE:
+      return "workspace missing or too small (echo_reduce_noalloc: the payloads exceed the static scratch)";
     case ECHO_ERR_STATE: return "null state, or another device is current";
     case ECHO_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";

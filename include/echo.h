@@ -57,7 +57,8 @@
  *     the direction have advanced; after a failed decode the compensator has
  *     too and `out` is not written.  Reset the direction before using it
  *     again.  No exception crosses the ABI; the library allocates no device
- *     memory and keeps no global mutable state.
+ *     memory and keeps no global mutable state, apart from the static
+ *     scratch of echo_reduce_noalloc.
  *   - A state may be used by one stream at a time (not re-entrant).
  *   - Inputs must be finite; for NaN or Inf the results are unspecified.
  */
@@ -218,6 +219,39 @@ echo_status echo_owner(const void* const* partials, echo_state* st, echo_dir dir
  * Every rank's decode of the broadcast payload into `out` (N fp32, or N
  * bfloat16 with out_bf16; 16-byte aligned, not in the workspace). */
 echo_status echo_decode(void* out, const echo_state* st, echo_stream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * One whole all-reduce, the same kernels and results as echo_reduce on a
+ * state whose carried vectors held what m_fast, m_slow and sender_err hold,
+ * but with no state handle and no workspace.  The stage-1 payloads of the P
+ * ranks and the broadcast payload go to a scratch buffer the library holds on
+ * each device: a static device array of ECHO_STATIC_SCRATCH_BYTES, kept from
+ * the first call on a device until the process ends.  The call allocates
+ * nothing, on the device or on the host.
+ *   cfg: as for echo_init_state.  The payloads take
+ *     P * (A(N/2) + A(4N/group)) + A(N/2) + A(4N/group) bytes, A(x) = x
+ *     rounded up to a multiple of 256; a larger message returns
+ *     ECHO_ERR_WORKSPACE before anything is launched.  (64 MiB holds, e.g.,
+ *     P = 4 with N = 2^24 elements, or P = 8 with N = 2^23.)
+ *   partials, out: as for echo_reduce.
+ *   m_fast, m_slow: the carried estimates of the direction the call belongs
+ *     to, N fp32 each (N bfloat16 with state_bf16), read and advanced in
+ *     place; ignored (may be NULL) when cfg->compensate is 0.  A direction
+ *     starts from zeroed vectors: zero them (e.g. with a fill kernel) to reset.
+ *   sender_err: with sender_feedback, the P ranks' carried stage-1 errors of
+ *     that direction, rank r at element offset r*N (fp32, or bfloat16 with
+ *     state_bf16), read and advanced in place; NULL otherwise.
+ * Every device pointer 16-byte aligned and on the current device; no two of
+ * out, m_fast, m_slow, sender_err and the partials overlap.  No part of the
+ * scratch needs to start at zero (every call writes each payload before it
+ * reads it); it keeps the last call's payloads.  All calls on one device
+ * share it: calls that overlap in time on one device (two streams, two host
+ * threads) race and must be serialised by the caller.  Errors as for
+ * echo_reduce, plus ECHO_ERR_WORKSPACE for a message beyond the scratch. */
+#define ECHO_STATIC_SCRATCH_BYTES (((size_t)64) << 20)
+echo_status echo_reduce_noalloc(const echo_config* cfg, const void* const* partials, void* out,
+                                void* m_fast, void* m_slow, void* sender_err, echo_stream_t stream);
 
 /* Source: Page R «Как Echo возвращает ошибку в следующие вызовы» (separate
  * estimates for the forward and the backward pass; each pass over the layer

@@ -204,6 +204,97 @@ void check_zero_covers(const HostLaunch& l, const std::vector<const Region*>& wa
   for (const Region* w : want) CHECK(w && inside(*w, z), "fill misses %s", w ? w->what.c_str() : "?");
 }
 
+// echo_reduce_noalloc: the same three launches as echo_reduce, with the
+// payloads carved from the static scratch exactly as a state carves them from
+// its workspace, and the caller's carried vectors in place of the state's.
+void check_noalloc(const Case& c, const std::vector<Region>& rs, const void* const* parts, void* out) {
+  const echo_config cfg = make_cfg(c);
+  const u64 N = static_cast<u64>(c.N), G = static_cast<u64>(c.group), P = static_cast<u64>(c.P);
+  auto al = [](u64 x) { return (x + 255) / 256 * 256; };
+  const u64 payload = P * (al(N / 2) + al(4 * (N / G))) + al(N / 2) + al(4 * (N / G));
+  const u64 sv = c.sb16 ? 2 : 4;
+  const u64 mf = 1ull << 51, ms = mf + al(sv * N) + 4096, se = ms + al(sv * N) + 4096;
+  void* m_fast = fake(mf);
+  void* m_slow = fake(ms);
+  void* serr = c.sfb ? fake(se) : nullptr;
+  g_launches.clear();
+  const echo_status got = echo_reduce_noalloc(&cfg, parts, out, m_fast, m_slow, serr, nullptr);
+  if (payload > ECHO_STATIC_SCRATCH_BYTES) {
+    CHECK(got == ECHO_ERR_WORKSPACE && g_launches.empty(), "no-alloc call beyond the scratch (%llu B)", payload);
+    return;
+  }
+  CHECK(got == ECHO_OK, "no-alloc call");
+  // the expected regions: the state's payload layout moved to the scratch, the caller's vectors
+  const Region* base = find(rs, "codes1[0]");
+  std::vector<Region> nr;
+  for (const Region& r : rs)
+    if (r.what.rfind("codes", 0) == 0 || r.what.rfind("scales", 0) == 0)
+      nr.push_back({r.what, r.lo - base->lo + kFakeScratch, r.hi - base->lo + kFakeScratch});
+  const Region scratch{"scratch", kFakeScratch, kFakeScratch + payload};
+  for (const Region& r : nr) CHECK(inside(r, scratch), "%s outside the scratch's payload bytes", r.what.c_str());
+  for (const char* dn : {"fwd", "bwd"}) {
+    const u64 f = c.compensate ? mf : 0, sl = c.compensate ? ms : 0;  // not passed without compensation
+    nr.push_back({std::string("m_fast ") + dn, f, f + sv * N});
+    nr.push_back({std::string("m_slow ") + dn, sl, sl + sv * N});
+    for (u64 r = 0; c.sfb && r < P; ++r)
+      nr.push_back({std::string("sender_err ") + dn + "[" + std::to_string(r) + "]", se + r * sv * N,
+                    se + (r + 1) * sv * N});
+  }
+  const Region anywhere{"", 0, ~0ull};
+  CHECK(g_launches.size() == 3, "no-alloc call launches three kernels (%zu)", g_launches.size());
+  if (g_launches.size() == 3) {
+    CHECK(g_launches[0].kind == HostLaunch::kStage1 && g_launches[1].kind == HostLaunch::kOwner &&
+              g_launches[2].kind == HostLaunch::kDecode,
+          "no-alloc launch order");
+    check_stage1(g_launches[0], c, nr, parts, 0, anywhere);
+    check_owner(g_launches[1], c, nr, parts, 0);
+    check_decode(g_launches[2], c, nr, out);
+  }
+  // a failing launch stops the call there
+  for (int k = 0; k < 3; ++k) {
+    g_launches.clear();
+    g_attempts = 0;
+    g_fail_at = k;
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, m_slow, serr, nullptr) == ECHO_ERR_HIP &&
+              static_cast<int>(g_launches.size()) == k,
+          "no-alloc call with launch %d failing", k);
+  }
+  g_fail_at = -1;
+  // bad arguments launch nothing
+  g_launches.clear();
+  const void* part_in_scratch[echo::kMaxRanks];
+  std::memcpy(part_in_scratch, parts, sizeof(part_in_scratch));
+  part_in_scratch[0] = fake(kFakeScratch + 256);
+  CHECK(echo_reduce_noalloc(&cfg, part_in_scratch, out, m_fast, m_slow, serr, nullptr) == ECHO_ERR_ARG,
+        "partial in the scratch");
+  CHECK(echo_reduce_noalloc(&cfg, parts, fake(kFakeScratch), m_fast, m_slow, serr, nullptr) == ECHO_ERR_ARG,
+        "output in the scratch");
+  CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, m_slow, c.sfb ? nullptr : fake(se), nullptr) == ECHO_ERR_ARG,
+        "sender errors given exactly when sender feedback is off");
+  if (c.compensate) {
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, nullptr, m_slow, serr, nullptr) == ECHO_ERR_ARG, "null m_fast");
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, fake(mf + 8), m_slow, serr, nullptr) == ECHO_ERR_ARG,
+          "misaligned m_fast");
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, fake(mf + 16), serr, nullptr) == ECHO_ERR_ARG,
+          "m_slow over m_fast");
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, const_cast<void*>(parts[c.P - 1]), serr, nullptr) ==
+              ECHO_ERR_ARG,
+          "m_slow over a partial");
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, out, m_slow, serr, nullptr) == ECHO_ERR_ARG, "m_fast over the output");
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, fake(kFakeScratch + 512), m_slow, serr, nullptr) == ECHO_ERR_ARG,
+          "m_fast in the scratch");
+  }
+  if (c.sfb) {
+    CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, m_slow, fake(se + 2), nullptr) == ECHO_ERR_ARG,
+          "misaligned sender errors");
+    if (c.compensate)
+      CHECK(echo_reduce_noalloc(&cfg, parts, out, m_fast, m_slow, fake(ms + 16), nullptr) == ECHO_ERR_ARG,
+            "sender errors over m_slow");
+  }
+  CHECK(echo_reduce_noalloc(nullptr, parts, out, m_fast, m_slow, serr, nullptr) == ECHO_ERR_ARG, "null config");
+  CHECK(g_launches.empty(), "bad no-alloc arguments launched %zu kernels", g_launches.size());
+}
+
 void run_case(const Case& c, u64 ws_offset) {
   char buf[200];
   std::snprintf(buf, sizeof(buf), "P=%d N=%lld G=%d %s comp=%d sfb=%d sb16=%d obf=%d own=%d off=%llu", c.P,
@@ -368,6 +459,8 @@ void run_case(const Case& c, u64 ws_offset) {
     CHECK(rs_b == largest_send && ag_b == (c.P - 1) * largest_seg && bf_b == (2 * (c.P - 1) * 2 * N) / c.P,
           "wire bytes %llu %llu %llu", (u64)rs_b, (u64)ag_b, (u64)bf_b);
   }
+
+  check_noalloc(c, rs, parts, out);
 
   // the fused product writes the same stage-1 regions
   if (c.dtype == ECHO_BF16 && c.group == 32 && !c.own && N % (128 * 128) == 0) {

@@ -78,6 +78,12 @@ hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t) {
   return hipSuccess;
 }
 
+// the static scratch: a fake device address far from every other fake buffer
+hipError_t static_scratch(int, void** ptr) {
+  *ptr = reinterpret_cast<void*>(static_cast<uintptr_t>(kFakeScratch));
+  return hipSuccess;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t) {
   if (fails_now()) return hipErrorLaunchFailure;
   HostLaunch l{};

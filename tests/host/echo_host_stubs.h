@@ -26,4 +26,9 @@ extern int g_device;  // what hipGetDevice reports
 // g_attempts was last cleared) equals g_fail_at returns hipErrorLaunchFailure
 // and records nothing; -1 = every launch succeeds.
 extern int g_fail_at;
+// Where the stand-in of the library's static scratch lives.
+constexpr unsigned long long kFakeScratch = 1ull << 50;
+namespace echo {
+hipError_t static_scratch(int device, void** ptr);
+}
 extern int g_attempts;
