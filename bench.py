@@ -173,6 +173,33 @@ def _graph_us(E, torch, parts, out, st, direction, reps):
     return [a.elapsed_time(b) * 1e3 / GRAPH_CALLS for a, b in ev], g
 
 
+def _stage_graph_us(E, torch, parts, out, st, reps) -> dict:
+    """Median GPU time per launch of each stage alone (stage 1, owner, decode),
+    GRAPH_CALLS back-to-back launches captured in one graph, over ``reps``
+    replays (forward direction)."""
+    stages = {"stage1": lambda: E.echo_stage1(parts, st, E.ECHO_FWD),
+              "owner": lambda: E.echo_owner(st, E.ECHO_FWD),
+              "decode": lambda: E.echo_decode(out, st)}
+    res = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(GRAPH_CALLS):
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        res[name] = round(_pct([a.elapsed_time(b) * 1e3 / GRAPH_CALLS for a, b in ev], 0.5), 2)
+    return res
+
+
 def _wall_us(E, torch, parts, out, st, direction, reps):
     """Host-clock time per call of ``reps`` back-to-back eager calls."""
     torch.cuda.synchronize()
@@ -322,6 +349,7 @@ def decode_report(E, synth, torch, dev) -> dict:
     eager = [a.elapsed_time(b) * 1e3 for a, b in ev_e]
     graph = [a.elapsed_time(b) * 1e3 for a, b in ev_g]
     g32, _ = _graph_us(E, torch, pbuf, gout, gst, E.ECHO_FWD, 20)
+    stage_us = _stage_graph_us(E, torch, pbuf, gout, gst, 20)
     alg = N * (P * 3.25 + 21.25)
     return {
         "config": "decode", "P": P, "numel_per_rank": N, "input_dtype": "bf16", "layers": L,
@@ -333,6 +361,10 @@ def decode_report(E, synth, torch, dev) -> dict:
                         "graph_32_calls_median": round(_pct(g32, 0.5), 2),
                         "graph_32_calls_p90": round(_pct(g32, 0.9), 2)},
         "GBps_alg_graph_32_calls": round(alg / (_pct(g32, 0.5) * 1e-6) / 1e9, 1),
+        # each stage alone, 32 back-to-back launches in one graph: their sum against the call's
+        # per-call time says whether the three-kernel call spends time between its kernels
+        "us_per_launch_graph_32_launches_of_one_stage": stage_us,
+        "us_per_call_minus_sum_of_stages": round(_pct(g32, 0.5) - sum(stage_us.values()), 2),
         "graph_replay_equals_eager_every_layer": graph_equal,
         "rel_rms_err_vs_exact_allreduce_chain": rel,
     }
@@ -532,6 +564,56 @@ def gemm_report(E, torch, dev) -> dict:
     return {"config": "gemm", "shapes": res}
 
 
+def trace_gaps(trace_csv: str, kernels_per_call: int = 3, calls_per_replay: int = GRAPH_CALLS) -> dict:
+    """Per-call kernel time against the gaps between kernels, from a rocprofv3
+    kernel trace of this benchmark: the library's dispatches are split into runs
+    that follow one another with no host gap (over 20 us), and the runs made of
+    whole graph replays (calls_per_replay calls of kernels_per_call kernels) are
+    summarised per call: the span from the first kernel's start to the last one's
+    end, the summed kernel durations, and the rest, the time between kernels."""
+    import csv
+    import statistics
+
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if any(k in name for k in ("echo_quant_pack_k", "echo_owner_k", "echo_unpack")):
+                kind = "stage1" if "quant_pack" in name else ("owner" if "owner" in name else "decode")
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind))
+    rows.sort()
+    runs, cur = [], []
+    for r in rows:
+        if cur and r[0] - cur[-1][1] > 20_000:  # ns
+            runs.append(cur)
+            cur = []
+        cur.append(r)
+    if cur:
+        runs.append(cur)
+    per_replay = kernels_per_call * calls_per_replay
+    span, busy, dur, gap_after = [], [], {}, {}
+    for run in runs:
+        if len(run) < per_replay or len(run) % per_replay:
+            continue
+        calls = len(run) // kernels_per_call
+        span.append((run[-1][1] - run[0][0]) / calls / 1e3)
+        busy.append(sum(e - s for s, e, _ in run) / calls / 1e3)
+        for i, (s, e, k) in enumerate(run):
+            dur.setdefault(k, []).append((e - s) / 1e3)
+            if i + 1 < len(run):
+                gap_after.setdefault(k, []).append((run[i + 1][0] - e) / 1e3)
+    if not span:
+        raise SystemExit(f"{trace_csv}: no run of whole {calls_per_replay}-call graph replays found")
+    med = statistics.median
+    return {"runs": len(span), "calls_per_run": [len(r) // kernels_per_call for r in runs
+                                                  if len(r) >= per_replay and len(r) % per_replay == 0][:4],
+            "us_per_call_span_median": round(med(span), 3),
+            "us_per_call_kernels_median": round(med(busy), 3),
+            "us_per_call_between_kernels_median": round(med(span) - med(busy), 3),
+            "kernel_us_median": {k: round(med(v), 3) for k, v in dur.items()},
+            "gap_us_after_kernel_median": {k: round(med(v), 3) for k, v in gap_after.items()}}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -665,6 +747,9 @@ def make_parser() -> argparse.ArgumentParser:
                     help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, WRITE_SIZE) of this benchmark, then exit")
     ap.add_argument("--counter-command", default="", help="command recorded with --ingest-counters")
+    ap.add_argument("--trace-gaps", metavar="KERNEL_TRACE_CSV",
+                    help="split the per-call time of the graph replays in a rocprofv3 kernel trace of this "
+                         "benchmark into kernel time and time between kernels, then exit")
     ap.add_argument("--config", choices=sorted(REPORTS) + ["all"],
                     help="instead of the 1 GiB headline, report latency, bandwidth and accuracy of "
                          "another workload (one JSON line each)")
@@ -684,6 +769,10 @@ def main():
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
+        return
+
+    if args.trace_gaps:
+        print(json.dumps(trace_gaps(args.trace_gaps)))
         return
 
     if args.gpus != 1:
