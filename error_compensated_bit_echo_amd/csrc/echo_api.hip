@@ -264,9 +264,15 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
 
 namespace {
 
+// The product kernel addresses each block's row panels of A and W (up to 256
+// rows of K bf16) through 32-bit buffer offsets: K up to 2^21 keeps a panel
+// within 1 GiB.
+constexpr int64_t kGemmMaxK = int64_t(1) << 21;
+
 bool gemm_shape_ok(int64_t M, int64_t K, int64_t H) {
   return M > 0 && K > 0 && H > 0 && M % echo::kGemmTileM == 0 && H % echo::kGemmTileN == 0 &&
-         K % echo::kGemmTileK == 0 && M / echo::kGemmTileM <= 65535 && H / echo::kGemmTileN <= INT32_MAX;
+         K % echo::kGemmTileK == 0 && K <= kGemmMaxK && M / echo::kGemmTileM <= 65535 &&
+         H / echo::kGemmTileN <= INT32_MAX;
 }
 
 echo_status gemm_inputs(const void* const* A, const void* const* W, int P, echo::GemmArgs* a) {

@@ -18,8 +18,10 @@
 // not a multiple of 256; 64 x 128 for short products, 32 x 64 per wavefront).
 // K advances 64 at a time through two LDS slabs: while the matrix cores work on
 // one slab, the next one streams from global memory straight into the other
-// (global_load_lds_dwordx4: each wavefront instruction fills 1 KiB of LDS, eight
-// 128-byte rows, with no register staging), so each K step needs one barrier.
+// (buffer_load_dwordx4 ... lds through a buffer resource over the block's row
+// panel: each wavefront instruction fills 1 KiB of LDS, eight 128-byte rows,
+// with no register staging), so each K step needs one barrier.  Within a K step
+// the fragments of the four 16-deep sub-steps are double-buffered in registers.
 // The slabs are unpadded; within a row the 16-byte chunk c of row r sits in slot
 // c ^ ((r / 2) % 8), which spreads the 32 rows a fragment read touches over all
 // LDS banks.  (Measured at P = 4, M = 2048, K = 3072, H = 4096: 11 % faster than
@@ -28,6 +30,8 @@
 // supplies A[l % 32][8 (l / 32) + i] and B[8 (l / 32) + i][l % 32], i < 8, and
 // accumulator v of lane l is C[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
 #pragma clang fp contract(off)
+
+#include <type_traits>
 
 #include "echo_device.h"
 
@@ -40,6 +44,46 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTileK = 64;
 static_assert(kTileK == 64, "the slab loads assume 64-element (128-byte) rows");
 
+// Fourth word of a raw buffer resource: 32-bit data format (any nonzero format
+// does for these loads; a zero format would make every load return zero).
+constexpr int kBufferWord3 = 0x00020000;
+
+// A raw buffer resource over `bytes` bytes from `base`, and one 16-byte-per-lane
+// load through it straight into LDS (lane l's 16 bytes land at lds + 16 l bytes;
+// an offset at or past `bytes` reads zeros).  The slab loads use these rather
+// than global_load_lds: the compiler counts a global (FLAT-encoded) load into
+// LDS as pending LDS traffic too, so every wait for fragment reads in the K loop
+// also waited for the next slab's loads (measured 4-5 % slower).  The builtins
+// exist only for the device; the host pass, which also compiles the kernel
+// bodies, gets stand-ins it never runs.
+struct BufRsrc {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ BufRsrc buffer_rsrc(const void* base, int32_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return BufRsrc{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferWord3)};
+#else
+  (void)base;
+  (void)bytes;
+  return BufRsrc{};
+#endif
+}
+__device__ __forceinline__ void buffer_load_lds16(BufRsrc r, uint16_t* lds, uint32_t voffset, uint32_t soffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r.r, (__attribute__((address_space(3))) void*)lds, 16, voffset,
+                                           soffset, 0, 0);
+#else
+  (void)r;
+  (void)lds;
+  (void)voffset;
+  (void)soffset;
+#endif
+}
+
+// s_waitcnt immediate that waits for every outstanding LDS access of this
+// wavefront (lgkmcnt 0) and not for vector-memory operations or exports.
+constexpr int kLdsDrained = 0xC07F;
+
 // Element offset of (row, 16-byte chunk c) in a swizzled slab of 64-element rows.
 __device__ __forceinline__ int slab_at(int row, int c) { return row * kTileK + 8 * (c ^ ((row >> 1) & 7)); }
 
@@ -47,6 +91,8 @@ __device__ __forceinline__ int slab_at(int row, int c) { return row * kTileK + 8
 // this wavefront are outstanding (lgkm and export counts not waited on):
 // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15.
 constexpr int vmcnt_at_most(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// The same, and every outstanding LDS access too (lgkmcnt 0).
+constexpr int vmcnt_at_most_lds_drained(int n) { return vmcnt_at_most(n) & ~(15 << 8); }
 
 // Workgroup barrier for the slab pipeline.  __syncthreads() would also make
 // every wavefront wait for all its outstanding global loads (its release fence
@@ -109,26 +155,36 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 
   // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks JA w ... of the A
   // slab and JW w ... of the W slab; in block i lane l writes slot l, i.e. row
-  // 8i + l/8, slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row
+  // 8i + l/8, slot l % 8, which holds chunk (l % 8) ^ ((row / 2) % 8) of that row.
+  // The loads go through buffer resources over the block's row panels of A and
+  // W (BM or TN rows of K elements; under 2^31 bytes for the K the launcher
+  // accepts): a lane's byte offset within the panel is fixed, the K step's is
+  // a scalar offset.
   const int wave = t >> 6;
-  auto issue = [&](int buf, int64_t k0) {
-    uint16_t* As = lds + buf * kSlab;
-    uint16_t* Ws = As + kSlabA;
-    const int sub = (lane & 7);
+  const BufRsrc rA = buffer_rsrc(A + m0 * K, static_cast<int32_t>(BM * K * 2));
+  const BufRsrc rW = buffer_rsrc(W + n0 * K, static_cast<int32_t>(TN * K * 2));
+  uint32_t offA[JA], offW[JW];
+  {
+    const int sub = lane & 7;
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
-      const int i = JA * wave + j;
-      const int row = 8 * i + (lane >> 3);
-      __builtin_amdgcn_global_load_lds(A + (m0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), As + 512 * i,
-                                       16, 0, 0);
+      const int row = 8 * (JA * wave + j) + (lane >> 3);
+      offA[j] = static_cast<uint32_t>((row * K + 8 * (sub ^ ((row >> 1) & 7))) * 2);
     }
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
-      const int i = JW * wave + j;
-      const int row = 8 * i + (lane >> 3);
-      __builtin_amdgcn_global_load_lds(W + (n0 + row) * K + k0 + 8 * (sub ^ ((row >> 1) & 7)), Ws + 512 * i,
-                                       16, 0, 0);
+      const int row = 8 * (JW * wave + j) + (lane >> 3);
+      offW[j] = static_cast<uint32_t>((row * K + 8 * (sub ^ ((row >> 1) & 7))) * 2);
     }
+  }
+  auto issue = [&](int buf, int64_t k0) {
+    uint16_t* As = lds + buf * kSlab;
+    uint16_t* Ws = As + kSlabA;
+    const uint32_t kb = static_cast<uint32_t>(k0 * 2);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) buffer_load_lds16(rA, As + 512 * (JA * wave + j), offA[j], kb);
+#pragma unroll
+    for (int j = 0; j < JW; ++j) buffer_load_lds16(rW, Ws + 512 * (JW * wave + j), offW[j], kb);
   };
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -140,7 +196,15 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 
   // K step `it` multiplies slab it % S; the loads of step it + S - 1 are issued
   // at its start into the slab step it - 1 used, which every wavefront has
-  // finished reading at the barrier that ended step it - 1
+  // finished reading: each waits for its own LDS reads before the barrier that
+  // ends a step.  The fragments of a step's four 16-deep sub-steps are
+  // double-buffered in registers: the reads of sub-step k + 1 go out before the
+  // MFMAs of sub-step k, and the reads of the next slab's first sub-step right
+  // after the barrier, before the last sub-step's MFMAs.  (The compiler's own
+  // wait before a sub-step's MFMAs would be for every outstanding LDS read, the
+  // new ones included; each sub-step therefore first drains the reads issued a
+  // sub-step earlier, which have had the MFMAs between to land, and its MFMAs
+  // need no wait.)
   const int64_t steps = K / kTileK;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -150,35 +214,69 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
   slab_barrier();
-  for (int64_t it = 0; it < steps; ++it) {
-    const int cur = static_cast<int>(it % S);
-    const bool more = it + S - 1 < steps;
-    if (more) issue(static_cast<int>((it + S - 1) % S), (it + S - 1) * kTileK);  // in flight below
-    const uint16_t* As = lds + cur * kSlab;
+  bf16x8 af[2][MI], bf[2][NJ];
+  auto read_frags = [&](auto buf, const uint16_t* As, int ks) {
     const uint16_t* Ws = As + kSlabA;
+    const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
 #pragma unroll
-    for (int ks = 0; ks < kTileK / 16; ++ks) {
-      const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
-      bf16x8 af[MI], bf[NJ];
+    for (int i = 0; i < MI; ++i)
+      af[buf][i] = *reinterpret_cast<const bf16x8*>(As + slab_at(RW * wm + 32 * i + (lane & 31), c));
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + slab_at(RW * wm + 32 * i + (lane & 31), c));
+    for (int j = 0; j < NJ; ++j)
+      bf[buf][j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(CW * wn + 32 * j + (lane & 31), c));
+  };
+  auto mfmas = [&](auto buf) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8*>(Ws + slab_at(CW * wn + 32 * j + (lane & 31), c));
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[j], af[i], acc[i][j], 0, 0, 0);  // C^T tile
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[buf][j], af[buf][i], acc[i][j], 0, 0, 0);  // C^T tile
+  };
+  // a sub-step: drain the reads of its own fragments, issue the next sub-step's
+  // reads, then its MFMAs, in that order
+  auto sub_step = [&](auto cur, auto next, const uint16_t* As, int ks_next) {
+    __builtin_amdgcn_s_waitcnt(kLdsDrained);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(next, As, ks_next);
+    mfmas(cur);
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);  // the LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);  // then the MFMAs
+  };
+  constexpr std::integral_constant<int, 0> B0{};
+  constexpr std::integral_constant<int, 1> B1{};
+  static_assert(kTileK / 16 == 4, "four sub-steps per K step");
+  // one K step; the last one issues no loads and needs no barrier before its
+  // MFMAs (but one after its reads when the written-out epilogue reuses the slabs)
+  auto step = [&](int64_t it, auto last) {
+    const int cur = static_cast<int>(it % S);
+    const bool more = it + S - 1 < steps;
+    if constexpr (!decltype(last)::value) {
+      if (more) issue(static_cast<int>((it + S - 1) % S), (it + S - 1) * kTileK);  // in flight below
     }
-    // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
-    if (more)
-      __builtin_amdgcn_s_waitcnt(vmcnt_at_most((S - 2) * kLoads));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-    slab_barrier();
-  }
+    const uint16_t* As = lds + cur * kSlab;
+    sub_step(B0, B1, As, 1);
+    sub_step(B1, B0, As, 2);
+    sub_step(B0, B1, As, 3);
+    if constexpr (!decltype(last)::value) {
+      // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
+      // and this wavefront's reads of slab `cur` are done
+      if (more)
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained((S - 2) * kLoads));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(0));
+      slab_barrier();
+      read_frags(B0, lds + static_cast<int>((it + 1) % S) * kSlab, 0);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kLdsDrained);
+      // the written-out epilogue reuses the slabs for its tile: every
+      // wavefront's reads of them are done before any wavefront writes it
+      if constexpr (!FUSED) slab_barrier();
+    }
+    mfmas(B1);
+  };
+  read_frags(B0, lds, 0);
+  for (int64_t it = 0; it + 1 < steps; ++it) step(it, std::false_type{});
+  step(steps - 1, std::true_type{});
 
   // Epilogue straight from the accumulators (no LDS round trip).  The product
   // is computed transposed, C^T = W * A^T, so lane l of tile (i, j) holds
