@@ -39,7 +39,21 @@ namespace echo {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Two fp32 values rounded to bfloat16 (nearest, ties to even: the hardware
+// conversion v_cvt_pk_bf16_f32), x in the low and y in the high half.
+__device__ __forceinline__ uint32_t bf16x2_rne(float x, float y) {
+  return __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(x), static_cast<__bf16>(y)});
+}
+
+// The value lane l ^ 32 holds (one v_permlane32_swap, which exchanges the two
+// 32-lane halves, and a select).
+__device__ __forceinline__ uint32_t xor32(uint32_t x, int half) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return half ? sw[0] : sw[1];
+}
 
 constexpr int kTileK = 64;
 static_assert(kTileK == 64, "the slab loads assume 64-element (128-byte) rows");
@@ -291,16 +305,22 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const int64_t m = m0 + RW * wm + 32 * i + (lane & 31);
       const int64_t e = m * H + n0 + CW * wn + 32 * j;  // first element of the row's group
-      float v[16];  // the bf16-rounded partial, widened
+      // the bf16-rounded partial: pk[q] holds columns 2q and 2q + 1 of the lane's
+      // 16 (in accumulator order), v the same values widened to fp32
+      uint32_t pk[8];
+      float v[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(static_cast<uint32_t>(bf16_rne(acc[i][j][k])) << 16);
+      for (int q = 0; q < 8; ++q) {
+        pk[q] = bf16x2_rne(acc[i][j][2 * q], acc[i][j][2 * q + 1]);
+        v[2 * q] = __uint_as_float(pk[q] << 16);
+        v[2 * q + 1] = __uint_as_float(pk[q] & 0xFFFF0000u);
+      }
       if constexpr (!FUSED) {
         // into the row-major LDS tile, 4 columns (8 bytes) per store; written out below
         const int row = RW * wm + 32 * i + (lane & 31);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {  // columns 8q + 4 half .. + 3
-          const uint32_t lo = (__float_as_uint(v[4 * q + 1]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q]) >> 16);
-          const uint32_t hi = (__float_as_uint(v[4 * q + 3]) & 0xFFFF0000u) | (__float_as_uint(v[4 * q + 2]) >> 16);
+          const uint32_t lo = pk[2 * q], hi = pk[2 * q + 1];
           *reinterpret_cast<uint2*>(lds + row * kLdsN + CW * wn + 32 * j + 8 * q + 4 * half) = make_uint2(lo, hi);
         }
       } else {
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < 16; ++k) amax = fmaxf(amax, __builtin_fabsf(v[k]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        amax = fmaxf(amax, __uint_as_float(xor32(__float_as_uint(amax), half)));
         const float s = echo_div7(amax);
         float v0[8], v1[8], kf[8];
 #pragma unroll
@@ -366,7 +386,7 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
         }
         // code word q of the group holds columns 8q .. 8q + 7, its low half-word from
         // the lower lane; the lower lane writes words 0 and 1, the upper 2 and 3
-        const uint32_t got = __shfl_xor(half ? w0 : w1, 32);
+        const uint32_t got = xor32(half ? w0 : w1, half);
         uint2 words;
         if (half == 0)
           words = make_uint2((w0 & 0xFFFFu) | (got << 16), (w0 >> 16) | (got & 0xFFFF0000u));
