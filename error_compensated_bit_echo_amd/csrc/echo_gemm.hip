@@ -12,14 +12,13 @@
 // bf16 partial, which the same kernel writes when asked to.
 //
 // Tiling: a block computes a 256 x 256 tile of one rank's [M, H] partial with 8
-// wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles
-// (256 x 128 tiles, 64 x 64 per wavefront, where H is not a multiple of 256 or
-// the larger tiles would leave CUs idle; 128 x 128 with 4 wavefronts where M is
-// not a multiple of 256; 64 x 128 for short products, 32 x 64 per wavefront).
-// K advances 64 at a time through two LDS slabs: while the matrix cores work on
-// one slab, the next one streams from global memory straight into the other
-// (buffer_load_dwordx4 ... lds through a buffer resource over the block's row
-// panel: each wavefront instruction fills 1 KiB of LDS, eight 128-byte rows,
+// wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles,
+// where the product is large enough; 128 x 128 with 8 wavefronts (32 x 64 each)
+// for mid-sized and short products; 64 x 128 with 4 wavefronts for the shortest.
+// K advances 64 at a time through a ring of LDS slabs: while the matrix cores
+// work on one slab, the next ones stream from global memory straight into the
+// others (buffer_load_dwordx4 ... lds through a buffer resource over the block's
+// row panel: each wavefront instruction fills 1 KiB of LDS, eight 128-byte rows,
 // with no register staging), so each K step needs one barrier.  Within a K step
 // the fragments of the four 16-deep sub-steps are double-buffered in registers.
 // The slabs are unpadded; within a row the 16-byte chunk c of row r sits in slot
@@ -62,6 +61,10 @@ static_assert(kTileK == 64, "the slab loads assume 64-element (128-byte) rows");
 // does for these loads; a zero format would make every load return zero).
 constexpr int kBufferWord3 = 0x00020000;
 
+// The non-temporal (nt) bit of the cache-policy operand: the lines are kept in
+// the caches as streaming data, evicted first.
+constexpr int kNonTemporal = 2;
+
 // A raw buffer resource over `bytes` bytes from `base`, and one 16-byte-per-lane
 // load through it straight into LDS (lane l's 16 bytes land at lds + 16 l bytes;
 // an offset at or past `bytes` reads zeros).  The slab loads use these rather
@@ -82,10 +85,12 @@ __device__ __forceinline__ BufRsrc buffer_rsrc(const void* base, int32_t bytes) 
   return BufRsrc{};
 #endif
 }
+// POLICY: the cache-policy operand of the load (0, or kNonTemporal).
+template <int POLICY>
 __device__ __forceinline__ void buffer_load_lds16(BufRsrc r, uint16_t* lds, uint32_t voffset, uint32_t soffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r.r, (__attribute__((address_space(3))) void*)lds, 16, voffset,
-                                           soffset, 0, 0);
+                                           soffset, 0, POLICY);
 #else
   (void)r;
   (void)lds;
@@ -123,19 +128,30 @@ __device__ __forceinline__ void slab_barrier() {
 // BM x TN: the block tile; NW: wavefronts, laid out (NW/2) x 2 over the
 // tile, each computing (2 BM / NW) rows x TN/2 columns; S: LDS slabs in the
 // pipeline (S - 1 K steps of loads in flight while one is multiplied).
-//   128 x 128, 4 wavefronts, 2 slabs (64 KiB): two blocks per CU;
-//   64 x 128, 4 wavefronts, 2 slabs: for short products that would otherwise
-//     leave CUs without a second block;
-//   256 x 128, 8 wavefronts, 2 slabs (96 KiB): one block per CU, half the
-//     slab loads per multiply-add of the 128-row tile (a third slab, which
-//     hides twice the load latency, measured slower);
 //   256 x 256, 8 wavefronts, 2 slabs (128 KiB; 132 KiB when the written-out
-//     tile needs more): one block per CU, a third fewer slab bytes per
-//     multiply-add than 256 x 128 (the fastest of these where M and H allow
-//     it and the grid still covers the CUs).
+//     tile needs more): one block per CU, the fewest slab bytes per multiply-add;
+//   128 x 128, 8 wavefronts, 2 slabs (64 KiB): two blocks per CU;
+//   128 x 128, 8 wavefronts, 4 slabs (128 KiB): one block per CU with three K
+//     steps of loads in flight, for products of at most one tile per CU, which
+//     stream their weights and are bound by memory rather than matrix work;
+//   64 x 128, 4 wavefronts, 4 slabs (96 KiB): the same for products of at most
+//     half a tile per CU, in twice as many blocks.
 // SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
-template <int BM, int TN, int NW, int S, bool FUSED, int SFB>
+// XG: the tile order.  The hardware hands the blocks of a launch to the eight
+// XCDs in turn (block i to XCD i % 8), and each XCD has its own L2.  With XG,
+// when the T tiles are a multiple of 8, block i takes tile (i % 8) T/8 + i / 8
+// of the tiles ordered row tile fastest, then column panel, then rank, so each
+// XCD works through one contiguous run of them: the row tiles of a column panel
+// share an XCD (its weights come from memory once), and so do as few ranks as
+// the run spans (each rank's activations come from memory once per XCD that
+// needs them; at P = 8 with 32 panels of 128 columns, one rank per XCD instead
+// of all eight on every XCD).  Without XG, tile (x, y, r) is block
+// x + gx (y + gy r), column panel fastest.
+// WNT: the weight loads are non-temporal, for the products of at most one tile
+// per CU, where the blocks that read a weight panel (one or two) run at the
+// same time on one XCD and nothing reads it later.
+template <int BM, int TN, int NW, int S, bool FUSED, int SFB, bool XG, bool WNT>
 __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   static_assert(FUSED || SFB == 0, "sender feedback only in the fused epilogue");
   constexpr int kThreads = 64 * NW;
@@ -153,7 +169,16 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   constexpr int kLdsN = TN + 8;                    // bf16 per LDS row of the written-out tile (padded)
   constexpr int kLdsTotal = (!FUSED && BM * kLdsN > S * kSlab) ? BM * kLdsN : S * kSlab;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsTotal];  // the written-out tile reuses the slabs
-  const int r = blockIdx.z;
+  unsigned bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (XG) {
+    const unsigned gx = gridDim.x, gy = gridDim.y, T = gx * gy * gridDim.z;
+    unsigned i = bx + gx * (by + gy * bz);
+    if (T % 8 == 0) i = (i % 8) * (T / 8) + i / 8;
+    by = i % gy;
+    bx = (i / gy) % gx;
+    bz = i / (gx * gy);
+  }
+  const int r = static_cast<int>(bz);
   const uint16_t* A = a.A[0];
   const uint16_t* W = a.W[0];
 #pragma unroll
@@ -163,8 +188,8 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
       W = a.W[i];
     }
   const int64_t K = a.K, H = a.H;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * TN;
+  const int64_t m0 = static_cast<int64_t>(by) * BM;
+  const int64_t n0 = static_cast<int64_t>(bx) * TN;
   const int t = threadIdx.x, lane = t & 63, wm = (t >> 6) >> 1, wn = (t >> 6) & 1;
 
   // global -> LDS slab `buf`: wavefront w fills 1 KiB blocks JA w ... of the A
@@ -196,9 +221,10 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
     uint16_t* Ws = As + kSlabA;
     const uint32_t kb = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
-    for (int j = 0; j < JA; ++j) buffer_load_lds16(rA, As + 512 * (JA * wave + j), offA[j], kb);
+    for (int j = 0; j < JA; ++j) buffer_load_lds16<0>(rA, As + 512 * (JA * wave + j), offA[j], kb);
 #pragma unroll
-    for (int j = 0; j < JW; ++j) buffer_load_lds16(rW, Ws + 512 * (JW * wave + j), offW[j], kb);
+    for (int j = 0; j < JW; ++j)
+      buffer_load_lds16<WNT ? kNonTemporal : 0>(rW, Ws + 512 * (JW * wave + j), offW[j], kb);
   };
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -418,38 +444,49 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 
 namespace {
 
-template <int BM, int TN, int NW, int S>
+template <int BM, int TN, int NW, int S, bool XG, bool WNT>
 hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.H / TN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
   if (!fused)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, false, 0>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, false, 0, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err == nullptr)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 0>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 0, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err_bf16)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 2>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 2, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 1>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 1, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 256 x 256 tiles of 8 wavefronts when M and H allow them and every CU still
-// gets a block, else 256 x 128 tiles when M allows them, else 128 x 128, unless
-// 128 x 128 tiles would give the 256 CUs fewer than two blocks each; then
-// 64 x 128.  Measured at P = 4, M = 2048, K = 3072, H = 4096 (fused / product
-// only, us): 256 x 256, 2 slabs 188.0 / 183.3 against 215.4 / 206.6 for 256 x 128
-// on the same machine (each K step moves 2/3 of the bytes per multiply-add);
-// 256 x 128, 2 slabs 208.2 / 201.4 against 128 x 128, 2 slabs 214.5 / 204.8;
-// 256 x 128, 3 slabs 226.0 / 208.7; 128 x 128, 3 slabs (one block per CU)
-// 280.6 / 267.3.
+// By the number b of 128 x 128 tiles of the whole launch (all ranks):
+//   b <= 128: 64 x 128, 4 slabs, grouped, weights non-temporal;
+//   b <= 256: 128 x 128, 8 wavefronts, 4 slabs, grouped, weights non-temporal;
+//   b >= 1024 with M and H multiples of 256: 256 x 256, grouped;
+//   else 128 x 128, 8 wavefronts, 2 slabs, grouped.
+// Measured with the weights cold (each call's weights last touched more than
+// 256 MB of traffic earlier, as in a model whose layers each bring their own):
+// fused product with stage 1, median of 5 x 40 calls, one run, against the
+// same shapes in other tile configurations, us:
+//   P = 2, M = 256, K = 1024, H = 1024: 11.3 against 12.9 for 64 x 128 tiles with 2 slabs;
+//   P = 4, M = 128, K = 3072, H = 4096: 29.9 against 46.5 (64 x 128, 2 slabs) and
+//     37.1 (128 x 128, 4 slabs);
+//   P = 8, M = 128, same K and H: 43.4 against 59.1 (64 x 128, 2 slabs) and 45.0
+//     (the same tiles with cached weight loads; 35.2 against 41.6 when the
+//     weights are still in the Infinity Cache);
+//   P = 8, M = 256: 72.7 against 78.2 (256 x 128) and 74.7 (128 x 128, 4 slabs);
+//   P = 4, M = 2048, K = 3072, H = 2176: 150.9 against 185.5 (256 x 128);
+//   P = 2, M = 2176, K = 3072, H = 4096: 145.8 against 149.2 (128 x 128, 4 wavefronts);
+//   P = 4, M = 2048, K = 3072, H = 4096: 196.9 against 205.0 in the column-panel-
+//     fastest order and 244.2 for 128 x 128 tiles with 2 slabs.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
-  const int64_t blocks128 = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
-  if (blocks128 < 512) return gemm_cfg<64, 128, 4, 2>(a, P, fused, s);
-  if (a.M % 256 == 0 && a.H % 256 == 0 && blocks128 / 4 >= 256) return gemm_cfg<256, 256, 8, 2>(a, P, fused, s);
-  if (a.M % 256 == 0) return gemm_cfg<256, 128, 8, 2>(a, P, fused, s);
-  return gemm_cfg<128, 128, 4, 2>(a, P, fused, s);
+  const int64_t b = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
+  if (b <= 128) return gemm_cfg<64, 128, 4, 4, true, true>(a, P, fused, s);
+  if (b <= 256) return gemm_cfg<128, 128, 8, 4, true, true>(a, P, fused, s);
+  if (b >= 1024 && a.M % 256 == 0 && a.H % 256 == 0) return gemm_cfg<256, 256, 8, 2, true, false>(a, P, fused, s);
+  return gemm_cfg<128, 128, 8, 2, true, false>(a, P, fused, s);
 }
 
 }  // namespace echo

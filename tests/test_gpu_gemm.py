@@ -16,29 +16,42 @@ from parity_helpers import _compare, _fetch, _state, _torch
 
 pytestmark = pytest.mark.gpu
 
-# Every block tile the launcher picks, each in its steady state: a K step
-# issues the loads of step + 1 into the slab that step - 1 read, which first
-# happens at the third step, so each tile runs at least 4 (and a ring of two
-# slabs is exercised over many turns).  The launcher takes
-#   64 x 128 when 128 x 128 tiles would give fewer than 512 blocks,
-#   256 x 256 when M and H are multiples of 256 and a quarter of those blocks still covers the 256 CUs,
-#   256 x 128 when M is a multiple of 256, and 128 x 128 otherwise.
+# Every tile configuration the launcher picks, each in its steady state: a K
+# step issues the loads of step + S - 1 into the slab that step - 1 read, so
+# with S slabs each tile runs at least S + 1 steps (and the ring is exercised
+# over many turns), plus fewer steps than slabs (the pipeline is never full)
+# and, for the grouped tile order, a tile count that is not a multiple of 8 (the
+# order falls back to column panel fastest).  By the number b of 128 x 128
+# tiles of the launch, the launcher takes
+#   b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
+#   b >= 1024 with M and H multiples of 256: 256 x 256, 2 slabs, grouped;
+#   else 128 x 128, 2 slabs, grouped.
 SHAPES = [
-    (1, 128, 64, 128),      # 64 x 128, 1 K step
-    (2, 256, 512, 384),     # 64 x 128, 8 steps
-    (3, 384, 1024, 256),    # 64 x 128, 16 steps
-    (8, 128, 3072, 512),    # 64 x 128, 48 steps
-    (2, 2048, 128, 2048),   # 256 x 128, 2 steps
-    (2, 2048, 512, 2048),   # 256 x 128, 8 steps
-    (2, 2176, 192, 2048),   # 128 x 128, 3 steps
-    (2, 2176, 512, 2048),   # 128 x 128, 8 steps
-    (4, 2048, 128, 2048),   # 256 x 256, 2 steps
-    (4, 2048, 576, 2048),   # 256 x 256, 9 steps (an odd count: the last step reads the other slab)
-    (4, 2048, 3072, 4096),  # 256 x 256, 48 steps: the product the benchmark times
+    (1, 128, 64, 128),       # b = 1: 64 x 128, 4 slabs, 2 tiles (not grouped), 1 K step
+    (2, 256, 512, 384),      # b = 12: 24 tiles (grouped), 8 steps
+    (3, 384, 1024, 256),     # b = 18: 36 tiles (not grouped), 16 steps
+    (2, 128, 64, 4096),      # b = 64: 1 step
+    (4, 128, 192, 2048),     # b = 64: 3 steps (the prologue fills every slab but one)
+    (8, 128, 3072, 1024),    # b = 64: 48 steps
+    (3, 128, 320, 2816),     # b = 66: 132 tiles (not grouped), 5 steps
+    (16, 128, 128, 2048),    # b = 256: 128 x 128, 4 slabs, 2 steps
+    (4, 256, 640, 4096),     # b = 256: 10 steps
+    (8, 128, 3072, 4096),    # b = 256: 48 steps: the short product the benchmark times
+    (3, 128, 320, 7296),     # b = 171: not grouped, 5 steps
+    (2, 2048, 128, 2048),    # b = 512: 128 x 128, 2 slabs, 2 steps
+    (2, 2048, 512, 2048),    # b = 512: 8 steps
+    (2, 2176, 192, 2048),    # b = 544: 3 steps
+    (2, 2176, 512, 2048),    # b = 544: 8 steps
+    (3, 128, 320, 11008),    # b = 258: not grouped, 5 steps
+    (4, 2048, 128, 2048),    # b = 1024: 256 x 256, 2 steps
+    (4, 2048, 576, 2048),    # b = 1024: 9 steps (an odd count: the last step reads the other slab)
+    (4, 2048, 3072, 4096),   # b = 2048: 48 steps: the product the benchmark times
+    (5, 2304, 64, 2304),     # b = 1620: 405 tiles (not grouped), 1 step
 ]
-# one shape per tile configuration in its steady state, for the whole-call tests
-STEADY = [(2, 256, 512, 384), (8, 128, 3072, 512), (2, 2048, 512, 2048), (2, 2176, 512, 2048),
-          (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
+# one shape per tile configuration in its steady state (and the benchmarked
+# ones), for the whole-call tests
+STEADY = [(2, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096), (8, 128, 3072, 4096),
+          (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
@@ -98,8 +111,9 @@ def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
         assert np.array_equal(vf["scales1"][r].cpu().numpy().view(np.uint32), s.view(np.uint32))
 
 
-@pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (2, 2048, 128, 2048),
-                                     (2, 2176, 128, 2048), (4, 2048, 192, 2048)] + STEADY)
+@pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (3, 128, 320, 2816),
+                                     (3, 128, 320, 7296), (2, 2048, 128, 2048), (2, 2176, 128, 2048),
+                                     (3, 128, 320, 11008), (4, 2048, 192, 2048)] + STEADY)
 def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
@@ -118,8 +132,9 @@ def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
 
 
-@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (4, 2048, 128, 2048), (2, 2048, 512, 2048),
-                                     (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)])
+@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096),
+                                     (8, 128, 3072, 4096), (2, 2048, 512, 2048), (2, 2176, 512, 2048),
+                                     (4, 2048, 128, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)])
 @pytest.mark.parametrize("sb16", [False, True])
 def test_fused_sender_feedback_calls_match_the_oracle(cuda, sb16, P, M, K, H):
     """Sender feedback in the fused epilogue: each rank's carried stage-1 error
@@ -169,9 +184,10 @@ def _special_inputs(case, P, M, K, H, seed, dev):
 
 @pytest.mark.parametrize("sfb", [False, True])
 @pytest.mark.parametrize("case", ["zeros_and_single_columns", "huge", "tiny", "subnormal"])
-@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 2048, 64, 2048), (4, 2048, 64, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 128, 64, 4096), (4, 256, 64, 4096),
+                                     (2, 2048, 64, 2048), (4, 2048, 64, 2048)])
 def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
-    """The fused epilogue on special values, 64 x 128, 256 x 128 and 256 x 256 tiles, with and
+    """The fused epilogue on special values, in every tile configuration, with and
     without sender feedback (bf16 state): whole calls against the oracle fed
     the written-out partials."""
     import error_compensated_bit_echo_amd as E
@@ -197,7 +213,7 @@ def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
 
 
-@pytest.mark.parametrize("P,M,K,H", [(8, 128, 256, 1024), (4, 2048, 128, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(8, 128, 256, 1024), (4, 256, 256, 4096), (4, 2048, 128, 2048)])
 def test_fused_calls_in_a_graph_match_eager_calls(cuda, P, M, K, H):
     """A graph holding a fused forward call (product with stage 1 and sender
     feedback, owner step, decode), a fused backward call and the written-out
