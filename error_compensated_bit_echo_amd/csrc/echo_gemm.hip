@@ -140,9 +140,10 @@ __device__ __forceinline__ void slab_barrier() {
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
 // XG: the tile order.  The hardware hands the blocks of a launch to the eight
 // XCDs in turn (block i to XCD i % 8), and each XCD has its own L2.  With XG,
-// when the T tiles are a multiple of 8, block i takes tile (i % 8) T/8 + i / 8
-// of the tiles ordered row tile fastest, then column panel, then rank, so each
-// XCD works through one contiguous run of them: the row tiles of a column panel
+// the tiles are ordered row tile fastest, then column panel, then rank, and
+// block i takes tile (i % 8) T/8 + i / 8 of them when the T tiles are a
+// multiple of 8 (else tile i), so that each XCD works through one contiguous
+// run of them: the row tiles of a column panel
 // share an XCD (its weights come from memory once), and so do as few ranks as
 // the run spans (each rank's activations come from memory once per XCD that
 // needs them; at P = 8 with 32 panels of 128 columns, one rank per XCD instead

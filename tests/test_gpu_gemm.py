@@ -20,33 +20,33 @@ pytestmark = pytest.mark.gpu
 # step issues the loads of step + S - 1 into the slab that step - 1 read, so
 # with S slabs each tile runs at least S + 1 steps (and the ring is exercised
 # over many turns), plus fewer steps than slabs (the pipeline is never full)
-# and, for the grouped tile order, a tile count that is not a multiple of 8 (the
-# order falls back to column panel fastest).  By the number b of 128 x 128
+# and, for the grouped tile order, a tile count that is not a multiple of 8 (block
+# i then takes tile i of the row-tile-fastest order, without the XCD grouping).  By the number b of 128 x 128
 # tiles of the launch, the launcher takes
 #   b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
 #   b >= 1024 with M and H multiples of 256: 256 x 256, 2 slabs, grouped;
 #   else 128 x 128, 2 slabs, grouped.
 SHAPES = [
-    (1, 128, 64, 128),       # b = 1: 64 x 128, 4 slabs, 2 tiles (not grouped), 1 K step
-    (2, 256, 512, 384),      # b = 12: 24 tiles (grouped), 8 steps
-    (3, 384, 1024, 256),     # b = 18: 36 tiles (not grouped), 16 steps
+    (1, 128, 64, 128),       # b = 1: 64 x 128, 4 slabs, 2 tiles, 1 K step
+    (2, 256, 512, 384),      # b = 12: 24 tiles, 8 steps
+    (3, 384, 1024, 256),     # b = 18: 36 tiles, 16 steps
     (2, 128, 64, 4096),      # b = 64: 1 step
     (4, 128, 192, 2048),     # b = 64: 3 steps (the prologue fills every slab but one)
     (8, 128, 3072, 1024),    # b = 64: 48 steps
-    (3, 128, 320, 2816),     # b = 66: 132 tiles (not grouped), 5 steps
+    (3, 128, 320, 2816),     # b = 66: 132 tiles (not a multiple of 8), 5 steps
     (16, 128, 128, 2048),    # b = 256: 128 x 128, 4 slabs, 2 steps
     (4, 256, 640, 4096),     # b = 256: 10 steps
     (8, 128, 3072, 4096),    # b = 256: 48 steps: the short product the benchmark times
-    (3, 128, 320, 7296),     # b = 171: not grouped, 5 steps
+    (3, 128, 320, 7296),     # b = 171 tiles (not a multiple of 8), 5 steps
     (2, 2048, 128, 2048),    # b = 512: 128 x 128, 2 slabs, 2 steps
     (2, 2048, 512, 2048),    # b = 512: 8 steps
     (2, 2176, 192, 2048),    # b = 544: 3 steps
     (2, 2176, 512, 2048),    # b = 544: 8 steps
-    (3, 128, 320, 11008),    # b = 258: not grouped, 5 steps
+    (3, 128, 320, 11008),    # b = 258 tiles (not a multiple of 8), 5 steps
     (4, 2048, 128, 2048),    # b = 1024: 256 x 256, 2 steps
     (4, 2048, 576, 2048),    # b = 1024: 9 steps (an odd count: the last step reads the other slab)
     (4, 2048, 3072, 4096),   # b = 2048: 48 steps: the product the benchmark times
-    (5, 2304, 64, 2304),     # b = 1620: 405 tiles (not grouped), 1 step
+    (5, 2304, 64, 2304),     # b = 1620: 405 tiles (not a multiple of 8), 1 step
 ]
 # one shape per tile configuration in its steady state (and the benchmarked
 # ones), for the whole-call tests
