@@ -128,9 +128,9 @@ __device__ __forceinline__ void slab_barrier() {
 // BM x TN: the block tile; NW: wavefronts, laid out (NW/2) x 2 over the
 // tile, each computing (2 BM / NW) rows x TN/2 columns; S: LDS slabs in the
 // pipeline (S - 1 K steps of loads in flight while one is multiplied).
-//   256 x 256, 8 wavefronts, 2 slabs (128 KiB; 132 KiB when the written-out
-//     tile needs more): one block per CU, the fewest slab bytes per multiply-add;
-//   128 x 128, 8 wavefronts, 2 slabs (64 KiB): two blocks per CU;
+//   256 x 256, 8 wavefronts, 2 slabs and a third W slab (160 KiB): one block
+//     per CU, the fewest slab bytes per multiply-add;
+//   128 x 128, 8 wavefronts, 2 slabs and a third W slab (80 KiB): two blocks per CU;
 //   128 x 128, 8 wavefronts, 4 slabs (128 KiB): one block per CU with three K
 //     steps of loads in flight, for products of at most one tile per CU, which
 //     stream their weights and are bound by memory rather than matrix work;
@@ -152,7 +152,9 @@ __device__ __forceinline__ void slab_barrier() {
 // WNT: the weight loads are non-temporal, for the products of at most one tile
 // per CU, where the blocks that read a weight panel (one or two) run at the
 // same time on one XCD and nothing reads it later.
-template <int BM, int TN, int NW, int S, bool FUSED, int SFB, bool XG, bool WNT>
+// WAHEAD (with S = 2): the weights are loaded a K step further ahead than the
+// activations, through a ring of three W slabs beside the two A slabs.
+template <int BM, int TN, int NW, int S, bool FUSED, int SFB, bool XG, bool WNT, bool WAHEAD>
 __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   static_assert(FUSED || SFB == 0, "sender feedback only in the fused epilogue");
   constexpr int kThreads = 64 * NW;
@@ -168,7 +170,10 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   constexpr int kSlabA = BM * kTileK;              // bf16 of one A slab
   constexpr int kSlab = (BM + TN) * kTileK;        // bf16 of one A + W slab
   constexpr int kLdsN = TN + 8;                    // bf16 per LDS row of the written-out tile (padded)
-  constexpr int kLdsTotal = (!FUSED && BM * kLdsN > S * kSlab) ? BM * kLdsN : S * kSlab;
+  static_assert(!WAHEAD || S == 2, "weights a step further ahead only with two activation slabs");
+  constexpr int kSlabW = TN * kTileK;              // bf16 of one W slab
+  constexpr int kRing = WAHEAD ? S * kSlabA + (S + 1) * kSlabW : S * kSlab;
+  constexpr int kLdsTotal = (!FUSED && BM * kLdsN > kRing) ? BM * kLdsN : kRing;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsTotal];  // the written-out tile reuses the slabs
   unsigned bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if constexpr (XG) {
@@ -235,10 +240,16 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // K step `it` multiplies slab it % S; the loads of step it + S - 1 are issued
-  // at its start into the slab step it - 1 used, which every wavefront has
-  // finished reading: each waits for its own LDS reads before the barrier that
-  // ends a step.  The fragments of a step's four 16-deep sub-steps are
+  // Two rings of LDS slabs.  Without WAHEAD, S slabs each hold a K step's A and
+  // W tiles: K step `it` multiplies slab it % S, and the loads of step
+  // it + S - 1 are issued at its start into the slab step it - 1 used.  With
+  // WAHEAD, two slabs of A tiles and, after them, three of W tiles: step it
+  // multiplies A slot it % 2 and W slot it % 3 and issues the loads of A for
+  // step it + 1 and of W for step it + 2, so the weights, which come from HBM
+  // when cold while the activations are usually cached, have two steps to
+  // arrive.  Either way a load goes into a slot that step it - 1 read and every
+  // wavefront has finished reading: each waits for its own LDS reads before
+  // the barrier that ends a step.  The fragments of a step's four 16-deep sub-steps are
   // double-buffered in registers: the reads of sub-step k + 1 go out before the
   // MFMAs of sub-step k, and the reads of the next slab's first sub-step right
   // after the barrier, before the last sub-step's MFMAs.  (The compiler's own
@@ -247,17 +258,8 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   // sub-step earlier, which have had the MFMAs between to land, and its MFMAs
   // need no wait.)
   const int64_t steps = K / kTileK;
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < steps) issue(s, static_cast<int64_t>(s) * kTileK);
-  if (steps >= S - 1)
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most((S - 2) * kLoads));  // step 0's slab has landed
-  else
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-  slab_barrier();
   bf16x8 af[2][MI], bf[2][NJ];
-  auto read_frags = [&](auto buf, const uint16_t* As, int ks) {
-    const uint16_t* Ws = As + kSlabA;
+  auto read_frags = [&](auto buf, const uint16_t* As, const uint16_t* Ws, int ks) {
     const int c = 2 * ks + (lane >> 5);  // lane supplies k = 8c .. 8c + 7
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -275,10 +277,10 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   };
   // a sub-step: drain the reads of its own fragments, issue the next sub-step's
   // reads, then its MFMAs, in that order
-  auto sub_step = [&](auto cur, auto next, const uint16_t* As, int ks_next) {
+  auto sub_step = [&](auto cur, auto next, const uint16_t* As, const uint16_t* Ws, int ks_next) {
     __builtin_amdgcn_s_waitcnt(kLdsDrained);
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(next, As, ks_next);
+    read_frags(next, As, Ws, ks_next);
     mfmas(cur);
     __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);  // the LDS reads first
     __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);  // then the MFMAs
@@ -286,38 +288,109 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
   static_assert(kTileK / 16 == 4, "four sub-steps per K step");
-  // one K step; the last one issues no loads and needs no barrier before its
-  // MFMAs (but one after its reads when the written-out epilogue reuses the slabs)
-  auto step = [&](int64_t it, auto last) {
-    const int cur = static_cast<int>(it % S);
-    const bool more = it + S - 1 < steps;
-    if constexpr (!decltype(last)::value) {
-      if (more) issue(static_cast<int>((it + S - 1) % S), (it + S - 1) * kTileK);  // in flight below
-    }
-    const uint16_t* As = lds + cur * kSlab;
-    sub_step(B0, B1, As, 1);
-    sub_step(B1, B0, As, 2);
-    sub_step(B0, B1, As, 3);
-    if constexpr (!decltype(last)::value) {
-      // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
-      // and this wavefront's reads of slab `cur` are done
-      if (more)
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained((S - 2) * kLoads));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(0));
-      slab_barrier();
-      read_frags(B0, lds + static_cast<int>((it + 1) % S) * kSlab, 0);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kLdsDrained);
-      // the written-out epilogue reuses the slabs for its tile: every
-      // wavefront's reads of them are done before any wavefront writes it
-      if constexpr (!FUSED) slab_barrier();
-    }
-    mfmas(B1);
-  };
-  read_frags(B0, lds, 0);
-  for (int64_t it = 0; it + 1 < steps; ++it) step(it, std::false_type{});
-  step(steps - 1, std::true_type{});
+  if constexpr (!WAHEAD) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < steps) issue(s, static_cast<int64_t>(s) * kTileK);
+    if (steps >= S - 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most((S - 2) * kLoads));  // step 0's slab has landed
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    slab_barrier();
+    // one K step; the last one issues no loads and needs no barrier before its
+    // MFMAs (but one after its reads when the written-out epilogue reuses the slabs)
+    auto step = [&](int64_t it, auto last) {
+      const int cur = static_cast<int>(it % S);
+      const bool more = it + S - 1 < steps;
+      if constexpr (!decltype(last)::value) {
+        if (more) issue(static_cast<int>((it + S - 1) % S), (it + S - 1) * kTileK);  // in flight below
+      }
+      const uint16_t* As = lds + cur * kSlab;
+      const uint16_t* Ws = As + kSlabA;
+      sub_step(B0, B1, As, Ws, 1);
+      sub_step(B1, B0, As, Ws, 2);
+      sub_step(B0, B1, As, Ws, 3);
+      if constexpr (!decltype(last)::value) {
+        // step it + 1's slab has landed (the S - 2 later steps' loads may still fly)
+        // and this wavefront's reads of slab `cur` are done
+        if (more)
+          __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained((S - 2) * kLoads));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(0));
+        slab_barrier();
+        const uint16_t* An = lds + static_cast<int>((it + 1) % S) * kSlab;
+        read_frags(B0, An, An + kSlabA, 0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kLdsDrained);
+        // the written-out epilogue reuses the slabs for its tile: every
+        // wavefront's reads of them are done before any wavefront writes it
+        if constexpr (!FUSED) slab_barrier();
+      }
+      mfmas(B1);
+    };
+    read_frags(B0, lds, lds + kSlabA, 0);
+    for (int64_t it = 0; it + 1 < steps; ++it) step(it, std::false_type{});
+    step(steps - 1, std::true_type{});
+  } else {
+    // Loads go out in the order A(0), W(0), W(1), then A(it + 1), W(it + 2) at
+    // step it, and complete in that order: at the end of step it A(it + 1) and
+    // W(it + 1) must have landed, and only W(it + 2), issued after A(it + 1), may
+    // still be in flight.  The slots are tracked incrementally (a 64-bit
+    // remainder by 3 each step cost several per cent).
+    uint16_t* const abase = lds;
+    uint16_t* const wbase = lds + S * kSlabA;
+    auto issue_a_to = [&](uint16_t* As, int64_t st) {
+      const uint32_t kb = static_cast<uint32_t>(st * kTileK * 2);
+#pragma unroll
+      for (int j = 0; j < JA; ++j) buffer_load_lds16<0>(rA, As + 512 * (JA * wave + j), offA[j], kb);
+    };
+    auto issue_w_to = [&](uint16_t* Ws, int64_t st) {
+      const uint32_t kb = static_cast<uint32_t>(st * kTileK * 2);
+#pragma unroll
+      for (int j = 0; j < JW; ++j)
+        buffer_load_lds16<WNT ? kNonTemporal : 0>(rW, Ws + 512 * (JW * wave + j), offW[j], kb);
+    };
+    int sa = 0, sw = 0;  // slots of the current step's A and W slabs
+    auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
+    issue_a_to(abase, 0);
+    issue_w_to(wbase, 0);
+    if (steps > 1) issue_w_to(wbase + kSlabW, 1);
+    if (steps > 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(JW));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    slab_barrier();
+    auto step = [&](int64_t it, auto last) {
+      const bool w_more = it + 2 < steps;
+      const int sa1 = sa ^ 1, sw1 = next3(sw), sw2 = next3(sw1);
+      if constexpr (!decltype(last)::value) {
+        issue_a_to(abase + sa1 * kSlabA, it + 1);
+        if (w_more) issue_w_to(wbase + sw2 * kSlabW, it + 2);
+      }
+      const uint16_t* As = abase + sa * kSlabA;
+      const uint16_t* Ws = wbase + sw * kSlabW;
+      sub_step(B0, B1, As, Ws, 1);
+      sub_step(B1, B0, As, Ws, 2);
+      sub_step(B0, B1, As, Ws, 3);
+      if constexpr (!decltype(last)::value) {
+        if (w_more)
+          __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(JW));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(0));
+        slab_barrier();
+        read_frags(B0, abase + sa1 * kSlabA, wbase + sw1 * kSlabW, 0);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kLdsDrained);
+        if constexpr (!FUSED) slab_barrier();
+      }
+      mfmas(B1);
+      sa = sa1;
+      sw = sw1;
+    };
+    read_frags(B0, abase, wbase, 0);
+    for (int64_t it = 0; it + 1 < steps; ++it) step(it, std::false_type{});
+    step(steps - 1, std::true_type{});
+  }
 
   // Epilogue straight from the accumulators (no LDS round trip).  The product
   // is computed transposed, C^T = W * A^T, so lane l of tile (i, j) holds
@@ -445,18 +518,18 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 
 namespace {
 
-template <int BM, int TN, int NW, int S, bool XG, bool WNT>
+template <int BM, int TN, int NW, int S, bool XG, bool WNT, bool WAHEAD>
 hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.H / TN), static_cast<unsigned>(a.M / BM),
                   static_cast<unsigned>(P));
   if (!fused)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, false, 0, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, false, 0, XG, WNT, WAHEAD>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err == nullptr)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 0, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 0, XG, WNT, WAHEAD>), grid, dim3(64 * NW), 0, s, a);
   else if (a.err_bf16)
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 2, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 2, XG, WNT, WAHEAD>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 1, XG, WNT>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((echo_gemm_k<BM, TN, NW, S, true, 1, XG, WNT, WAHEAD>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
@@ -465,29 +538,34 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 // By the number b of 128 x 128 tiles of the whole launch (all ranks):
 //   b <= 128: 64 x 128, 4 slabs, grouped, weights non-temporal;
 //   b <= 256: 128 x 128, 8 wavefronts, 4 slabs, grouped, weights non-temporal;
-//   b >= 1024 with M and H multiples of 256: 256 x 256, grouped;
-//   else 128 x 128, 8 wavefronts, 2 slabs, grouped.
+//   b >= 1024 with M and H multiples of 256: 256 x 256, grouped, weights ahead;
+//   else 128 x 128, 8 wavefronts, 2 slabs, grouped, weights ahead.
 // Measured with the weights cold (each call's weights last touched more than
 // 256 MB of traffic earlier, as in a model whose layers each bring their own):
-// fused product with stage 1, median of 5 x 40 calls, one run, against the
-// same shapes in other tile configurations, us:
+// fused product with stage 1, median of 5 x 40 calls, against the same shapes
+// in other tile configurations, each comparison from one run, us:
 //   P = 2, M = 256, K = 1024, H = 1024: 11.3 against 12.9 for 64 x 128 tiles with 2 slabs;
 //   P = 4, M = 128, K = 3072, H = 4096: 29.9 against 46.5 (64 x 128, 2 slabs) and
 //     37.1 (128 x 128, 4 slabs);
 //   P = 8, M = 128, same K and H: 43.4 against 59.1 (64 x 128, 2 slabs) and 45.0
 //     (the same tiles with cached weight loads; 35.2 against 41.6 when the
 //     weights are still in the Infinity Cache);
-//   P = 8, M = 256: 72.7 against 78.2 (256 x 128) and 74.7 (128 x 128, 4 slabs);
-//   P = 4, M = 2048, K = 3072, H = 2176: 150.9 against 185.5 (256 x 128);
-//   P = 2, M = 2176, K = 3072, H = 4096: 145.8 against 149.2 (128 x 128, 4 wavefronts);
-//   P = 4, M = 2048, K = 3072, H = 4096: 196.9 against 205.0 in the column-panel-
-//     fastest order and 244.2 for 128 x 128 tiles with 2 slabs.
+//   P = 4, M = 2048, K = 3072, H = 4096: 178.9 against 190.2 without the third W
+//     slab (175.2 against 171.2 with the weights in the Infinity Cache), 205.0 in
+//     the column-panel-fastest order and 244.2 for 128 x 128 tiles with 2 slabs;
+//     at K = 12288, 678 against 726;
+//   P = 4, M = 2048, K = 3072, H = 2176: 127.8 against 149.8 without the third W
+//     slab and 185.5 for 256 x 128 tiles;
+//   P = 2, M = 2176, K = 3072, H = 4096: 127.0 against 144.8 without the third W
+//     slab and 149.2 for 128 x 128 tiles of 4 wavefronts;
+//   P = 8, M = 256, K = 3072, H = 4096: 67.5 against 72.2 without the third W
+//     slab, 74.7 for 128 x 128 tiles with 4 slabs and 78.2 for 256 x 128.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const int64_t b = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
-  if (b <= 128) return gemm_cfg<64, 128, 4, 4, true, true>(a, P, fused, s);
-  if (b <= 256) return gemm_cfg<128, 128, 8, 4, true, true>(a, P, fused, s);
-  if (b >= 1024 && a.M % 256 == 0 && a.H % 256 == 0) return gemm_cfg<256, 256, 8, 2, true, false>(a, P, fused, s);
-  return gemm_cfg<128, 128, 8, 2, true, false>(a, P, fused, s);
+  if (b <= 128) return gemm_cfg<64, 128, 4, 4, true, true, false>(a, P, fused, s);
+  if (b <= 256) return gemm_cfg<128, 128, 8, 4, true, true, false>(a, P, fused, s);
+  if (b >= 1024 && a.M % 256 == 0 && a.H % 256 == 0) return gemm_cfg<256, 256, 8, 2, true, false, true>(a, P, fused, s);
+  return gemm_cfg<128, 128, 8, 2, true, false, true>(a, P, fused, s);
 }
 
 }  // namespace echo
