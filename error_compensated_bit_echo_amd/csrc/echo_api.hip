@@ -269,14 +269,15 @@ namespace {
 // within 1 GiB.
 constexpr int64_t kGemmMaxK = int64_t(1) << 21;
 
-// The product kernel numbers its tiles in 32-bit arithmetic: with at most 2^26
-// tiles of 128 x 128 per rank (2^40 elements, far beyond device memory), 16
-// ranks and two tiles of 64 x 128 per such tile stay below 2^31.
+// The product kernel numbers its tiles in 32-bit arithmetic: with at most 2^27
+// tiles of 64 x 128 per rank (2^40 elements, far beyond device memory), 16
+// ranks stay below 2^31.  The grid's row count, M / 64 at most, stays within
+// the 65535 blocks a launch dimension allows.
 bool gemm_shape_ok(int64_t M, int64_t K, int64_t H) {
-  return M > 0 && K > 0 && H > 0 && M % echo::kGemmTileM == 0 && H % echo::kGemmTileN == 0 &&
-         K % echo::kGemmTileK == 0 && K <= kGemmMaxK && M / echo::kGemmTileM <= 65535 &&
+  return M > 0 && K > 0 && H > 0 && M % echo::kGemmRowStep == 0 && H % echo::kGemmTileN == 0 &&
+         K % echo::kGemmTileK == 0 && K <= kGemmMaxK && M / echo::kGemmRowStep <= 65535 &&
          H / echo::kGemmTileN <= (int64_t{1} << 26) &&
-         (M / echo::kGemmTileM) * (H / echo::kGemmTileN) <= (int64_t{1} << 26);
+         (M / echo::kGemmRowStep) * (H / echo::kGemmTileN) <= (int64_t{1} << 27);
 }
 
 echo_status gemm_inputs(const void* const* A, const void* const* W, int P, echo::GemmArgs* a) {

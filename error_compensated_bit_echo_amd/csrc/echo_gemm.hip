@@ -535,7 +535,7 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 
 }  // namespace
 
-// By the number b of 128 x 128 tiles of the whole launch (all ranks):
+// For M a multiple of 128, by the number b of 128 x 128 tiles of the whole launch (all ranks):
 //   b <= 128: 64 x 128, 4 slabs, grouped, weights non-temporal;
 //   b <= 256: 128 x 128, 8 wavefronts, 4 slabs, grouped, weights non-temporal;
 //   b >= 1024 with M and H multiples of 256: 256 x 256, grouped, weights ahead;
@@ -561,6 +561,11 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 //   P = 8, M = 256, K = 3072, H = 4096: 67.5 against 72.2 without the third W
 //     slab, 74.7 for 128 x 128 tiles with 4 slabs and 78.2 for 256 x 128.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+  // M a multiple of 64 but not of 128: 64 x 128 tiles, 4 slabs, grouped; the
+  // weight loads non-temporal for M = 64, where each weight panel has one reader
+  if (a.M % kGemmTileM != 0)
+    return a.M == kGemmRowStep ? gemm_cfg<64, 128, 4, 4, true, true, false>(a, P, fused, s)
+                               : gemm_cfg<64, 128, 4, 4, true, false, false>(a, P, fused, s);
   const int64_t b = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
   if (b <= 128) return gemm_cfg<64, 128, 4, 4, true, true, false>(a, P, fused, s);
   if (b <= 256) return gemm_cfg<128, 128, 8, 4, true, true, false>(a, P, fused, s);

@@ -82,7 +82,7 @@ hipError_t launch_decode(const uint32_t* codes, const float* scales, void* out,
 hipError_t launch_zero(float* p, int64_t n_floats, hipStream_t s);
 
 // The producing product partial_r = bf16(A_r * W_r^T) of every rank (A_r [M, K],
-// W_r [H, K], bf16 row-major; M % 128 == 0, H % 128 == 0, K % 64 == 0), either
+// W_r [H, K], bf16 row-major; M % 64 == 0, H % 128 == 0, K % 64 == 0), either
 // written out (out[r], [M, H] bf16) or quantized in the epilogue into the
 // stage-1 payload (codes / scales as in Stage1Args, group 32; with err set, the
 // rank's stage-1 error is added first and updated, as stage 1 does).
@@ -99,7 +99,9 @@ struct GemmArgs {
   int64_t err_stride;   // 4-byte words between ranks (err == nullptr: no sender feedback)
   int32_t err_bf16;     // the errors are bfloat16 bits (with the bf16 state), else fp32
 };
-constexpr int kGemmTileM = 128, kGemmTileN = 128, kGemmTileK = 64;
+// kGemmTileM x kGemmTileN: the tile unit the launcher counts; M must be a
+// multiple of kGemmRowStep, H of kGemmTileN and K of kGemmTileK.
+constexpr int kGemmTileM = 128, kGemmTileN = 128, kGemmTileK = 64, kGemmRowStep = 64;
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s);
 
 }  // namespace echo

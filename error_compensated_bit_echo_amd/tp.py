@@ -203,8 +203,8 @@ class TPMLPStack:
     Weights are fp32 and seeded.  product "f32": the products are taken in fp32
     and each rank's partial output is rounded to bf16 (the wire dtype);
     "bf16" / "bf16_fused": the row-parallel product runs in bfloat16 on
-    libecho's kernel (written out, or with stage 1 in its epilogue; T and H
-    multiples of 128, F/P of 64)."""
+    libecho's kernel (written out, or with stage 1 in its epilogue; T a
+    multiple of 64, H of 128, F/P of 64)."""
 
     def __init__(self, layers: int, hidden: int, ffn: int, P: int, seed: int = 0, device=None,
                  product: str = "f32"):

@@ -185,8 +185,8 @@ echo_status echo_stage1(const void* const* partials, echo_state* st, echo_dir di
  * `dir` is only validated).  Follow with echo_owner and echo_decode on `dir`.
  * A, W: host arrays of P device pointers, 16-byte aligned, read-only.
  * Requires a bf16 state with group 32 and no own_exact (the owner would need
- * the partial itself), M and H multiples of 128 (M/128 <= 65535 and
- * (M/128)*(H/128) <= 2^26), K a multiple of 64 and at most 2^21.  Errors: ECHO_ERR_ARG (null or misaligned pointer, A or W
+ * the partial itself), M a multiple of 64 (M/64 <= 65535), H a multiple of
+ * 128 ((M/64)*(H/128) <= 2^27), K a multiple of 64 and at most 2^21.  Errors: ECHO_ERR_ARG (null or misaligned pointer, A or W
  * overlapping the workspace, own_exact on, bad dir), ECHO_ERR_SHAPE (sizes,
  * M*H != N, group != 32), ECHO_ERR_DTYPE (state not bf16), ECHO_ERR_STATE,
  * ECHO_ERR_HIP. */

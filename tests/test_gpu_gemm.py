@@ -22,11 +22,16 @@ pytestmark = pytest.mark.gpu
 # over many turns), plus fewer steps than slabs (the pipeline is never full)
 # and, for the grouped tile order, a tile count that is not a multiple of 8 (block
 # i then takes tile i of the row-tile-fastest order, without the XCD grouping).  By the number b of 128 x 128
-# tiles of the launch, the launcher takes
+# tiles of the launch, the launcher takes, for M a multiple of 128,
 #   b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
 #   b >= 1024 with M and H multiples of 256: 256 x 256, 2 slabs, grouped;
-#   else 128 x 128, 2 slabs, grouped.
+#   else 128 x 128, 2 slabs, grouped;
+# and 64 x 128 tiles with 4 slabs, grouped, for M an odd multiple of 64.
 SHAPES = [
+    (2, 64, 64, 128),        # M = 64: 64 x 128, 4 tiles, 1 K step
+    (8, 64, 512, 4096),      # M = 64: the decode-shaped layer's product (K = 4096 / 8), 8 steps
+    (3, 192, 320, 2816),     # M = 192: 198 tiles (not a multiple of 8), 5 steps
+    (4, 320, 1024, 1024),    # M = 320: 160 tiles, 16 steps
     (1, 128, 64, 128),       # b = 1: 64 x 128, 4 slabs, 2 tiles, 1 K step
     (2, 256, 512, 384),      # b = 12: 24 tiles, 8 steps
     (3, 384, 1024, 256),     # b = 18: 36 tiles, 16 steps
@@ -50,7 +55,7 @@ SHAPES = [
 ]
 # one shape per tile configuration in its steady state (and the benchmarked
 # ones), for the whole-call tests
-STEADY = [(2, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096), (8, 128, 3072, 4096),
+STEADY = [(8, 64, 512, 4096), (4, 320, 1024, 1024), (2, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096), (8, 128, 3072, 4096),
           (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
 
 
@@ -132,7 +137,8 @@ def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"call {t}") == 0
 
 
-@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096),
+@pytest.mark.parametrize("P,M,K,H", [(3, 256, 512, 384), (8, 64, 512, 4096), (3, 192, 320, 2816),
+                                     (8, 128, 3072, 1024), (4, 256, 640, 4096),
                                      (8, 128, 3072, 4096), (2, 2048, 512, 2048), (2, 2176, 512, 2048),
                                      (4, 2048, 128, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)])
 @pytest.mark.parametrize("sb16", [False, True])
@@ -184,7 +190,7 @@ def _special_inputs(case, P, M, K, H, seed, dev):
 
 @pytest.mark.parametrize("sfb", [False, True])
 @pytest.mark.parametrize("case", ["zeros_and_single_columns", "huge", "tiny", "subnormal"])
-@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 128, 64, 4096), (4, 256, 64, 4096),
+@pytest.mark.parametrize("P,M,K,H", [(2, 256, 128, 256), (2, 64, 128, 2048), (2, 128, 64, 4096), (4, 256, 64, 4096),
                                      (2, 2048, 64, 2048), (4, 2048, 64, 2048)])
 def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
     """The fused epilogue on special values, in every tile configuration, with and
@@ -213,7 +219,8 @@ def test_fused_special_values_match_the_oracle(cuda, P, M, K, H, case, sfb):
         assert _compare(_fetch(st, out, 0), o, so, 0, True, f"{case} call {t}") == 0
 
 
-@pytest.mark.parametrize("P,M,K,H", [(8, 128, 256, 1024), (4, 256, 256, 4096), (4, 2048, 128, 2048)])
+@pytest.mark.parametrize("P,M,K,H", [(8, 64, 512, 4096), (8, 128, 256, 1024), (4, 256, 256, 4096),
+                                     (4, 2048, 128, 2048)])
 def test_fused_calls_in_a_graph_match_eager_calls(cuda, P, M, K, H):
     """A graph holding a fused forward call (product with stage 1 and sender
     feedback, owner step, decode), a fused backward call and the written-out
@@ -283,7 +290,7 @@ def test_argument_errors(cuda):
     st = _state(P, M * H, "bf16", group=64)
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_SHAPE
     st = _state(P, M * H, "bf16")
-    assert lib.echo_gemm_stage1(arr(A), arr(W), 64, K, st.handle, 0, s) == B.ECHO_ERR_SHAPE
+    assert lib.echo_gemm_stage1(arr(A), arr(W), 96, K, st.handle, 0, s) == B.ECHO_ERR_SHAPE  # M % 64 != 0
     assert lib.echo_gemm_stage1(arr(A), arr(W), M, 96, st.handle, 0, s) == B.ECHO_ERR_SHAPE
     bad = (ctypes.c_void_p * P)(A[0].data_ptr(), A[1].data_ptr() + 2)
     assert lib.echo_gemm_stage1(bad, arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
