@@ -580,7 +580,103 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
                        if "cached" in t else {}),
                     "bf16_peak_TFLOPs": 2500.0,
                     "partial_bytes_not_written_or_read": 2 * 2 * P * M * H})
-    return {"config": "gemm", "shapes": res}
+    return {"config": "gemm", "shapes": res, "decode_layer": decode_layer_report(E, torch, dev)}
+
+
+def decode_layer_report(E, torch, dev) -> dict:
+    """The decode-shaped layer's row-parallel product and its reduction: P = 8
+    ranks, 64 tokens, K = 512 per rank (a 4096-wide layer split 8 ways), H = 4096.
+    Our variants run as 32 calls captured in one graph, each call on its own
+    weight set (1 GiB of weights in all, so every call reads its weights from
+    HBM), timed over ten replays (median, us per call): fused_product = the
+    product with stage 1 in its epilogue; fused_layer = that, the owner step and
+    the decode (the layer's whole reduction); unfused_layer = the product written
+    out, then echo_reduce; product = the product alone.  torch's product (one
+    library call per rank) is not captured; it is timed, with echo_reduce, as
+    eager calls from Python, beside our fused layer timed the same way.  The
+    fused layer's output must equal the unfused layer's, which is checked."""
+    P, M, K, H = 8, 64, 512, 4096
+    sets = GRAPH_CALLS
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    A = [torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16) for _ in range(P)]
+    Ws = [[(torch.randn(H, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16) for _ in range(P)]
+          for _ in range(sets)]
+    Wts = [[w.t().contiguous() for w in W] for W in Ws]
+    st = E.echo_init_state(E.EchoConfig.make(P, M * H, "bf16"), device=dev)
+    out = torch.empty(M * H, dtype=torch.float32, device=dev)
+    parts = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
+    flat = [q.view(-1) for q in parts]
+
+    def fused_product(W):
+        E.echo_gemm_stage1(A, W, st)
+
+    def fused_layer(W):
+        E.echo_gemm_stage1(A, W, st)
+        E.echo_owner(st, E.ECHO_FWD)
+        E.echo_decode(out, st)
+
+    def unfused_layer(W):
+        E.echo_gemm_bf16(A, W, parts)
+        E.echo_reduce(flat, out, st, E.ECHO_FWD)
+
+    def product(W):
+        E.echo_gemm_bf16(A, W, parts)
+
+    def library_layer(Wt):
+        for r in range(P):
+            torch.matmul(A[r], Wt[r], out=parts[r])
+        E.echo_reduce(flat, out, st, E.ECHO_FWD)
+
+    # the fused layer's output equals the unfused layer's (fresh state each)
+    E.echo_reset(st, 3)
+    fused_layer(Ws[0])
+    ref = out.clone()
+    E.echo_reset(st, 3)
+    unfused_layer(Ws[0])
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, ref))
+    if not same:
+        raise RuntimeError("the fused decode layer's output differs from the unfused layer's")
+
+    def median_us(run, calls, reps=10):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / calls)
+        return round(sorted(ts)[len(ts) // 2], 2)
+
+    graph_us = {}
+    for name, fn in (("fused_product", fused_product), ("fused_layer", fused_layer),
+                     ("unfused_layer", unfused_layer), ("product", product)):
+        fn(Ws[0])
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(sets):
+                fn(Ws[i])
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        graph_us[name] = median_us(gr.replay, sets)
+
+    def eager(fn, ws):
+        def run():
+            for i in range(sets):
+                fn(ws[i])
+        run()
+        torch.cuda.synchronize()
+        return median_us(run, sets)
+
+    eager_us = {"fused_layer": eager(fused_layer, Ws), "library_then_echo_reduce": eager(library_layer, Wts)}
+    return {"P": P, "M": M, "K": K, "H": H, "weights": f"cold: {sets} sets of {P * H * K * 2 / 2 ** 20:.0f} MiB",
+            "fused_layer_equals_unfused_layer": same, "us_per_call_graph_32": graph_us,
+            "weight_GBps_fused_product": round(P * H * K * 2 / (graph_us["fused_product"] * 1e-6) / 1e9, 1),
+            "us_per_call_eager": eager_us}
 
 
 def trace_gaps(trace_csv: str, kernels_per_call: int = 3, calls_per_replay: int = GRAPH_CALLS) -> dict:
