@@ -894,7 +894,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P ranks "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); the P ranks "
               "are emulated as P partial buffers in one GPU's HBM.", file=sys.stderr)
         sys.exit(2)
 
