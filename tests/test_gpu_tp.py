@@ -81,13 +81,15 @@ def test_tp_step_errors_against_exact_allreduce(cuda):
         assert e_loss < 0.05 and e_dx < 0.5 and e_dw < 0.5
 
 
+@pytest.mark.parametrize("tokens", [T, 64])
 @pytest.mark.parametrize("variant", [{}, {"sender_feedback": True, "state_bf16": True}])
-def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant):
+def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant, tokens):
     """Row-parallel products in bfloat16 on libecho's kernel: with stage 1 in the
     product's epilogue the whole training step (loss, input and weight
     gradients) is bit-identical to the product written out and reduced by
     echo_reduce, and every reduction matches the oracle run on the partials the
-    written-out product gives (teacher-forced, one oracle state per direction)."""
+    written-out product gives (teacher-forced, one oracle state per direction).
+    64 tokens take the product's 64-row tiles."""
     import torch
     import error_compensated_bit_echo_amd as E
     from error_compensated_bit_echo_amd import tp
@@ -96,22 +98,22 @@ def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant):
         model = tp.TPMLPStack(L, H, F, P, seed=11, device=cuda, product=prod)
         g = torch.Generator(device=cuda)
         g.manual_seed(12)
-        x0 = torch.randn(T, H, generator=g, device=cuda)
-        target = torch.randn(T, H, generator=g, device=cuda)
-        group = tp.EchoGroup(P, T * H, mode="echo", device=cuda, record=(prod == "bf16_fused"), **variant)
+        x0 = torch.randn(tokens, H, generator=g, device=cuda)
+        target = torch.randn(tokens, H, generator=g, device=cuda)
+        group = tp.EchoGroup(P, tokens * H, mode="echo", device=cuda, record=(prod == "bf16_fused"), **variant)
         res[prod] = (tp.train_step(model, group, x0, target), group)
     (lf, dxf, dwf), gf = res["bf16_fused"]
     (lu, dxu, dwu), _ = res["bf16"]
     assert torch.equal(lf, lu) and torch.equal(dxf, dxu)
     assert all(torch.equal(a, b) for a, b in zip(dwf, dwu))
 
-    st = eo.OracleState(T * H)
+    st = eo.OracleState(tokens * H)
     assert [d for d, _, _ in gf.log] == [0] * L + [1] * L
     for k, (d, parts, out) in enumerate(gf.log):
         if d == 0:
             tag, A, W = parts
             assert tag == "product"
-            written = [torch.empty(T, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
+            written = [torch.empty(tokens, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
             E.echo_gemm_bf16(A, W, written)
             parts = written
         host = np.stack([p.reshape(-1).float().cpu().numpy() for p in parts])
