@@ -504,6 +504,10 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
     finds its weights in the 256 MB Infinity Cache, as in a model whose layers
     each bring their own weights.  The activations stay the same.  The same
     timings with one weight set (cached after the first call) are given beside.
+    torch's product gets the weights as they are given, [H, K] (transposed in the
+    call): hipBLASLt was faster that way than on pre-transposed [K, H] copies
+    (51.5 against 56.8 us at the prefill-like shape, 20.2 against 25.6 us at the
+    decode-like one, per rank).
     `weights` ("cold", "cached" or "both") picks which of the two are timed, so
     that a profiler's kernel trace holds one kind only."""
     res = []
@@ -515,7 +519,6 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
         A = [torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16) for _ in range(P)]
         Ws = [[(torch.randn(H, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16) for _ in range(P)]
               for _ in range(nsets)]
-        Wts = [[w.t().contiguous() for w in W] for W in Ws]  # [K, H] for a plain (not transposed) library product
         out = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
         st = E.echo_init_state(E.EchoConfig.make(P, M * H, "bf16"), device=dev)
         flat = [o.view(-1) for o in out]
@@ -528,8 +531,9 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
             E.echo_stage1(flat, st)
 
         def library_unfused(i):
+            # the library's faster layout here: W_r as given ([H, K]), transposed in the call
             for r in range(P):
-                torch.matmul(A[r], Wts[i][r], out=out[r])
+                torch.matmul(A[r], Ws[i][r].t(), out=out[r])
             E.echo_stage1(flat, st)
 
         def product_only(i):
@@ -602,7 +606,6 @@ def decode_layer_report(E, torch, dev) -> dict:
     A = [torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16) for _ in range(P)]
     Ws = [[(torch.randn(H, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16) for _ in range(P)]
           for _ in range(sets)]
-    Wts = [[w.t().contiguous() for w in W] for W in Ws]
     st = E.echo_init_state(E.EchoConfig.make(P, M * H, "bf16"), device=dev)
     out = torch.empty(M * H, dtype=torch.float32, device=dev)
     parts = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in range(P)]
@@ -623,9 +626,9 @@ def decode_layer_report(E, torch, dev) -> dict:
     def product(W):
         E.echo_gemm_bf16(A, W, parts)
 
-    def library_layer(Wt):
+    def library_layer(W):
         for r in range(P):
-            torch.matmul(A[r], Wt[r], out=parts[r])
+            torch.matmul(A[r], W[r].t(), out=parts[r])
         E.echo_reduce(flat, out, st, E.ECHO_FWD)
 
     # the fused layer's output equals the unfused layer's (fresh state each)
@@ -672,7 +675,7 @@ def decode_layer_report(E, torch, dev) -> dict:
         torch.cuda.synchronize()
         return median_us(run, sets)
 
-    eager_us = {"fused_layer": eager(fused_layer, Ws), "library_then_echo_reduce": eager(library_layer, Wts)}
+    eager_us = {"fused_layer": eager(fused_layer, Ws), "library_then_echo_reduce": eager(library_layer, Ws)}
     return {"P": P, "M": M, "K": K, "H": H, "weights": f"cold: {sets} sets of {P * H * K * 2 / 2 ** 20:.0f} MiB",
             "fused_layer_equals_unfused_layer": same, "us_per_call_graph_32": graph_us,
             "weight_GBps_fused_product": round(P * H * K * 2 / (graph_us["fused_product"] * 1e-6) / 1e9, 1),
