@@ -271,6 +271,34 @@ def test_fused_calls_in_a_graph_match_eager_calls(cuda, P, M, K, H):
         _ = (oe * 2).sum().item()  # unrelated eager work between replays
 
 
+def test_largest_row_count(cuda):
+    """M = 64 * 65535, the most rows the product accepts: 65535 row blocks of 64
+    in the launch grid.  Sampled row blocks (the first, one in the middle and
+    the last) of the written-out product against the exact product of the same
+    bf16 inputs, and the whole fused payload bit for bit against stage 1 of the
+    written-out product."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, M, K, H = 1, 64 * 65535, 64, 128
+    A, W = _inputs(P, M, K, H, 9, cuda)
+    out = _unfused(A, W)
+    w_host = W[0].float().cpu().numpy().astype(np.float64)
+    for r0 in (0, (M // 2) // 64 * 64, M - 64):
+        a = A[0][r0:r0 + 64].float().cpu().numpy().astype(np.float64)
+        exact = a @ w_host.T
+        mag = np.abs(a) @ np.abs(w_host).T
+        got = out[0][r0:r0 + 64].float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + mag * K * 2.0 ** -24), f"rows {r0}.."
+    N = M * H
+    fused = E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=False), device=cuda)
+    E.echo_gemm_stage1(A, W, fused)
+    ref = E.echo_init_state(E.EchoConfig.make(P, N, "bf16", compensate=False), device=cuda)
+    E.echo_stage1([out[0].view(-1)], ref)
+    vf, vr = E.echo_debug_views(fused), E.echo_debug_views(ref)
+    torch.cuda.synchronize()
+    assert torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
+
+
 def test_argument_errors(cuda):
     import ctypes
     import error_compensated_bit_echo_amd as E
