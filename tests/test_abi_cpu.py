@@ -155,7 +155,8 @@ def test_product_entry_point_rejects_bad_shapes_without_touching_the_gpu():
     outs = (ctypes.c_void_p * 2)(1 << 20, 2 << 20)
     for P, M, K, H in ((0, 128, 64, 128), (17, 128, 64, 128), (2, 100, 64, 128), (2, 96, 64, 128),
                        (2, 128, 96, 128), (2, 128, 64, 200), (2, 0, 64, 128), (2, 64 * 65536, 64, 128),
-                       (2, 64 * 65535, 64, 128 * 32770), (1, 128, 64, 128 * (2 ** 26 + 1))):
+                       (2, 64 * 65535, 64, 128 * 32770), (1, 128, 64, 128 * (2 ** 26 + 1)),
+                       (1, 64, 2 ** 21 + 64, 128)):
         assert lib.echo_gemm_bf16(fake, fake, outs, P, M, K, H, None) == B.ECHO_ERR_SHAPE
     nulls = (ctypes.c_void_p * 2)(None, None)
     assert lib.echo_gemm_bf16(nulls, fake, outs, 2, 128, 64, 128, None) == B.ECHO_ERR_ARG

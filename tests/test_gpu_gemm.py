@@ -299,6 +299,33 @@ def test_largest_row_count(cuda):
     assert torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
 
 
+def test_largest_k(cuda):
+    """K = 2^21, the longest product accepted (a 64-row panel then spans 256 MiB
+    of 32-bit buffer offsets, the K step's offset reaching 4 MiB): eight sampled
+    output columns against the exact product of the same bf16 inputs, and the
+    fused payload bit for bit against stage 1 of the written-out product."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    P, M, K, H = 1, 64, 1 << 21, 128
+    A, W = _inputs(P, M, K, H, 13, cuda)
+    out = _unfused(A, W)
+    cols = [0, 1, 31, 32, 63, 64, 100, 127]
+    a = A[0].float().cpu().numpy().astype(np.float64)
+    w = W[0][cols].float().cpu().numpy().astype(np.float64)
+    exact = a @ w.T
+    mag = np.abs(a) @ np.abs(w).T
+    got = out[0][:, cols].float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * 2.0 ** -8 + mag * K * 2.0 ** -24)
+    N = M * H
+    fused = E.echo_init_state(E.EchoConfig.make(P, N, "bf16"), device=cuda)
+    E.echo_gemm_stage1(A, W, fused)
+    ref = E.echo_init_state(E.EchoConfig.make(P, N, "bf16"), device=cuda)
+    E.echo_stage1([out[0].view(-1)], ref)
+    vf, vr = E.echo_debug_views(fused), E.echo_debug_views(ref)
+    torch.cuda.synchronize()
+    assert torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
+
+
 def test_argument_errors(cuda):
     import ctypes
     import error_compensated_bit_echo_amd as E
