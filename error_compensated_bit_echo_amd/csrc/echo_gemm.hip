@@ -14,7 +14,8 @@
 // Tiling: a block computes a 256 x 256 tile of one rank's [M, H] partial with 8
 // wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles,
 // where the product is large enough; 128 x 128 with 8 wavefronts (32 x 64 each)
-// for mid-sized and short products; 64 x 128 with 4 wavefronts for the shortest.
+// for mid-sized and short products; 64 x 128 with 4 wavefronts for the shortest
+// and where M is an odd multiple of 64.
 // K advances 64 at a time through a ring of LDS slabs: while the matrix cores
 // work on one slab, the next ones stream from global memory straight into the
 // others (buffer_load_dwordx4 ... lds through a buffer resource over the block's
@@ -135,7 +136,7 @@ __device__ __forceinline__ void slab_barrier() {
 //     steps of loads in flight, for products of at most one tile per CU, which
 //     stream their weights and are bound by memory rather than matrix work;
 //   64 x 128, 4 wavefronts, 4 slabs (96 KiB): the same for products of at most
-//     half a tile per CU, in twice as many blocks.
+//     half a tile per CU, in twice as many blocks, and for M an odd multiple of 64.
 // SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
 // XG: the tile order.  The hardware hands the blocks of a launch to the eight
@@ -143,12 +144,11 @@ __device__ __forceinline__ void slab_barrier() {
 // the tiles are ordered row tile fastest, then column panel, then rank, and
 // block i takes tile (i % 8) T/8 + i / 8 of them when the T tiles are a
 // multiple of 8 (else tile i), so that each XCD works through one contiguous
-// run of them: the row tiles of a column panel
-// share an XCD (its weights come from memory once), and so do as few ranks as
-// the run spans (each rank's activations come from memory once per XCD that
-// needs them; at P = 8 with 32 panels of 128 columns, one rank per XCD instead
-// of all eight on every XCD).  Without XG, tile (x, y, r) is block
-// x + gx (y + gy r), column panel fastest.
+// run of them: the row tiles of a column panel share an XCD (its weights come
+// from memory once), and so do as few ranks as the run spans (each rank's
+// activations come from memory once per XCD that needs them; at P = 8 with 32
+// panels of 128 columns, one rank per XCD instead of all eight on every XCD).
+// Without XG, tile (x, y, r) is block x + gx (y + gy r), column panel fastest.
 // WNT: the weight loads are non-temporal, for the products of at most one tile
 // per CU, where the blocks that read a weight panel (one or two) run at the
 // same time on one XCD and nothing reads it later.
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // Two rings of LDS slabs.  Without WAHEAD, S slabs each hold a K step's A and
-  // W tiles: K step `it` multiplies slab it % S, and the loads of step
+  // The slab rings.  Without WAHEAD, S slabs each hold a K step's A and W
+  // tiles: K step `it` multiplies slab it % S, and the loads of step
   // it + S - 1 are issued at its start into the slab step it - 1 used.  With
   // WAHEAD, two slabs of A tiles and, after them, three of W tiles: step it
   // multiplies A slot it % 2 and W slot it % 3 and issues the loads of A for
@@ -249,14 +249,14 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   // when cold while the activations are usually cached, have two steps to
   // arrive.  Either way a load goes into a slot that step it - 1 read and every
   // wavefront has finished reading: each waits for its own LDS reads before
-  // the barrier that ends a step.  The fragments of a step's four 16-deep sub-steps are
-  // double-buffered in registers: the reads of sub-step k + 1 go out before the
-  // MFMAs of sub-step k, and the reads of the next slab's first sub-step right
-  // after the barrier, before the last sub-step's MFMAs.  (The compiler's own
-  // wait before a sub-step's MFMAs would be for every outstanding LDS read, the
-  // new ones included; each sub-step therefore first drains the reads issued a
-  // sub-step earlier, which have had the MFMAs between to land, and its MFMAs
-  // need no wait.)
+  // the barrier that ends a step.  The fragments of a step's four 16-deep
+  // sub-steps are double-buffered in registers: the reads of sub-step k + 1 go
+  // out before the MFMAs of sub-step k, and the reads of the next slab's first
+  // sub-step right after the barrier, before the last sub-step's MFMAs.  (The
+  // compiler's own wait before a sub-step's MFMAs would be for every
+  // outstanding LDS read, the new ones included; each sub-step therefore first
+  // drains the reads issued a sub-step earlier, which have had the MFMAs
+  // between to land, and its MFMAs need no wait.)
   const int64_t steps = K / kTileK;
   bf16x8 af[2][MI], bf[2][NJ];
   auto read_frags = [&](auto buf, const uint16_t* As, const uint16_t* Ws, int ks) {
