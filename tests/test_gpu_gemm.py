@@ -52,6 +52,8 @@ SHAPES = [
     (4, 2048, 576, 2048),    # b = 1024: 9 steps (an odd count: the last step reads the other slab)
     (4, 2048, 3072, 4096),   # b = 2048: 48 steps: the product the benchmark times
     (5, 2304, 64, 2304),     # b = 1620: 405 tiles (not a multiple of 8), 1 step
+    (16, 384, 192, 1024),    # b = 384: 128 x 128, 2 slabs, 16 ranks, 3 steps
+    (16, 1024, 128, 1024),   # b = 1024: 256 x 256, 16 ranks, 2 steps
 ]
 # one shape per tile configuration in its steady state (and the benchmarked
 # ones), for the whole-call tests
@@ -118,7 +120,7 @@ def test_fused_payload_equals_stage1_of_the_unfused_partial(cuda, P, M, K, H):
 
 @pytest.mark.parametrize("P,M,K,H", [(4, 256, 1024, 512), (8, 128, 512, 1024), (3, 128, 320, 2816),
                                      (3, 128, 320, 7296), (2, 2048, 128, 2048), (2, 2176, 128, 2048),
-                                     (3, 128, 320, 11008), (4, 2048, 192, 2048)] + STEADY)
+                                     (3, 128, 320, 11008), (4, 2048, 192, 2048), (16, 1024, 128, 1024)] + STEADY)
 def test_fused_whole_calls_match_the_oracle(cuda, P, M, K, H):
     import error_compensated_bit_echo_amd as E
     torch = _torch()
