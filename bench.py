@@ -293,8 +293,9 @@ def decode_report(E, synth, torch, dev) -> dict:
     compensation, without, with compensation and sender feedback, and an exact
     all-reduce in float64).  Per-call
     latency of echo_reduce: eager from Python (includes the binding's host
-    time), one captured call replayed per layer, and 32 back-to-back calls in
-    one graph (the library's own per-call time)."""
+    time), eager from plain C through the C ABI, one captured call replayed per
+    layer, and 32 back-to-back calls in one graph (the library's own per-call
+    time)."""
     c = synth.DECODE_CHAIN
     P, rows, hd, L = 8, c["rows"], c["hidden"], c["layers"]
     N = rows * hd
@@ -367,7 +368,26 @@ def decode_report(E, synth, torch, dev) -> dict:
         "us_per_call_minus_sum_of_stages": round(_pct(g32, 0.5) - sum(stage_us.values()), 2),
         "graph_replay_equals_eager_every_layer": graph_equal,
         "rel_rms_err_vs_exact_allreduce_chain": rel,
+        "c_abi_eager": c_abi_latency(P, N),
     }
+
+
+def c_abi_latency(P: int, N: int, calls: int = 2000) -> dict:
+    """Per-call latency of eager echo_reduce calls made from plain C through the
+    C ABI (tests/c_client/echo_c_latency, built with the library): device time of
+    back-to-back calls, the host's time to issue one call, and one call followed
+    by a stream synchronize.  Run as a child process on the same GPU."""
+    import subprocess
+
+    from error_compensated_bit_echo_amd import build as b
+    if not os.path.exists(b.C_LATENCY):
+        raise RuntimeError(f"{b.C_LATENCY} is not built (python -c 'import __graft_entry__ as g; g.build()')")
+    r = subprocess.run([b.C_LATENCY, str(P), str(N), str(calls)], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        raise RuntimeError(f"echo_c_latency failed ({r.returncode}): {r.stderr.strip()}")
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"us_per_call": {k: res[k] for k in ("device_us", "enqueue_us", "roundtrip_us")}, "calls": calls,
+            "note": "plain C, default stream, the same partials every call"}
 
 
 def tp_report(torch, dev) -> dict:

@@ -76,19 +76,28 @@ def build_library(verbose: bool = False, jobs: int = 0) -> str:
 
 C_CLIENT_SRC = os.path.join(ROOT, "tests", "c_client", "echo_c_client.c")
 C_CLIENT = os.path.join(ROOT, "tests", "c_client", "echo_c_client")
+C_LATENCY_SRC = os.path.join(ROOT, "tests", "c_client", "echo_c_latency.c")
+C_LATENCY = os.path.join(ROOT, "tests", "c_client", "echo_c_latency")
+
+
+def _build_c(src: str, exe: str, verbose: bool) -> str:
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-D__HIP_PLATFORM_AMD__", "-D_POSIX_C_SOURCE=199309L", f"-I{INCLUDE}", "-isystem",
+           os.path.join(rocm, "include"), src, f"-L{PKG}", "-lecho", f"-L{os.path.join(rocm, 'lib')}",
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../error_compensated_bit_echo_amd",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", exe]
+    _run(cmd, verbose)
+    return exe
 
 
 def build_c_client(verbose: bool = False) -> str:
-    """Compile the plain C test client of the C ABI (gcc, strict C11) against
-    the built libecho.so and the HIP runtime; returns its path."""
-    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
-    cmd = [shutil.which("gcc") or "gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic",
-           "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", "-isystem", os.path.join(rocm, "include"),
-           C_CLIENT_SRC, f"-L{PKG}", "-lecho", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
-           "-Wl,-rpath,$ORIGIN/../../error_compensated_bit_echo_amd",
-           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_CLIENT]
-    _run(cmd, verbose)
-    return C_CLIENT
+    """Compile the plain C clients of the C ABI (gcc, strict C11) against the
+    built libecho.so and the HIP runtime: the test client and the per-call
+    latency program that `bench.py --config decode` runs; returns the test
+    client's path."""
+    _build_c(C_LATENCY_SRC, C_LATENCY, verbose)
+    return _build_c(C_CLIENT_SRC, C_CLIENT, verbose)
 
 
 if __name__ == "__main__":
