@@ -360,18 +360,42 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     slab_barrier();
+    // The 256-column tiles issue W(it + 2) a quarter at a time, one share before
+    // each sub-step's MFMAs, rather than in one burst with A(it + 1) at the
+    // step's start; A(it + 1) still goes out first, so the end-of-step wait is
+    // unchanged.  (Measured with the weights cold: at P = 4, M = 2048,
+    // K = 3072, H = 4096 176.2 against 181.8 us, at P = 8 345.3 against 358.7;
+    // no faster on the 128 x 128 tiles, nor with A spread over the first two
+    // sub-steps as well.)
+    constexpr bool kSpreadW = TN == 256;
+    static_assert(!kSpreadW || JW % 4 == 0, "weight loads split evenly over the four sub-steps");
     auto step = [&](int64_t it, auto last) {
       const bool w_more = it + 2 < steps;
       const int sa1 = sa ^ 1, sw1 = next3(sw), sw2 = next3(sw1);
+      constexpr bool kSpread = kSpreadW && !decltype(last)::value;
+      auto issue_w_share = [&](int q) {  // share q of W(it + 2): loads q JW/4 .. (q + 1) JW/4 - 1
+        const uint32_t kb = static_cast<uint32_t>((it + 2) * kTileK * 2);
+        uint16_t* const Ws2 = wbase + sw2 * kSlabW;
+#pragma unroll
+        for (int j = q * (JW / 4); j < (q + 1) * (JW / 4); ++j)
+          buffer_load_lds16<WNT ? kNonTemporal : 0>(rW, Ws2 + 512 * (JW * wave + j), offW[j], kb);
+      };
       if constexpr (!decltype(last)::value) {
         issue_a_to(abase + sa1 * kSlabA, it + 1);
-        if (w_more) issue_w_to(wbase + sw2 * kSlabW, it + 2);
+        if constexpr (kSpread) {
+          if (w_more) issue_w_share(0);
+        } else {
+          if (w_more) issue_w_to(wbase + sw2 * kSlabW, it + 2);
+        }
       }
       const uint16_t* As = abase + sa * kSlabA;
       const uint16_t* Ws = wbase + sw * kSlabW;
       sub_step(B0, B1, As, Ws, 1);
+      if constexpr (kSpread) if (w_more) issue_w_share(1);
       sub_step(B1, B0, As, Ws, 2);
+      if constexpr (kSpread) if (w_more) issue_w_share(2);
       sub_step(B0, B1, As, Ws, 3);
+      if constexpr (kSpread) if (w_more) issue_w_share(3);
       if constexpr (!decltype(last)::value) {
         if (w_more)
           __builtin_amdgcn_s_waitcnt(vmcnt_at_most_lds_drained(JW));
