@@ -15,7 +15,8 @@
 // wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles,
 // where the product is large enough; 128 x 128 with 8 wavefronts (32 x 64 each)
 // for mid-sized and short products; 64 x 128 with 4 wavefronts for the shortest
-// and where M is an odd multiple of 64.
+// and where M is an odd multiple of 64; 64 x 64 with 4 wavefronts (one 32 x 32
+// MFMA tile each) where even 64 x 128 tiles would leave CUs idle.
 // K advances 64 at a time through a ring of LDS slabs: while the matrix cores
 // work on one slab, the next ones stream from global memory straight into the
 // others (buffer_load_dwordx4 ... lds through a buffer resource over the block's
@@ -136,7 +137,9 @@ __device__ __forceinline__ void slab_barrier() {
 //     steps of loads in flight, for products of at most one tile per CU, which
 //     stream their weights and are bound by memory rather than matrix work;
 //   64 x 128, 4 wavefronts, 4 slabs (96 KiB): the same for products of at most
-//     half a tile per CU, in twice as many blocks, and for M an odd multiple of 64.
+//     half a tile per CU, in twice as many blocks, and for M an odd multiple of 64;
+//   64 x 64, 4 wavefronts, 4 slabs (64 KiB): the same where 64 x 128 tiles would
+//     number at most 128, half the CUs.
 // SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
 // XG: the tile order.  The hardware hands the blocks of a launch to the eight
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
   constexpr int CW = TN / 2;                       // columns per wavefront
   constexpr int NJ = CW / 32;                      // 32-column MFMA tiles per wavefront
   static_assert(MI == 1 || MI == 2, "one or two 32-row MFMA tiles per wavefront");
-  static_assert(TN == 128 || TN == 256, "128- or 256-column block tiles");
+  static_assert(TN == 64 || TN == 128 || TN == 256, "64-, 128- or 256-column block tiles");
   constexpr int JA = BM / (8 * NW), JW = TN / (8 * NW);  // 1 KiB slab blocks per wavefront
   static_assert(JA * 8 * NW == BM && JW * 8 * NW == TN, "slab blocks split evenly");
   constexpr int kLoads = JA + JW;                  // global loads per wavefront per slab
@@ -559,7 +562,15 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 
 }  // namespace
 
-// For M a multiple of 128, by the number b of 128 x 128 tiles of the whole launch (all ranks):
+// Where the launch has at most 128 tiles of 64 x 128 (all ranks), 64 x 64 tiles,
+// 4 slabs, grouped, weights non-temporal: one block per CU instead of one per two
+// CUs.  Measured cold (as below), us: P = 2, M = 128, K = 3072, H = 4096: 19.3
+// against 27.5 for 64 x 128 tiles; P = 4, M = 64, same K and H: 21.8 against
+// 30.2; P = 1, M = 128, K = 4096, H = 8192: 24.1 against 32.4; P = 2, M = 128,
+// K = 512, H = 4096: 7.5 against 8.6.  With 256 tiles of 64 x 128 they were no
+// faster (P = 8, M = 64, K = 512, H = 4096: 11.5 against 11.5) or slower (P = 4,
+// M = 128, K = 3072, H = 4096: 35.6 against 30.3), and 6 or 8 slabs no faster.
+// Otherwise, for M a multiple of 128, by the number b of 128 x 128 tiles of the whole launch:
 //   b <= 128: 64 x 128, 4 slabs, grouped, weights non-temporal;
 //   b <= 256: 128 x 128, 8 wavefronts, 4 slabs, grouped, weights non-temporal;
 //   b >= 1024 with M and H multiples of 256: 256 x 256, grouped, weights ahead;
@@ -585,6 +596,9 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 //   P = 8, M = 256, K = 3072, H = 4096: 67.5 against 72.2 without the third W
 //     slab, 74.7 for 128 x 128 tiles with 4 slabs and 78.2 for 256 x 128.
 hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
+  // at most 128 tiles of 64 x 128 over all ranks: 64 x 64 tiles
+  if ((a.M / kGemmRowStep) * (a.H / kGemmTileN) * P <= 128)
+    return gemm_cfg<64, 64, 4, 4, true, true, false>(a, P, fused, s);
   // M a multiple of 64 but not of 128: 64 x 128 tiles, 4 slabs, grouped; the
   // weight loads non-temporal for M = 64, where each weight panel has one reader
   if (a.M % kGemmTileM != 0)

@@ -21,24 +21,29 @@ pytestmark = pytest.mark.gpu
 # with S slabs each tile runs at least S + 1 steps (and the ring is exercised
 # over many turns), plus fewer steps than slabs (the pipeline is never full)
 # and, for the grouped tile order, a tile count that is not a multiple of 8 (block
-# i then takes tile i of the row-tile-fastest order, without the XCD grouping).  By the number b of 128 x 128
-# tiles of the launch, the launcher takes, for M a multiple of 128,
-#   b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
+# i then takes tile i of the row-tile-fastest order, without the XCD grouping).
+# With n the number of 64 x 128 tiles of the launch (all ranks) and b that of
+# 128 x 128 tiles, the launcher takes
+#   n <= 128: 64 x 64, 4 slabs, grouped;
+#   else, for M an odd multiple of 64: 64 x 128, 4 slabs, grouped;
+#   else b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
 #   b >= 1024 with M and H multiples of 256: 256 x 256, 2 slabs, grouped;
-#   else 128 x 128, 2 slabs, grouped;
-# and 64 x 128 tiles with 4 slabs, grouped, for M an odd multiple of 64.
+#   else 128 x 128, 2 slabs, grouped.
 SHAPES = [
-    (2, 64, 64, 128),        # M = 64: 64 x 128, 4 tiles, 1 K step
-    (8, 64, 512, 4096),      # M = 64: the decode-shaped layer's product (K = 4096 / 8), 8 steps
-    (3, 192, 320, 2816),     # M = 192: 198 tiles (not a multiple of 8), 5 steps
-    (4, 320, 1024, 1024),    # M = 320: 160 tiles, 16 steps
-    (1, 128, 64, 128),       # b = 1: 64 x 128, 4 slabs, 2 tiles, 1 K step
-    (2, 256, 512, 384),      # b = 12: 24 tiles, 8 steps
-    (3, 384, 1024, 256),     # b = 18: 36 tiles, 16 steps
-    (2, 128, 64, 4096),      # b = 64: 1 step
-    (4, 128, 192, 2048),     # b = 64: 3 steps (the prologue fills every slab but one)
-    (8, 128, 3072, 1024),    # b = 64: 48 steps
-    (3, 128, 320, 2816),     # b = 66: 132 tiles (not a multiple of 8), 5 steps
+    (2, 64, 64, 128),        # n = 2: 64 x 64, 4 tiles, 1 K step
+    (1, 128, 64, 128),       # n = 2: 64 x 64, 4 tiles, 1 K step
+    (4, 128, 192, 2048),     # n = 128: 64 x 64, 256 tiles, 3 steps (the prologue fills every slab but one)
+    (2, 128, 64, 4096),      # n = 128: 64 x 64, 256 tiles, 1 step
+    (3, 64, 320, 1408),      # n = 33: 64 x 64, 66 tiles (not a multiple of 8), 5 steps
+    (2, 256, 512, 384),      # n = 24: 64 x 64, 48 tiles, 8 steps
+    (3, 384, 1024, 256),     # n = 36: 64 x 64, 72 tiles, 16 steps
+    (8, 128, 3072, 1024),    # n = 128: 64 x 64, 256 tiles, 48 steps
+    (8, 64, 512, 4096),      # M = 64, n = 256: 64 x 128, the decode-shaped layer's product (K = 4096 / 8), 8 steps
+    (3, 192, 320, 2816),     # M = 192: 64 x 128, 198 tiles (not a multiple of 8), 5 steps
+    (4, 320, 1024, 1024),    # M = 320: 64 x 128, 160 tiles, 16 steps
+    (4, 128, 128, 4096),     # b = 128: 64 x 128, 256 tiles, 2 steps
+    (4, 128, 1024, 4096),    # b = 128: 64 x 128, 16 steps
+    (3, 128, 320, 2816),     # b = 66: 64 x 128, 132 tiles (not a multiple of 8), 5 steps
     (16, 128, 128, 2048),    # b = 256: 128 x 128, 4 slabs, 2 steps
     (4, 256, 640, 4096),     # b = 256: 10 steps
     (8, 128, 3072, 4096),    # b = 256: 48 steps: the short product the benchmark times
@@ -57,8 +62,8 @@ SHAPES = [
 ]
 # one shape per tile configuration in its steady state (and the benchmarked
 # ones), for the whole-call tests
-STEADY = [(8, 64, 512, 4096), (4, 320, 1024, 1024), (2, 256, 512, 384), (8, 128, 3072, 1024), (4, 256, 640, 4096), (8, 128, 3072, 4096),
-          (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
+STEADY = [(8, 64, 512, 4096), (4, 320, 1024, 1024), (2, 256, 512, 384), (8, 128, 3072, 1024), (4, 128, 1024, 4096),
+          (4, 256, 640, 4096), (8, 128, 3072, 4096), (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
