@@ -139,7 +139,9 @@ __device__ __forceinline__ void slab_barrier() {
 //   64 x 128, 4 wavefronts, 4 slabs (96 KiB): the same for products of at most
 //     half a tile per CU, in twice as many blocks, and for M an odd multiple of 64;
 //   64 x 64, 4 wavefronts, 4 slabs (64 KiB): the same where 64 x 128 tiles would
-//     number at most 128, half the CUs.
+//     number at most 128, half the CUs;
+//   256 x 128, 8 wavefronts, 3 slabs (144 KiB): one block per CU for products of
+//     one to two 128 x 128 tiles per CU, each weight panel read once per block.
 // SFB (fused only): 0 no sender feedback; 1 the rank's stage-1 errors are fp32;
 // 2 they are bfloat16 (each new error rounded to nearest even before it is kept).
 // XG: the tile order.  The hardware hands the blocks of a launch to the eight
@@ -573,6 +575,13 @@ hipError_t gemm_cfg(const GemmArgs& a, int P, bool fused, hipStream_t s) {
 // Otherwise, for M a multiple of 128, by the number b of 128 x 128 tiles of the whole launch:
 //   b <= 128: 64 x 128, 4 slabs, grouped, weights non-temporal;
 //   b <= 256: 128 x 128, 8 wavefronts, 4 slabs, grouped, weights non-temporal;
+//   b <= 512 with M a multiple of 256: 256 x 128, 8 wavefronts, 3 slabs, grouped,
+//     weights non-temporal (cold, us: P = 8, M = 256, K = 3072, H = 4096 61.5
+//     against 68.1 for 128 x 128 tiles with 2 slabs and weights ahead; P = 6,
+//     same M, K and H, 53.9 against 64.1; P = 4, M = 512, 55.4 against 60.7;
+//     P = 16, M = 256, H = 2048, 60.9 against 68.8; P = 1, M = 2048, 55.9 against
+//     56.4; with the weights in the Infinity Cache 4-12 % slower, e.g. 61.5
+//     against 54.6 at the first shape);
 //   b >= 1024 with M and H multiples of 256: 256 x 256, grouped, weights ahead;
 //   else 128 x 128, 8 wavefronts, 2 slabs, grouped, weights ahead.
 // Measured with the weights cold (each call's weights last touched more than
@@ -607,6 +616,7 @@ hipError_t launch_gemm(const GemmArgs& a, int P, bool fused, hipStream_t s) {
   const int64_t b = (a.M / kGemmTileM) * (a.H / kGemmTileN) * P;
   if (b <= 128) return gemm_cfg<64, 128, 4, 4, true, true, false>(a, P, fused, s);
   if (b <= 256) return gemm_cfg<128, 128, 8, 4, true, true, false>(a, P, fused, s);
+  if (b <= 512 && a.M % 256 == 0) return gemm_cfg<256, 128, 8, 3, true, true, false>(a, P, fused, s);
   if (b >= 1024 && a.M % 256 == 0 && a.H % 256 == 0) return gemm_cfg<256, 256, 8, 2, true, false, true>(a, P, fused, s);
   return gemm_cfg<128, 128, 8, 2, true, false, true>(a, P, fused, s);
 }

@@ -27,6 +27,7 @@ pytestmark = pytest.mark.gpu
 #   n <= 128: 64 x 64, 4 slabs, grouped;
 #   else, for M an odd multiple of 64: 64 x 128, 4 slabs, grouped;
 #   else b <= 128: 64 x 128, 4 slabs, grouped;  b <= 256: 128 x 128, 4 slabs, grouped;
+#   b <= 512 with M a multiple of 256: 256 x 128, 3 slabs, grouped;
 #   b >= 1024 with M and H multiples of 256: 256 x 256, 2 slabs, grouped;
 #   else 128 x 128, 2 slabs, grouped.
 SHAPES = [
@@ -48,9 +49,13 @@ SHAPES = [
     (4, 256, 640, 4096),     # b = 256: 10 steps
     (8, 128, 3072, 4096),    # b = 256: 48 steps: the short product the benchmark times
     (3, 128, 320, 7296),     # b = 171 tiles (not a multiple of 8), 5 steps
-    (2, 2048, 128, 2048),    # b = 512: 128 x 128, 2 slabs, 2 steps
-    (2, 2048, 512, 2048),    # b = 512: 8 steps
-    (2, 2176, 192, 2048),    # b = 544: 3 steps
+    (4, 512, 128, 4096),     # b = 512: 256 x 128, 3 slabs, 256 tiles, 2 steps
+    (3, 512, 320, 2816),     # b = 264: 256 x 128, 132 tiles (not a multiple of 8), 5 steps
+    (6, 256, 320, 4096),     # b = 384: 256 x 128, 192 tiles, 5 steps
+    (8, 256, 3072, 4096),    # b = 512: 256 x 128, 256 tiles, 48 steps
+    (2, 2048, 128, 2048),    # b = 512, M = 2048: 256 x 128, 3 slabs, 2 steps
+    (2, 2048, 512, 2048),    # b = 512: 256 x 128, 8 steps
+    (2, 2176, 192, 2048),    # b = 544: 128 x 128, 2 slabs, 3 steps
     (2, 2176, 512, 2048),    # b = 544: 8 steps
     (3, 128, 320, 11008),    # b = 258 tiles (not a multiple of 8), 5 steps
     (4, 2048, 128, 2048),    # b = 1024: 256 x 256, 2 steps
@@ -63,7 +68,8 @@ SHAPES = [
 # one shape per tile configuration in its steady state (and the benchmarked
 # ones), for the whole-call tests
 STEADY = [(8, 64, 512, 4096), (4, 320, 1024, 1024), (2, 256, 512, 384), (8, 128, 3072, 1024), (4, 128, 1024, 4096),
-          (4, 256, 640, 4096), (8, 128, 3072, 4096), (2, 2176, 512, 2048), (4, 2048, 576, 2048), (4, 2048, 3072, 4096)]
+          (4, 256, 640, 4096), (8, 128, 3072, 4096), (2, 2048, 512, 2048), (2, 2176, 512, 2048), (4, 2048, 576, 2048),
+          (4, 2048, 3072, 4096)]
 
 
 def _inputs(P, M, K, H, seed, dev, w=None):
