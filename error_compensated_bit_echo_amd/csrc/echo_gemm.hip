@@ -154,9 +154,9 @@ __device__ __forceinline__ void slab_barrier() {
 // activations come from memory once per XCD that needs them; at P = 8 with 32
 // panels of 128 columns, one rank per XCD instead of all eight on every XCD).
 // Without XG, tile (x, y, r) is block x + gx (y + gy r), column panel fastest.
-// WNT: the weight loads are non-temporal, for the products of at most one tile
-// per CU, where the blocks that read a weight panel (one or two) run at the
-// same time on one XCD and nothing reads it later.
+// WNT: the weight loads are non-temporal, for the short products (at most two
+// 128 x 128 tiles per CU), where the few blocks that read a weight panel run at
+// the same time on one XCD and nothing reads it later.
 // WAHEAD (with S = 2): the weights are loaded a K step further ahead than the
 // activations, through a ring of three W slabs beside the two A slabs.
 template <int BM, int TN, int NW, int S, bool FUSED, int SFB, bool XG, bool WNT, bool WAHEAD>
