@@ -531,7 +531,9 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
     `weights` ("cold", "cached" or "both") picks which of the two are timed, so
     that a profiler's kernel trace holds one kind only."""
     res = []
-    for P, M, K, H in ((4, 2048, 3072, 4096), (8, 128, 3072, 4096)):
+    # prefill-like (256 x 256 tiles), decode-like at 128 and 256 tokens (128 x 128 and 256 x 128
+    # tiles), and a two-rank decode-like product (64 x 64 tiles)
+    for P, M, K, H in ((4, 2048, 3072, 4096), (8, 128, 3072, 4096), (8, 256, 3072, 4096), (2, 128, 3072, 4096)):
         g = torch.Generator(device=dev)
         g.manual_seed(5)
         set_bytes = P * H * K * 2
