@@ -32,3 +32,25 @@ def test_c_client_matches_the_oracle(tmp_path):
             else:
                 got = np.fromfile(tmp_path / f"out{c}_{t}.bin", dtype=np.float32)
             assert np.array_equal(got.view(np.uint32), o["out"].view(np.uint32)), f"config {c} call {t}"
+
+
+LATENCY = os.path.join(ROOT, "tests", "c_client", "echo_c_latency")
+
+
+def test_c_latency_program_reports_its_three_figures():
+    """The per-call latency program (plain C, eager calls) runs and prints one
+    JSON line with positive figures, the round trip of a call and a synchronize
+    at least half the back-to-back device time (a loose bound that catches a
+    figure scaled by the wrong call count), and refuses bad arguments."""
+    import json
+
+    assert os.path.exists(LATENCY), "the latency program is not built: run __graft_entry__.build()"
+    res = subprocess.run([LATENCY, "4", str(32 * 1024), "50"], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr + res.stdout
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    assert (r["P"], r["N"], r["calls"]) == (4, 32 * 1024, 50)
+    assert r["device_us"] > 0 and r["enqueue_us"] > 0
+    assert r["roundtrip_us"] >= 0.5 * r["device_us"]
+    # bad arguments are refused before the GPU is touched
+    bad = subprocess.run([LATENCY, "4", "33", "10"], capture_output=True, text=True, timeout=60)
+    assert bad.returncode == 2
