@@ -367,3 +367,44 @@ def test_argument_errors(cuda):
     assert lib.echo_gemm_stage1(inside, arr(W), M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
     assert lib.echo_gemm_stage1(arr(A), inside, M, K, st.handle, 0, s) == B.ECHO_ERR_ARG
     torch.cuda.synchronize()
+
+
+def _random_shapes(n, seed):
+    """n seeded product shapes: P in 1..16, M = 64 m (m <= 40), K = 64 k (k <= 24), H = 128 h (h <= 32),
+    at most 48 Mi output elements over the ranks.  Seed 23 puts at least three shapes on each tile
+    configuration of the launcher."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        P = int(rng.integers(1, 17))
+        M = 64 * int(rng.integers(1, 41))
+        K = 64 * int(rng.integers(1, 25))
+        H = 128 * int(rng.integers(1, 33))
+        if P * M * H <= 48 * 2 ** 20:
+            shapes.append((P, M, K, H))
+    return shapes
+
+
+@pytest.mark.parametrize("P,M,K,H", _random_shapes(48, 23))
+def test_random_shapes(cuda, P, M, K, H):
+    """Seeded random shapes: sampled rows of every rank's product within the exact bound, and the
+    whole fused payload equal to stage 1 of the written-out product."""
+    import error_compensated_bit_echo_amd as E
+    torch = _torch()
+    A, W = _inputs(P, M, K, H, 5, cuda)
+    out = _unfused(A, W)
+    rows = np.unique(np.linspace(0, M - 1, 16).astype(np.int64))
+    for r in range(P):
+        a = A[r][rows].float().cpu().numpy().astype(np.float64)
+        w = W[r].float().cpu().numpy().astype(np.float64)
+        exact = a @ w.T
+        bound = np.abs(exact) * 2.0 ** -8 + (np.abs(a) @ np.abs(w).T) * K * 2.0 ** -24
+        got = out[r][rows].float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - exact) <= bound), f"rank {r}"
+    fused = _state(P, M * H, "bf16")
+    E.echo_gemm_stage1(A, W, fused)
+    ref = _state(P, M * H, "bf16")
+    E.echo_stage1([o.reshape(-1) for o in out], ref)
+    vf, vr = E.echo_debug_views(fused), E.echo_debug_views(ref)
+    torch.cuda.synchronize()
+    assert torch.equal(vf["codes1"], vr["codes1"]) and torch.equal(vf["scales1"], vr["scales1"])
