@@ -605,6 +605,8 @@ def gemm_report(E, torch, dev, weights: str = "both") -> dict:
                     **({"us_weights_cached": {k: round(v, 2) for k, v in t["cached"].items()}}
                        if "cached" in t else {}),
                     "bf16_peak_TFLOPs": 2500.0,
+                    **({"fused_frac_of_bf16_peak": round(flop / (t["cold"]["fused"] * 1e-6) / 1e12 / 2500.0, 3)}
+                       if "cold" in t else {}),
                     "partial_bytes_not_written_or_read": 2 * 2 * P * M * H})
     return {"config": "gemm", "shapes": res, "decode_layer": decode_layer_report(E, torch, dev)}
 
