@@ -24,7 +24,9 @@ The row-parallel product and ``g`` can also run as one step in bfloat16
 (``product="bf16_fused"``): libecho's MFMA product writes each rank's stage-1
 payload straight from its accumulators, then the owner and decode stages
 finish the all-reduce; ``"bf16"`` runs the same product written out followed
-by a whole Echo call, which gives bit-identical results.
+by a whole Echo call, which gives bit-identical results.  The same holds for
+``f`` in the backward pass: the input-gradient products of the column-parallel
+layer run on libecho's kernel, on the backward state.
 """
 from __future__ import annotations
 
@@ -66,9 +68,9 @@ class EchoGroup:
             B.echo_reset(self.state, 3)
         self.log.clear()
 
-    def product_allreduce(self, A, W, fused: bool):
-        """Forward all-reduce of bf16(A_r @ W_r^T) (A_r [T, K], W_r [H, K] bf16)
-        on the forward state: fused, stage 1 runs in the product's epilogue;
+    def product_allreduce(self, A, W, fused: bool, direction: int = B.ECHO_FWD):
+        """All-reduce of bf16(A_r @ W_r^T) (A_r [T, K], W_r [H, K] bf16) on the
+        state of `direction`: fused, stage 1 runs in the product's epilogue;
         otherwise the product is written out and reduced by a whole call."""
         import torch
 
@@ -79,16 +81,16 @@ class EchoGroup:
         T, H = A[0].shape[0], W[0].shape[0]
         out = torch.empty(self.numel, dtype=torch.float32, device=self.device)
         if fused:
-            B.echo_gemm_stage1(A, W, self.state, B.ECHO_FWD)
-            B.echo_owner(self.state, B.ECHO_FWD)
+            B.echo_gemm_stage1(A, W, self.state, direction)
+            B.echo_owner(self.state, direction)
             B.echo_decode(out, self.state)
         else:
             parts = [torch.empty(T, H, dtype=torch.bfloat16, device=self.device) for _ in range(self.P)]
             B.echo_gemm_bf16(A, W, parts)
-            B.echo_reduce([p.view(-1) for p in parts], out, self.state, B.ECHO_FWD)
+            B.echo_reduce([p.view(-1) for p in parts], out, self.state, direction)
         if self.record:
-            self.log.append((B.ECHO_FWD, ("product", [a.detach().clone() for a in A],
-                                          [w.detach().clone() for w in W]), out.detach().clone()))
+            self.log.append((direction, ("product", [a.detach().clone() for a in A],
+                                         [w.detach().clone() for w in W]), out.detach().clone()))
         return out
 
     def allreduce(self, partials, direction: int):
@@ -166,7 +168,29 @@ def _fns():
             out = ctx.group.allreduce(parts, B.ECHO_BWD)
             return None, out.view(ctx.shape).to(ctx.dtype)
 
-    return ReduceForward, ReduceBackward, RowParallelEcho
+    class ColumnParallelEcho(torch.autograd.Function):
+        """f(a) @ W1_r with the input-gradient products in bfloat16 on libecho's
+        matrix-core kernel: forward gives every rank's pre-activation a @ W1_r
+        (fp32, no reduction); backward gives dL/da through Echo on the backward
+        state as sum_r bf16(bf16(dpre_r) @ bf16(W1_r)^T) (fused: stage 1 in the
+        product's epilogue), and the fp32 weight gradients a^T dpre_r."""
+
+        @staticmethod
+        def forward(ctx, group: "EchoGroup", fused: bool, a, *w1s):
+            ctx.save_for_backward(a, *w1s)
+            ctx.group, ctx.fused = group, fused
+            return tuple(a @ w for w in w1s)
+
+        @staticmethod
+        def backward(ctx, *gpres):
+            a, *w1s = ctx.saved_tensors
+            A = [g.to(torch.bfloat16).contiguous() for g in gpres]   # [T, F/P]
+            W = [w.to(torch.bfloat16).contiguous() for w in w1s]     # [H, F/P]: output features by K
+            da = ctx.group.product_allreduce(A, W, ctx.fused, B.ECHO_BWD).view(a.shape)
+            dw = [a.t().contiguous() @ g for g in gpres]
+            return (None, None, da) + tuple(dw)
+
+    return ReduceForward, ReduceBackward, RowParallelEcho, ColumnParallelEcho
 
 
 _FNS = None
@@ -178,6 +202,15 @@ def row_parallel_echo(group: "EchoGroup", hs, ws, shape, fused: bool):
     if _FNS is None:
         _FNS = _fns()
     return _FNS[2].apply(group, shape, fused, *hs, *ws)
+
+
+def column_parallel_echo(group: "EchoGroup", a, ws, fused: bool):
+    """[a @ W1_r] with the input gradient through bf16 products on libecho's
+    kernel and Echo's backward state (see ColumnParallelEcho)."""
+    global _FNS
+    if _FNS is None:
+        _FNS = _fns()
+    return _FNS[3].apply(group, fused, a, *ws)
 
 
 def reduce_forward(group: EchoGroup, partials, shape):
@@ -202,9 +235,11 @@ class TPMLPStack:
     F/P rows); x <- x + g(sum_r gelu(f(a)_r @ W1_r) @ W2_r), a = rmsnorm(x).
     Weights are fp32 and seeded.  product "f32": the products are taken in fp32
     and each rank's partial output is rounded to bf16 (the wire dtype);
-    "bf16" / "bf16_fused": the row-parallel product runs in bfloat16 on
-    libecho's kernel (written out, or with stage 1 in its epilogue; T a
-    multiple of 64, H of 128, F/P of 64)."""
+    "bf16" / "bf16_fused": the products whose outputs are reduced run in
+    bfloat16 on libecho's kernel, the row-parallel W2 product in the forward
+    pass and the column-parallel W1 input-gradient product in the backward
+    pass (written out, or with stage 1 in their epilogues; T a multiple of 64,
+    H of 128, F/P of 64)."""
 
     def __init__(self, layers: int, hidden: int, ffn: int, P: int, seed: int = 0, device=None,
                  product: str = "f32"):
@@ -235,8 +270,12 @@ class TPMLPStack:
 
         for l in range(self.L):
             a = x * torch.rsqrt(x.pow(2).mean(dim=-1, keepdim=True) + 1e-6)
-            xs = replicate(group, a)
-            hs = [torch.nn.functional.gelu(xs[r] @ self.w1[l][r]) for r in range(self.P)]
+            if self.product == "f32":
+                xs = replicate(group, a)
+                hs = [torch.nn.functional.gelu(xs[r] @ self.w1[l][r]) for r in range(self.P)]
+            else:
+                pres = column_parallel_echo(group, a, self.w1[l], self.product == "bf16_fused")
+                hs = [torch.nn.functional.gelu(p) for p in pres]
             if self.product == "f32":
                 partials = [(hs[r] @ self.w2[l][r]).to(torch.bfloat16) for r in range(self.P)]
                 y = reduce_forward(group, [p.reshape(-1) for p in partials], x.shape)

@@ -84,12 +84,13 @@ def test_tp_step_errors_against_exact_allreduce(cuda):
 @pytest.mark.parametrize("tokens", [T, 64])
 @pytest.mark.parametrize("variant", [{}, {"sender_feedback": True, "state_bf16": True}])
 def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant, tokens):
-    """Row-parallel products in bfloat16 on libecho's kernel: with stage 1 in the
-    product's epilogue the whole training step (loss, input and weight
-    gradients) is bit-identical to the product written out and reduced by
-    echo_reduce, and every reduction matches the oracle run on the partials the
-    written-out product gives (teacher-forced, one oracle state per direction).
-    64 tokens take the product's 64-row tiles."""
+    """The products whose outputs are reduced in bfloat16 on libecho's kernel
+    (row-parallel W2 forward, column-parallel W1 input gradient backward): with
+    stage 1 in the products' epilogues the whole training step (loss, input and
+    weight gradients) is bit-identical to the products written out and reduced
+    by echo_reduce, and every reduction of both directions matches the oracle run
+    on the partials the written-out product gives (teacher-forced, one oracle
+    state per direction).  At this width both token counts take the product's 64 x 64 tiles."""
     import torch
     import error_compensated_bit_echo_amd as E
     from error_compensated_bit_echo_amd import tp
@@ -110,12 +111,12 @@ def test_tp_bf16_product_fused_matches_unfused_and_the_oracle(cuda, variant, tok
     st = eo.OracleState(tokens * H)
     assert [d for d, _, _ in gf.log] == [0] * L + [1] * L
     for k, (d, parts, out) in enumerate(gf.log):
-        if d == 0:
-            tag, A, W = parts
-            assert tag == "product"
-            written = [torch.empty(tokens, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
-            E.echo_gemm_bf16(A, W, written)
-            parts = written
+        # every reduction of the step is a product's: W2's forward, W1's input gradient backward
+        tag, A, W = parts
+        assert tag == "product"
+        written = [torch.empty(tokens, H, dtype=torch.bfloat16, device=cuda) for _ in range(P)]
+        E.echo_gemm_bf16(A, W, written)
+        parts = written
         host = np.stack([p.reshape(-1).float().cpu().numpy() for p in parts])
         o = eo.echo_call(host, st, d, **variant)
         assert np.array_equal(out.cpu().numpy().view(np.uint32), o["out"].view(np.uint32)), f"call {k} dir {d}"
