@@ -14,9 +14,12 @@
 // Tiling: a block computes a 256 x 256 tile of one rank's [M, H] partial with 8
 // wavefronts, each a 64 x 128 sub-tile of 2 x 4 v_mfma_f32_32x32x16_bf16 tiles,
 // where the product is large enough; 128 x 128 with 8 wavefronts (32 x 64 each)
-// for mid-sized and short products; 64 x 128 with 4 wavefronts for the shortest
-// and where M is an odd multiple of 64; 64 x 64 with 4 wavefronts (one 32 x 32
-// MFMA tile each) where even 64 x 128 tiles would leave CUs idle.
+// for mid-sized and short products; 256 x 128 with 8 wavefronts (64 x 64 each)
+// for products of one to two 128 x 128 tiles per CU; 64 x 128 with 4 wavefronts
+// for the shortest and where M is an odd multiple of 64; 64 x 64 with 4
+// wavefronts (one 32 x 32 MFMA tile each) where even 64 x 128 tiles would leave
+// CUs idle.  The 256 x 256 tiles issue each K step's weight loads a quarter per
+// 16-deep sub-step rather than in one burst.
 // K advances 64 at a time through a ring of LDS slabs: while the matrix cores
 // work on one slab, the next ones stream from global memory straight into the
 // others (buffer_load_dwordx4 ... lds through a buffer resource over the block's
@@ -365,10 +368,10 @@ __global__ __launch_bounds__(64 * NW) void echo_gemm_k(const GemmArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     slab_barrier();
-    // The 256-column tiles issue W(it + 2) a quarter at a time, one share before
-    // each sub-step's MFMAs, rather than in one burst with A(it + 1) at the
-    // step's start; A(it + 1) still goes out first, so the end-of-step wait is
-    // unchanged.  (Measured with the weights cold: at P = 4, M = 2048,
+    // The 256-column tiles issue W(it + 2) a quarter at a time, one share at the
+    // step's start after A(it + 1) and one after the MFMAs of each of the first
+    // three sub-steps, rather than in one burst with A(it + 1); A(it + 1) still
+    // goes out first, so the end-of-step wait is unchanged.  (Measured with the weights cold: at P = 4, M = 2048,
     // K = 3072, H = 4096 176.2 against 181.8 us, at P = 8 345.3 against 358.7;
     // no faster on the 128 x 128 tiles, nor with A spread over the first two
     // sub-steps as well.)
